@@ -1,0 +1,172 @@
+"""Fine-grained-scaled FP8 GEMM, dense / M-grouped contiguous / M-grouped masked.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Operation (DeepGEMM digest, GeekNews topic 19459, "GEMM arayuzu ve yerlesim
+kisitlari"): the NT GEMM D = A @ B.T with A [M, K] row-major and B [N, K]
+(K-contiguous rows); the C addend of the pages is not part of this path.  The
+fp32 accumulation is "promoted" once per 128-wide K slice (GeekNews topic
+19444, opening bullets; 7minutos.es, "Detalles y beneficios tecnicos"):
+
+    a[m,k] = dec(A[m,k]) * sa[k//128][m]
+    b[n,k] = dec(B[n,k]) * sb[n//128][k//128]
+    X[m,n] = sum_k a[m,k] * b[n,k]                (float64, the true value)
+    D[m,n] = bf16_RNE(X[m,n])                      (expected output)
+    S[m,n] = sum_k |a[m,k] * b[n,k]|              (magnitude for error bounds)
+
+The promotion only changes where rounding happens, not the value computed,
+so the oracle evaluates the definition.  Two forms are provided and
+cross-checked in the tests:
+
+(i)  ``gemm_blockwise``: per 128-K slice, the float64 product of the decoded
+     codes (exact: every e4m3 value is a multiple of 2^-9 below 2^9, so a
+     128-term slice sum has at most 43 significant bits), then scaled by
+     sa*sb (exact in float64) and accumulated in float64.
+(ii) ``gemm_dequant``: decode-and-scale both operands (exact in float64),
+     then one float64 matmul.
+
+Grouped forms ("Dense ve Grouped GEMM" of the same digest):
+
+* contiguous: experts share N and K; each row r of A belongs to expert
+  m_indices[r] and uses B[m_indices[r]], sb[m_indices[r]].  Reading for the
+  padding rows the pages leave open: an index < 0 marks a padding row whose
+  output is left untouched.
+* masked: group g computes rows [0, min(max(mask[g], 0), M_cap)) of A[g]
+  against B[g]; all other rows of D[g] are left untouched.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .e4m3 import decode, bf16_rne_bits
+
+GROUP = 128
+
+
+def _check_dense(A, sa, B, sb):
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2 or K % GROUP:
+        raise ValueError("A and B need the same K, a multiple of 128")
+    Kb = K // GROUP
+    Nb = -(-N // GROUP)
+    if sa.shape[0] != Kb or sa.shape[1] < M:
+        raise ValueError(f"sa must be [K/128, >=M], got {sa.shape}")
+    if sb.shape != (Nb, Kb):
+        raise ValueError(f"sb must be [ceil(N/128), K/128], got {sb.shape}")
+    return M, N, K, Kb
+
+
+def gemm_blockwise(A, sa, B, sb, with_magnitude: bool = False):
+    """Form (i).  A uint8 [M,K], sa f32 [K/128, >=M], B uint8 [N,K], sb f32 [Nb,Kb].
+
+    Returns X float64 [M, N] (and S when ``with_magnitude``).
+    """
+    A = np.asarray(A, np.uint8)
+    B = np.asarray(B, np.uint8)
+    sa = np.asarray(sa, np.float32)
+    sb = np.asarray(sb, np.float32)
+    M, N, K, Kb = _check_dense(A, sa, B, sb)
+    a = decode(A)
+    b = decode(B)
+    nblk = np.arange(N) // GROUP
+    X = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64) if with_magnitude else None
+    for kb in range(Kb):
+        ks = slice(kb * GROUP, (kb + 1) * GROUP)
+        P = a[:, ks] @ b[:, ks].T  # exact slice partial
+        scale = sa[kb, :M].astype(np.float64)[:, None] * sb[nblk, kb].astype(np.float64)[None, :]
+        X += P * scale
+        if with_magnitude:
+            S += (np.abs(a[:, ks]) @ np.abs(b[:, ks]).T) * np.abs(scale)
+    return (X, S) if with_magnitude else X
+
+
+def gemm_dequant(A, sa, B, sb):
+    """Form (ii): dequantise both operands exactly, then one float64 matmul."""
+    A = np.asarray(A, np.uint8)
+    B = np.asarray(B, np.uint8)
+    sa = np.asarray(sa, np.float32)
+    sb = np.asarray(sb, np.float32)
+    M, N, K, Kb = _check_dense(A, sa, B, sb)
+    kblk = np.arange(K) // GROUP
+    nblk = np.arange(N) // GROUP
+    a = decode(A) * sa[kblk, :M].T.astype(np.float64)
+    b = decode(B) * sb[nblk][:, kblk].astype(np.float64)
+    return a @ b.T
+
+
+def gemm_nt(A, sa, B, sb, with_magnitude: bool = False):
+    """Dense NT GEMM: float64 X (and S).  Use ``to_bf16`` for the D bits."""
+    return gemm_blockwise(A, sa, B, sb, with_magnitude=with_magnitude)
+
+
+def to_bf16(X) -> np.ndarray:
+    """Expected BF16 output bits, D = bf16_RNE(X)."""
+    return bf16_rne_bits(X)
+
+
+def gemm_grouped_contiguous(A, sa, B, sb, m_indices, with_magnitude: bool = False):
+    """Contiguous M-grouped GEMM.
+
+    A uint8 [M_total, K]; sa f32 [K/128, >=M_total];
+    B uint8 [G, N, K]; sb f32 [G, Nb, Kb]; m_indices int [M_total].
+    Returns (X float64 [M_total, N], valid bool [M_total]) (+ S).
+    Rows with m_indices < 0 are not valid: their X rows are 0 and the
+    library must leave them untouched.
+    """
+    A = np.asarray(A, np.uint8)
+    B = np.asarray(B, np.uint8)
+    sa = np.asarray(sa, np.float32)
+    sb = np.asarray(sb, np.float32)
+    idx = np.asarray(m_indices).astype(np.int64)
+    G, N, K = B.shape
+    M = A.shape[0]
+    if idx.shape != (M,):
+        raise ValueError("m_indices must have one entry per row of A")
+    if (idx >= G).any():
+        raise ValueError("expert index out of range")
+    X = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64) if with_magnitude else None
+    for e in np.unique(idx[idx >= 0]):
+        rows = np.nonzero(idx == e)[0]
+        res = gemm_blockwise(A[rows], sa[:, rows], B[e], sb[e], with_magnitude=with_magnitude)
+        if with_magnitude:
+            X[rows], S[rows] = res
+        else:
+            X[rows] = res
+    valid = idx >= 0
+    return (X, valid, S) if with_magnitude else (X, valid)
+
+
+def gemm_grouped_masked(A, sa, B, sb, masked_m, with_magnitude: bool = False):
+    """Masked M-grouped GEMM.
+
+    A uint8 [G, M_cap, K]; sa f32 [G, K/128, >=M_cap];
+    B uint8 [G, N, K]; sb f32 [G, Nb, Kb]; masked_m int [G].
+    Returns (X float64 [G, M_cap, N], valid bool [G, M_cap]) (+ S).
+    """
+    A = np.asarray(A, np.uint8)
+    B = np.asarray(B, np.uint8)
+    sa = np.asarray(sa, np.float32)
+    sb = np.asarray(sb, np.float32)
+    mask = np.asarray(masked_m).astype(np.int64)
+    G, M_cap, K = A.shape
+    N = B.shape[1]
+    if mask.shape != (G,):
+        raise ValueError("masked_m must have one entry per group")
+    X = np.zeros((G, M_cap, N), dtype=np.float64)
+    S = np.zeros((G, M_cap, N), dtype=np.float64) if with_magnitude else None
+    valid = np.zeros((G, M_cap), dtype=bool)
+    for g in range(G):
+        rows = int(min(max(mask[g], 0), M_cap))
+        valid[g, :rows] = True
+        if rows == 0:
+            continue
+        res = gemm_blockwise(A[g, :rows], sa[g][:, :rows], B[g], sb[g], with_magnitude=with_magnitude)
+        if with_magnitude:
+            X[g, :rows], S[g, :rows] = res
+        else:
+            X[g, :rows] = res
+    return (X, valid, S) if with_magnitude else (X, valid)
