@@ -1,0 +1,162 @@
+/*
+ * fp8gemm.h -- C ABI of the MI355X (gfx950) FP8 e4m3 fine-grained-scaled GEMM library.
+ *
+ * Operation.  The NT GEMM D = A . B^T (DeepGEMM digest, GeekNews topic 19459,
+ * section "GEMM arayuzu ve yerlesim kisitlari": the naming is D = C + A @ B
+ * with NT meaning A row-major and B stored [N,K]; this library has no C
+ * addend) with DeepSeek-V3 fine-grained scaling (GeekNews topic 19444,
+ * opening bullets; 7minutos.es, "Detalles y beneficios tecnicos"):
+ *
+ *     D[m,n] = bf16( sum_kb  P_kb[m,n] * sa[kb][m] * sb[n/128][kb] )
+ *     P_kb[m,n] = sum_{k in slice kb} e4m3(A[m,k]) * e4m3(B[n,k])
+ *
+ * Each 128-wide K slice is computed by the matrix cores into a fresh fp32
+ * partial P_kb and then scaled and added ("promoted") into an fp32
+ * accumulator; the accumulator is rounded once to BF16 (nearest-even).
+ *
+ * Types.  FP8 operands are e4m3fn bytes (OCP: bias 7, max 448, NaN 0x7F/0xFF)
+ * passed as uint8_t.  Scales are IEEE fp32.  BF16 results are uint16_t bit
+ * patterns.  Kb = K/128, Nb = ceil(N/128).
+ *
+ * Scale layouts.  Activation scales are per (row, 128-wide K group) and are
+ * stored K-group-major ("transposed", as the digest requires for the LHS
+ * factors): sa[kb * ld_sa + m], ld_sa >= rows.  Weight scales
+ * are per 128x128 block, row-major: sb[nb * Kb + kb].
+ *
+ * Ownership.  Every pointer named "device" is device memory owned by the
+ * caller; the library never allocates, frees or retains pointers, and never
+ * synchronises the host.  Each GEMM or cast call only enqueues kernels on
+ * `stream` (a hipStream_t; NULL is the default stream) and returns.  The calls
+ * are therefore safe to capture in a HIP graph, which is what the masked form
+ * is for (the host never learns the per-expert counts).
+ *
+ * Errors.  Preconditions that the host can check are checked before anything
+ * is launched; on failure the call returns the status, launches nothing, and
+ * fg_last_error() describes the failure (thread-local, valid until the next
+ * call on the same thread).  A call with no output elements (M == 0 or
+ * N == 0, M_total == 0, M_cap == 0) returns FG_OK without launching.  A
+ * launch failure returns FG_EHIP with the HIP error string.  Preconditions on
+ * device-resident metadata (expert indices, masks) are documented per call
+ * and are not checked (checking would need a host synchronisation).
+ */
+#ifndef FP8GEMM_H
+#define FP8GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FG_OK = 0,
+  FG_EINVAL = 1,      /* null pointer, negative size, G <= 0, leading dimension too small */
+  FG_EALIGN = 2,      /* K % 128 != 0, M_total % 128 != 0, misaligned operand pointer or row stride */
+  FG_EUNSUPPORTED = 3,/* sizes beyond what the kernels index (see per call) */
+  FG_EHIP = 4         /* a HIP launch failed; see fg_last_error() */
+} fg_status;
+
+/*
+ * Dense NT GEMM (the digest's fp8_gemm_nt without C).
+ *   A   device [M, K] e4m3, row stride lda bytes   (lda >= K, lda % 16 == 0, A 16-byte aligned)
+ *   sa  device fp32 [Kb][ld_sa]                    (ld_sa >= M, 4-byte aligned)
+ *   B   device [N, K] e4m3, row stride ldb bytes   (ldb >= K, ldb % 16 == 0, B 16-byte aligned)
+ *   sb  device fp32 [Nb][Kb]                       (4-byte aligned)
+ *   D   device [M, N] bf16, row stride ldd elems   (ldd >= N, 2-byte aligned; rows that are 8- or
+ *       16-byte aligned get vector stores); written
+ * M, N >= 0 arbitrary; K % 128 == 0.  K == 0 writes D = 0 (sa, sb may then be NULL).
+ * Only D[0:M, 0:N] is written.
+ */
+fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const uint8_t* B, int64_t ldb, const float* sb,
+                      uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
+
+/*
+ * M-grouped "contiguous" GEMM (digest, section "Dense ve Grouped GEMM": the
+ * experts share N and K; every expert's rows are concatenated along M and each
+ * expert segment is aligned to the GEMM M block, here 128 rows).
+ *   A         device [M_total, K] e4m3, packed rows (row stride K)
+ *   sa        device fp32 [Kb][ld_sa], ld_sa >= M_total
+ *   B         device [G, N, K] e4m3, packed
+ *   sb        device fp32 [G][Nb][Kb]
+ *   m_indices device int32 [M_total]: expert of each row, or -1 for a padding row
+ *   D         device [M_total, N] bf16, packed (row stride N)
+ * M_total % 128 == 0, K % 128 == 0, G >= 1.
+ * Device-side precondition (not checked): within each aligned 128-row block
+ * every non-negative index is the same value e < G.  The block is computed
+ * against B[e], where e is the largest index in the block; rows whose index
+ * is not e (padding) are left untouched; a block of padding only is skipped.
+ */
+fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t ld_sa,
+                                      const uint8_t* B, const float* sb,
+                                      const int32_t* m_indices,
+                                      uint16_t* D, int M_total, int N, int K, int G, void* stream);
+
+/*
+ * M-grouped "masked" GEMM for decoding (digest, "Dense ve Grouped GEMM": the
+ * per-expert token count lives on the device, the CPU does not know it, and
+ * only the valid region is computed).
+ *   A        device [G, M_cap, K] e4m3, packed
+ *   sa       device fp32 [G][Kb][ld_sa], ld_sa >= M_cap
+ *   B        device [G, N, K] e4m3, packed
+ *   sb       device fp32 [G][Nb][Kb]
+ *   masked_m device int32 [G]: valid rows of each group
+ *   D        device [G, M_cap, N] bf16, packed
+ *   expected_m  host hint of the typical count (0 = unknown); only picks a tile shape
+ * Group g computes rows [0, clamp(masked_m[g], 0, M_cap)); every other row of
+ * D[g] is left untouched (bit for bit).  K % 128 == 0, G >= 1.
+ */
+fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_sa,
+                                  const uint8_t* B, const float* sb,
+                                  const int32_t* masked_m,
+                                  uint16_t* D, int G, int M_cap, int N, int K,
+                                  int expected_m, void* stream);
+
+/*
+ * Per-token (1 x 128) FP8 cast of activations (the digest leaves casting to
+ * the user, "GEMM arayuzu ve yerlesim kisitlari"; this is the library's own
+ * helper).  For each row m and group kb:
+ *     amax = max |x[m, 128kb : 128kb+128]|
+ *     s    = max(amax, 1e-4f) / 448          (fp32, correctly rounded)
+ *     q    = e4m3_RNE(x / s)                 (fp32 division, nearest-even)
+ *   x   device fp32 [M, K], row stride ldx elements (ldx >= K, ldx % 4 == 0, 16-byte aligned)
+ *   q   device [M, K] e4m3, packed (row stride K), 8-byte aligned
+ *   sa  device fp32 [Kb][ld_sa], ld_sa >= M (written; the GEMM's activation-scale layout)
+ * K % 128 == 0.  Input values must be finite.
+ */
+fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa,
+                             int M, int K, void* stream);
+
+/*
+ * Per-block (128 x 128) FP8 cast of a weight matrix, same formula with amax
+ * taken over each 128x128 block (the last row block covers N % 128 rows).
+ *   w   device fp32 [N, K], row stride ldw elements (ldw >= K, ldw % 4 == 0, 16-byte aligned)
+ *   q   device [N, K] e4m3, packed, 4-byte aligned
+ *   sb  device fp32 [Nb][Kb] (written; the GEMM's weight-scale layout)
+ * K % 128 == 0.  For expert weights [G, N, K] with N % 128 == 0 one call on
+ * [G*N, K] yields the [G][Nb][Kb] layout; otherwise call once per expert.
+ */
+fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
+                             int N, int K, void* stream);
+
+/* Row alignment of each expert segment in the contiguous layout: 128. */
+int fg_get_mk_alignment_for_contiguous_layout(void);
+
+/* Cap on the compute units the GEMM kernels spread their persistent workgroups
+ * over (the digest's set_num_sms); 0 (the default) means all of them.  The
+ * result bits do not depend on this value.  Process-wide, not thread-safe
+ * against concurrent launches. */
+void fg_set_num_cus(int n);
+int fg_get_num_cus(void);
+
+/* Description of the last failure on this thread ("" after success). */
+const char* fg_last_error(void);
+
+/* Library version string. */
+const char* fg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H */

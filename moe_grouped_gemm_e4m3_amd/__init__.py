@@ -1,0 +1,262 @@
+"""MI355X (gfx950) FP8 e4m3 fine-grained-scaled GEMM: Python binding.
+
+A thin ctypes layer over ``libfp8gemm.so`` (C ABI in ``include/fp8gemm.h``).
+Each function takes torch CUDA tensors, checks dtypes and devices, and passes
+raw pointers, sizes and the current HIP stream to the C entry point of the
+same name.  Every step of the computation runs in the library's HIP kernels;
+there is no host or PyTorch fallback: if the library cannot be loaded, every
+call raises.
+
+Layouts (Kb = K/128, Nb = ceil(N/128)):
+  A   e4m3 [M, K] (uint8 or torch.float8_e4m3fn), rows K-contiguous
+  sa  fp32 [Kb, M] view of a [Kb, ld_sa] buffer (activation scales, K-group-major)
+  B   e4m3 [N, K]                      sb  fp32 [Nb, Kb]
+  D   bf16 [M, N]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8gemm.so")
+
+__all__ = [
+    "FP8GemmError",
+    "load_library",
+    "library_path",
+    "gemm_fp8_nt",
+    "gemm_fp8_grouped_contiguous",
+    "gemm_fp8_grouped_masked",
+    "fp8_cast_per_token",
+    "fp8_cast_per_block",
+    "get_mk_alignment_for_contiguous_layout",
+    "set_num_cus",
+    "get_num_cus",
+    "aligned_scale_ld",
+    "empty_activation_scales",
+    "EXPORTED_SYMBOLS",
+]
+
+FG_STATUS = {0: "FG_OK", 1: "FG_EINVAL", 2: "FG_EALIGN", 3: "FG_EUNSUPPORTED", 4: "FG_EHIP"}
+
+# name -> (restype, argtypes); one entry per declaration in include/fp8gemm.h
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_SIGNATURES = {
+    "gemm_fp8_nt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
+    "gemm_fp8_grouped_contiguous": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "gemm_fp8_grouped_masked": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
+    "fp8_cast_per_block": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
+    "fg_get_mk_alignment_for_contiguous_layout": (_I, []),
+    "fg_set_num_cus": (None, [_I]),
+    "fg_get_num_cus": (_I, []),
+    "fg_last_error": (ctypes.c_char_p, []),
+    "fg_version": (ctypes.c_char_p, []),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class FP8GemmError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        self.status = status
+        self.status_name = FG_STATUS.get(status, str(status))
+        super().__init__(f"{fn}: {self.status_name}: {msg}")
+
+
+def library_path() -> str:
+    return os.environ.get("FG_LIBRARY", LIB_PATH)
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle; raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} not found: build it with `python -m moe_grouped_gemm_e4m3_amd.build` (no fallback path exists)"
+        )
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _call(name: str, *args):
+    lib = load_library()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise FP8GemmError(name, st, lib.fg_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _fp8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    return t
+
+
+def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 CUDA tensor")
+    return t
+
+
+def _unit_inner(t: torch.Tensor, name: str):
+    if t.dim() >= 1 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def aligned_scale_ld(rows: int) -> int:
+    """Leading dimension for activation scales: rows rounded up to 4 floats."""
+    return max(4, (rows + 3) // 4 * 4)
+
+
+def empty_activation_scales(rows: int, K: int, device="cuda", groups: int | None = None) -> torch.Tensor:
+    """A [Kb, rows] (or [G, Kb, rows]) view of a padded [.., Kb, ld_sa] fp32 buffer."""
+    ld = aligned_scale_ld(rows)
+    Kb = K // 128
+    if groups is None:
+        return torch.empty(Kb, ld, dtype=torch.float32, device=device)[:, :rows]
+    return torch.empty(groups, Kb, ld, dtype=torch.float32, device=device)[:, :, :rows]
+
+
+def gemm_fp8_nt(A, sa, B, sb, D, stream=None):
+    """D[M,N] = bf16(A . B^T) with 1x128 activation and 128x128 weight scales."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    if D.dtype != torch.bfloat16 or not D.is_cuda:
+        raise TypeError("D must be a bfloat16 CUDA tensor")
+    for t, n in ((A, "A"), (B, "B"), (sa, "sa"), (D, "D")):
+        _unit_inner(t, n)
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous [Nb, Kb]")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(D.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)}")
+    _call(
+        "gemm_fp8_nt",
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        _ptr(D), D.stride(0), M, N, K, _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_grouped_contiguous(A, sa, B, sb, m_indices, D, stream=None):
+    """Contiguous M-grouped GEMM: row r of A uses expert m_indices[r] (-1 = padding, untouched)."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    if m_indices.dtype != torch.int32 or not m_indices.is_cuda or not m_indices.is_contiguous():
+        raise TypeError("m_indices must be a contiguous int32 CUDA tensor")
+    if D.dtype != torch.bfloat16 or not D.is_contiguous():
+        raise TypeError("D must be a contiguous bfloat16 CUDA tensor")
+    if not (A.is_contiguous() and B.is_contiguous() and sb.is_contiguous()):
+        raise ValueError("A, B and sb must be contiguous")
+    _unit_inner(sa, "sa")
+    M, K = A.shape
+    G, N, K2 = B.shape
+    if K2 != K or tuple(D.shape) != (M, N) or m_indices.shape[0] != M:
+        raise ValueError("shape mismatch")
+    _call(
+        "gemm_fp8_grouped_contiguous",
+        _ptr(A), _ptr(sa), sa.stride(0), _ptr(B), _ptr(sb), _ptr(m_indices), _ptr(D),
+        M, N, K, G, _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_grouped_masked(A, sa, B, sb, masked_m, D, expected_m: int = 0, stream=None):
+    """Masked M-grouped GEMM: group g computes rows [0, masked_m[g]) of A[g]; other rows of D untouched."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    if masked_m.dtype != torch.int32 or not masked_m.is_cuda or not masked_m.is_contiguous():
+        raise TypeError("masked_m must be a contiguous int32 CUDA tensor")
+    if D.dtype != torch.bfloat16 or not D.is_contiguous():
+        raise TypeError("D must be a contiguous bfloat16 CUDA tensor")
+    if not (A.is_contiguous() and B.is_contiguous() and sb.is_contiguous()):
+        raise ValueError("A, B and sb must be contiguous")
+    G, Mc, K = A.shape
+    N = B.shape[1]
+    if sa.dim() != 3 or sa.shape[0] != G or sa.stride(2) != 1 or sa.stride(0) != sa.shape[1] * sa.stride(1):
+        raise ValueError("sa must be a [G, Kb, M_cap] view of a [G, Kb, ld_sa] buffer")
+    if B.shape != (G, N, K) or tuple(D.shape) != (G, Mc, N) or masked_m.shape[0] != G:
+        raise ValueError("shape mismatch")
+    _call(
+        "gemm_fp8_grouped_masked",
+        _ptr(A), _ptr(sa), sa.stride(1), _ptr(B), _ptr(sb), _ptr(masked_m), _ptr(D),
+        G, Mc, N, K, int(expected_m), _stream(stream),
+    )
+    return D
+
+
+def fp8_cast_per_token(x, q=None, sa=None, stream=None):
+    """1x128 cast of fp32 activations [M, K] -> (q uint8 [M, K], sa fp32 [Kb, M] view)."""
+    x = _f32(x, "x")
+    _unit_inner(x, "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = empty_activation_scales(M, K, device=x.device)
+    q = _fp8(q, "q")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _unit_inner(sa, "sa")
+    _call("fp8_cast_per_token", _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
+    return q, sa
+
+
+def fp8_cast_per_block(w, q=None, sb=None, stream=None):
+    """128x128 cast of fp32 weights [N, K] -> (q uint8 [N, K], sb fp32 [Nb, Kb])."""
+    w = _f32(w, "w")
+    _unit_inner(w, "w")
+    N, K = w.shape
+    if q is None:
+        q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
+    if sb is None:
+        sb = torch.empty((N + 127) // 128, K // 128, dtype=torch.float32, device=w.device)
+    q = _fp8(q, "q")
+    if not (q.is_contiguous() and sb.is_contiguous()):
+        raise ValueError("q and sb must be contiguous")
+    _call("fp8_cast_per_block", _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
+    return q, sb
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return load_library().fg_get_mk_alignment_for_contiguous_layout()
+
+
+def set_num_cus(n: int) -> None:
+    load_library().fg_set_num_cus(int(n))
+
+
+def get_num_cus() -> int:
+    return load_library().fg_get_num_cus()

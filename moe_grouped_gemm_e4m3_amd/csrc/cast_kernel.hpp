@@ -1,0 +1,115 @@
+// cast_kernel.hpp -- fine-grained FP8 e4m3 casts (1x128 per token, 128x128 per block).
+//
+// The digest leaves FP8 casting to the user ("GEMM arayuzu ve yerlesim
+// kisitlari", DeepGEMM digest, GeekNews topic 19459) and fixes the factors as
+// fp32; the granularity (1x128 activations, 128x128 weights) is the
+// DeepSeek-V3 fine-grained scheme the release summary names.  Per group:
+//     amax = max |x|,  s = max(amax, 1e-4f) / 448,  q = e4m3_RNE(x / s)
+// with an IEEE fp32 division (hipcc's default float division is correctly
+// rounded) and a bit-exact round-to-nearest-even encoder.  Both kernels are
+// HBM-bound streams: 16-byte loads, one pass over the input.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fg {
+
+// fp32 -> e4m3fn code, round to nearest even, for |v| < 464 (the caller's
+// division by s = amax/448 guarantees |v| <= 448 * (1 + 2^-23)).
+//  * |v| >= 2^-6 (normal e4m3): round the fp32 significand to 3 bits with a
+//    nearest-even bias (carries move into the exponent), then re-bias the
+//    exponent from 127 to 7.
+//  * |v| <  2^-6 (subnormal e4m3, step 2^-9): code = rint(|v| * 512), where
+//    rint rounds half to even; 8 lands exactly on the smallest normal code.
+// The sign bit is copied, so -0 and tiny negatives give 0x80.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x3c800000u) {
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float scale_of(float amax) { return fmaxf(amax, 1e-4f) / 448.0f; }
+
+__device__ __forceinline__ float absmax4(float4 v, float m) {
+  return fmaxf(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))), m);
+}
+
+__device__ __forceinline__ uint32_t encode4(float4 v, float s) {
+  return e4m3_rne(v.x / s) | (e4m3_rne(v.y / s) << 8) | (e4m3_rne(v.z / s) << 16) | (e4m3_rne(v.w / s) << 24);
+}
+
+// One 16-lane group per (row, 128-column group); each lane handles 8 floats.
+__global__ __launch_bounds__(256) void cast_per_token_kernel(const float* __restrict__ x, int64_t ldx,
+                                                             uint8_t* __restrict__ q, float* __restrict__ sa,
+                                                             int64_t ld_sa, int M, int K, int64_t total_lanes) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total_lanes) return;  // total_lanes % 16 == 0: a group is all in or all out
+  const int Kb = K >> 7;
+  const int64_t grp = gid >> 4;
+  const int sub = (int)(gid & 15);
+  const int m = (int)(grp / Kb);
+  const int kb = (int)(grp - (int64_t)m * Kb);
+  const float* src = x + (int64_t)m * ldx + kb * 128 + sub * 8;
+  const float4 v0 = *(const float4*)src;
+  const float4 v1 = *(const float4*)(src + 4);
+  float amax = absmax4(v1, absmax4(v0, 0.f));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  const float s = scale_of(amax);
+  uint2 out;
+  out.x = encode4(v0, s);
+  out.y = encode4(v1, s);
+  *(uint2*)(q + (int64_t)m * K + kb * 128 + sub * 8) = out;
+  if (sub == 0) sa[(int64_t)kb * ld_sa + m] = s;
+}
+
+// One workgroup per 128x128 block: 32 lanes cover a 128-float row, 8 rows per
+// pass, 16 passes; the block is kept in registers between the amax reduction
+// and the encode.
+__global__ __launch_bounds__(256) void cast_per_block_kernel(const float* __restrict__ w, int64_t ldw,
+                                                             uint8_t* __restrict__ q, float* __restrict__ sb,
+                                                             int N, int K) {
+  __shared__ float red[4];
+  const int Kb = K >> 7;
+  const int nb = blockIdx.x / Kb;
+  const int kb = blockIdx.x - nb * Kb;
+  const int tid = threadIdx.x;
+  const int c = tid & 31;
+  const int r0 = tid >> 5;
+  const int rows = min(128, N - nb * 128);
+  const float* base = w + (int64_t)nb * 128 * ldw + kb * 128 + c * 4;
+  float4 v[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + 8 * i;
+    if (r < rows) {
+      v[i] = *(const float4*)(base + (int64_t)r * ldw);
+      amax = absmax4(v[i], amax);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = scale_of(amax);
+  uint8_t* qb = q + (int64_t)nb * 128 * K + kb * 128 + c * 4;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + 8 * i;
+    if (r < rows) *(uint32_t*)(qb + (int64_t)r * K) = encode4(v[i], s);
+  }
+  if (tid == 0) sb[(int64_t)nb * Kb + kb] = s;
+}
+
+}  // namespace fg

@@ -1,0 +1,357 @@
+// fp8gemm.hip -- C ABI of the gfx950 FP8 fine-grained-scaled GEMM library.
+//
+// Host side: argument validation (nothing is launched on a failed check),
+// tile-configuration choice, persistent-grid sizing and asynchronous launch
+// on the caller's stream.  The library holds no device memory of its own.
+// The API mirrors the operations of the DeepGEMM digest (GeekNews topic
+// 19459): "GEMM arayuzu ve yerlesim kisitlari" (NT dense GEMM, fp32 scale
+// factors with a transposed LHS layout), "Dense ve Grouped GEMM" (contiguous
+// and masked M-grouped forms) and "Yardimci fonksiyonlar ve ortam
+// degiskenleri" (CU cap, contiguous-layout alignment query).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fp8gemm.h"
+#include "cast_kernel.hpp"
+#include "gemm_kernel.hpp"
+
+#define FG_TRY(x)                    \
+  do {                               \
+    fg_status st__ = (x);            \
+    if (st__ != FG_OK) return st__;  \
+  } while (0)
+#define FG_TRY_ST FG_TRY
+
+namespace {
+
+thread_local std::string g_err;
+int g_num_cus_cap = 0;
+
+fg_status fail(fg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device properties, looked up once per device.
+struct DeviceInfo {
+  int cus = 0;
+  bool ok = false;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+fg_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FG_EHIP, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev[dev].ok) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(FG_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    g_dev[dev].cus = n;
+    g_dev[dev].ok = true;
+  }
+  *cus = g_dev[dev].cus;
+  return FG_OK;
+}
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM configurations.
+
+using CfgDefault = fg::TileCfg<128, 128, 64, 64>;
+using CfgBig = fg::BigCfg<256, 256, 4, 2>;
+
+template <class K>
+int occupancy_of(K kernel, int threads, int* cache) {
+  if (*cache == 0) {
+    int o = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, threads, 0);
+    *cache = (e == hipSuccess && o >= 1) ? o : 1;
+  }
+  return *cache;
+}
+
+fg_status launch_grid(int occ, int64_t slots, int64_t* grid) {
+  int cus = 0;
+  fg_status st = device_cus(&cus);
+  if (st != FG_OK) return st;
+  if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
+  int64_t g = (int64_t)cus * occ;
+  if (g > slots) g = slots;
+  if (g < 1) g = 1;
+  *grid = g;
+  return FG_OK;
+}
+
+void print_config(const char* what, const fg::GemmParams& p, int bm, int bn, int threads, int64_t grid, int occ) {
+  if (env_flag("FG_PRINT_CONFIGS")) {
+    fprintf(stderr, "[fp8gemm] %s M=%d N=%d K=%d G=%d tile=%dx%d threads=%d tiles=%d grid=%lld occ=%d\n", what, p.rows,
+            p.N, p.K, p.G, bm, bn, threads, p.num_tiles, (long long)grid, occ);
+  }
+}
+
+template <class C, int L>
+fg_status launch_gemm(fg::GemmParams& p, hipStream_t stream, const char* what) {
+  static int occ_cache = 0;
+  const int occ = occupancy_of(fg::gemm_fp8_kernel<C, L>, C::THREADS, &occ_cache);
+  p.group_m = 8;
+  int64_t grid = 0;
+  FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
+  print_config(what, p, C::BM, C::BN, C::THREADS, grid, occ);
+  hipLaunchKernelGGL((fg::gemm_fp8_kernel<C, L>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return FG_OK;
+}
+
+template <class C, int L>
+fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
+  static int occ_cache = 0;
+  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L>, C::THREADS, &occ_cache);
+  p.group_m = 8;
+  int64_t grid = 0;
+  FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
+  print_config(what, p, C::BM, C::BN, C::THREADS, grid, occ);
+  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return FG_OK;
+}
+
+// Tiles the large kernel would have; it is used when they cover at least
+// half of the device, otherwise the 128x128 kernel spreads the work wider.
+// FG_FORCE_CONFIG=big|small overrides the choice (tuning and tests).
+bool prefer_big(int64_t big_tiles) {
+  const char* f = getenv("FG_FORCE_CONFIG");
+  if (f && strcmp(f, "big") == 0) return true;
+  if (f && strcmp(f, "small") == 0) return false;
+  int cus = 0;
+  if (device_cus(&cus) != FG_OK) return true;
+  return big_tiles * 2 >= cus;
+}
+
+fg_status check_ld(int64_t ld, int64_t row, int64_t mult, const char* name) {
+  if (ld < row) return fail(FG_EINVAL, "%s=%lld is smaller than the row length %lld", name, (long long)ld, (long long)row);
+  if (ld % mult) return fail(FG_EALIGN, "%s=%lld is not a multiple of %lld", name, (long long)ld, (long long)mult);
+  return FG_OK;
+}
+
+
+fg_status check_ptr(const void* p, uintptr_t align, const char* name) {
+  if (!p) return fail(FG_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(FG_EALIGN, "%s is not %u-byte aligned", name, (unsigned)align);
+  return FG_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Buffer offsets inside a tile are 32-bit: rows of up to 16 MiB.
+constexpr int64_t kMaxLd = (int64_t)1 << 24;
+
+fg_status check_row_bytes(int64_t lda, int64_t ldb) {
+  if (lda > kMaxLd || ldb > kMaxLd) return fail(FG_EUNSUPPORTED, "operand rows above 16 MiB");
+  return FG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                      const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* stream) {
+  g_err.clear();
+  if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M == 0 || N == 0) return FG_OK;
+  if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
+  FG_TRY(check_ptr(D, 2, "D"));
+  FG_TRY(check_ld(ldd, N, 1, "ldd"));
+  if (K > 0) {
+    FG_TRY(check_ptr(A, 16, "A"));
+    FG_TRY(check_ptr(B, 16, "B"));
+    FG_TRY(check_ptr(sa, 4, "sa"));
+    FG_TRY(check_ptr(sb, 4, "sb"));
+    FG_TRY(check_ld(lda, K, 16, "lda"));
+    FG_TRY(check_ld(ldb, K, 16, "ldb"));
+    FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+    FG_TRY(check_row_bytes(lda, ldb));
+  }
+  fg::GemmParams p{};
+  p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  if (K > 0) {
+    using C = CfgBig;
+    const int64_t tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+    if (prefer_big(tm * tn) && tm * tn < ((int64_t)1 << 30)) {
+      p.tiles_m = (int)tm;
+      p.tiles_n = (int)tn;
+      p.num_tiles = (int)(tm * tn);
+      return launch_big<C, fg::kDense>(p, (hipStream_t)stream, "gemm_fp8_nt");
+    }
+  }
+  using C = CfgDefault;
+  p.tiles_m = (M + C::BM - 1) / C::BM;
+  p.tiles_n = (N + C::BN - 1) / C::BN;
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  return launch_gemm<C, fg::kDense>(p, (hipStream_t)stream, "gemm_fp8_nt");
+}
+
+fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t ld_sa, const uint8_t* B,
+                                      const float* sb, const int32_t* m_indices, uint16_t* D, int M_total, int N,
+                                      int K, int G, void* stream) {
+  g_err.clear();
+  if (M_total < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_total=%d N=%d K=%d", M_total, N, K);
+  if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M_total % 128) return fail(FG_EALIGN, "M_total=%d is not a multiple of 128", M_total);
+  if (M_total == 0 || N == 0) return FG_OK;
+  if (M_total > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_total or N above 2^30");
+  FG_TRY(check_ptr(D, 2, "D"));
+  FG_TRY(check_ptr(m_indices, 4, "m_indices"));
+  if (K > 0) {
+    FG_TRY(check_ptr(A, 16, "A"));
+    FG_TRY(check_ptr(B, 16, "B"));
+    FG_TRY(check_ptr(sa, 4, "sa"));
+    FG_TRY(check_ptr(sb, 4, "sb"));
+    FG_TRY(check_ld(ld_sa, M_total, 1, "ld_sa"));
+    FG_TRY(check_row_bytes(K, K));
+  }
+  fg::GemmParams p{};
+  p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
+  p.m_indices = m_indices;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  if (K > 0) {
+    // 256-row tiles: a tile whose halves hold different experts runs as two segments
+    using C = CfgBig;
+    p.tiles_m = (M_total + C::BM - 1) / C::BM;
+    p.tiles_n = (N + C::BN - 1) / C::BN;
+    p.num_tiles = p.tiles_m * p.tiles_n;
+    return launch_big<C, fg::kContiguous>(p, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
+  }
+  using C = CfgDefault;
+  static_assert(128 % C::BM == 0, "contiguous tiles must not straddle a 128-row expert block");
+  p.tiles_m = M_total / C::BM;
+  p.tiles_n = (N + C::BN - 1) / C::BN;
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  return launch_gemm<C, fg::kContiguous>(p, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
+}
+
+fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_sa, const uint8_t* B, const float* sb,
+                                  const int32_t* masked_m, uint16_t* D, int G, int M_cap, int N, int K,
+                                  int expected_m, void* stream) {
+  g_err.clear();
+  (void)expected_m;
+  if (M_cap < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_cap=%d N=%d K=%d", M_cap, N, K);
+  if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M_cap == 0 || N == 0) return FG_OK;
+  if (M_cap > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_cap or N above 2^30");
+  FG_TRY(check_ptr(D, 2, "D"));
+  FG_TRY(check_ptr(masked_m, 4, "masked_m"));
+  if (K > 0) {
+    FG_TRY(check_ptr(A, 16, "A"));
+    FG_TRY(check_ptr(B, 16, "B"));
+    FG_TRY(check_ptr(sa, 4, "sa"));
+    FG_TRY(check_ptr(sb, 4, "sb"));
+    FG_TRY(check_ld(ld_sa, M_cap, 1, "ld_sa"));
+    FG_TRY(check_row_bytes(K, K));
+  }
+  fg::GemmParams p{};
+  p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
+  p.masked_m = masked_m;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  if (K > 0) {
+    using C = CfgBig;
+    p.tiles_m = (M_cap + C::BM - 1) / C::BM;
+    p.tiles_n = (N + C::BN - 1) / C::BN;
+    const int64_t slots = (int64_t)G * p.tiles_m * p.tiles_n;
+    if (slots > (int64_t)1 << 30) return fail(FG_EUNSUPPORTED, "too many tiles");
+    p.num_tiles = (int)slots;
+    return launch_big<C, fg::kMasked>(p, (hipStream_t)stream, "gemm_fp8_grouped_masked");
+  }
+  using C = CfgDefault;
+  p.tiles_m = (M_cap + C::BM - 1) / C::BM;
+  p.tiles_n = (N + C::BN - 1) / C::BN;
+  const int64_t slots = (int64_t)G * p.tiles_m * p.tiles_n;
+  if (slots > (int64_t)1 << 30) return fail(FG_EUNSUPPORTED, "too many tiles");
+  p.num_tiles = (int)slots;
+  return launch_gemm<C, fg::kMasked>(p, (hipStream_t)stream, "gemm_fp8_grouped_masked");
+}
+
+fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa, int M, int K,
+                             void* stream) {
+  g_err.clear();
+  if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(x, 16, "x"));
+  FG_TRY(check_ptr(q, 8, "q"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ld(ldx, K, 4, "ldx"));
+  FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+  const int64_t lanes = (int64_t)M * (K / 128) * 16;
+  const int64_t blocks = (lanes + 255) / 256;
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL(fg::cast_per_token_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, ldx, q,
+                     sa, ld_sa, M, K, lanes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_token launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb, int N, int K, void* stream) {
+  g_err.clear();
+  if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (N == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(w, 16, "w"));
+  FG_TRY(check_ptr(q, 4, "q"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(ldw, K, 4, "ldw"));
+  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL(fg::cast_per_block_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
+                     sb, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+int fg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+void fg_set_num_cus(int n) { g_num_cus_cap = n > 0 ? n : 0; }
+
+int fg_get_num_cus(void) {
+  if (g_num_cus_cap > 0) return g_num_cus_cap;
+  int cus = 0;
+  if (device_cus(&cus) != FG_OK) return 0;
+  return cus;
+}
+
+const char* fg_last_error(void) { return g_err.c_str(); }
+
+const char* fg_version(void) { return "fp8gemm-gfx950 0.1"; }
+
+}  // extern "C"

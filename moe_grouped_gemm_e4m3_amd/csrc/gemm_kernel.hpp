@@ -1,0 +1,671 @@
+// gemm_kernel.hpp -- gfx950 FP8 e4m3 GEMM with per-128-K-slice fp32 promotion.
+//
+// Computes D = bf16( sum_kb P_kb * sa[kb][m] * sb[n/128][kb] ) where P_kb is the
+// fp32 matrix-core partial of one 128-wide K slice (DeepGEMM digest, GeekNews
+// topic 19459, "GEMM arayuzu ve yerlesim kisitlari" for the NT operation;
+// GeekNews topic 19444 opening bullets and 7minutos.es "Detalles y beneficios
+// tecnicos" for the two-level accumulation).  One kernel body serves the
+// dense, contiguous-grouped and masked-grouped forms ("Dense ve Grouped GEMM"
+// of the same digest); they differ only in how a tile id becomes a problem
+// tile and which output rows may be stored.
+//
+// Mapping to CDNA4:
+//  * v_mfma_f32_16x16x128_f8f6f4 computes one 16x16 output block over a whole
+//    128-deep K slice, so each MFMA result *is* a slice partial P (C input 0),
+//    and the promotion is one v_fma_f32 per element per slice.
+//  * The MFMA's first operand is the B (weight) fragment and its second the A
+//    fragment, so the result block is transposed: lane l holds activation row
+//    m = l%16 and 4 weight rows.  The activation scale is then a per-lane
+//    register and the weight scale a per-wave scalar: s = sa[m] * sb.
+//  * Weight rows are permuted inside each wave's N range so that after the
+//    slices each lane owns WN/4 consecutive output columns (vector stores).
+//  * Operands are staged through double-buffered LDS with 16-byte chunks
+//    XOR-swizzled per row (conflict-free 128-bit fragment reads); the next
+//    slice's global loads are in flight during the current slice's MFMAs.
+//  * A persistent grid walks tiles in a grouped-M raster; consecutive tiles of
+//    one raster window land on one XCD (workgroups are dealt to the 8 XCDs
+//    round-robin) so they share that XCD's L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fg {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum LayoutKind { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+struct GemmParams {
+  const uint8_t* A;  // dense/contiguous: [rows, K] (lda); masked: [G, M_cap, K] packed
+  int64_t lda;       // bytes
+  const float* sa;   // [Kb][ld_sa] (masked: per group)
+  int64_t ld_sa;     // floats
+  const uint8_t* B;  // [N, K] (ldb) or [G, N, K] packed
+  int64_t ldb;       // bytes
+  const float* sb;   // [Nb][Kb] or [G][Nb][Kb]
+  uint16_t* D;       // [rows, N] (ldd) or [G, M_cap, N]
+  int64_t ldd;       // elements
+  const int32_t* m_indices;  // contiguous
+  const int32_t* masked_m;   // masked
+  int rows;     // dense: M; contiguous: M_total; masked: M_cap
+  int N, K, G;
+  int Kb, Nb;
+  int tiles_m, tiles_n;  // per group
+  int num_tiles;         // tile slots walked by the persistent grid
+  int group_m;           // raster band height in tiles
+};
+
+// Position of a workgroup in the persistent walk such that the workgroups of
+// one XCD take consecutive work ids.
+__device__ __forceinline__ int xcd_local_id(int b, int grid) {
+  if (grid & 7) return b;
+  return (b & 7) * (grid >> 3) + (b >> 3);
+}
+
+// Grouped-M raster: bands of group_m tile rows, walked column by column.
+__device__ __forceinline__ void raster(int w, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int band_size = group_m * tiles_n;
+  const int band = w / band_size;
+  const int first = band * group_m;
+  const int rows = min(group_m, tiles_m - first);
+  const int idx = w - band * band_size;
+  tm = first + idx % rows;
+  tn = idx / rows;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// XOR swizzles of the 16-byte chunk index inside a 128-byte LDS row.
+// A rows are read 16 consecutive rows at a time.
+__device__ __forceinline__ int swz_a(int row) { return row & 7; }
+// B rows are read in the permuted order n = Q*(i/4) + 4t + i%4 (Q = WN/4), so
+// the 8 rows of one lane octet are {4t+j, Q+4t+j}: mix bit log2(Q) in.
+template <int Q>
+__device__ __forceinline__ int swz_b(int row) {
+  return (row & 3) | (((row / Q) & 1) << 2);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;  // v_cvt_pk_bf16_f32: round to nearest even
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int THREADS = WAVES_M * WAVES_N * 64;
+  static constexpr int SM = WM / 16, SN = WN / 16;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int CA = BM * 8 / THREADS;  // 16-byte chunks per thread per slice
+  static constexpr int CB = BN * 8 / THREADS;
+  static_assert(BM % WM == 0 && BN % WN == 0, "tile");
+  static_assert(WM % 16 == 0 && WN % 32 == 0 && WN <= 128 && 128 % WN == 0, "wave tile");
+  static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "loader");
+};
+
+// Everything a workgroup needs to know about the tile it computes.
+struct Tile {
+  const uint8_t* A;   // row 0 of the (group's) A
+  const float* sa;    // (group's) activation scales
+  const uint8_t* B;   // row 0 of the (group's / expert's) B
+  const float* sb;    // (group's / expert's) weight scales
+  uint16_t* D;        // row 0 of the (group's) D
+  int m0, n0;
+  int rows_alloc;     // rows addressable in A / sa (reads clamp to it)
+  int rows_valid;     // dense/masked: rows < rows_valid are stored
+  int expert;         // contiguous: rows whose index equals it are stored
+};
+
+template <int L>
+__device__ __forceinline__ bool resolve_tile(const GemmParams& p, int w, int BM, int BN, Tile& t) {
+  int tm, tn;
+  if (L == kMasked) {
+    const int per_group = p.tiles_m * p.tiles_n;
+    const int g = w / per_group;
+    raster(w - g * per_group, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int valid = min(max(p.masked_m[g], 0), p.rows);
+    if (tm * BM >= valid) return false;
+    const int64_t Kb = p.Kb;
+    t.A = p.A + (int64_t)g * p.rows * p.K;
+    t.sa = p.sa + (int64_t)g * Kb * p.ld_sa;
+    t.B = p.B + (int64_t)g * p.N * p.K;
+    t.sb = p.sb + (int64_t)g * p.Nb * Kb;
+    t.D = p.D + (int64_t)g * p.rows * p.N;
+    t.rows_valid = valid;
+    t.expert = 0;
+  } else {
+    raster(w, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    t.A = p.A;
+    t.sa = p.sa;
+    t.D = p.D;
+    t.rows_valid = p.rows;
+    if (L == kContiguous) {
+      // expert of this 128-aligned row block: the largest index in it
+      const int lane = threadIdx.x & 63;
+      int e = -1;
+      for (int r = lane; r < BM; r += 64) {
+        const int m = min(tm * BM + r, p.rows - 1);
+        e = max(e, p.m_indices[m]);
+      }
+      e = wave_max(e);
+      e = __builtin_amdgcn_readfirstlane(e);
+      if (e < 0) return false;  // padding only
+      t.expert = e;
+      t.B = p.B + (int64_t)e * p.N * p.K;
+      t.sb = p.sb + (int64_t)e * p.Nb * p.Kb;
+    } else {
+      t.expert = 0;
+      t.B = p.B;
+      t.sb = p.sb;
+    }
+  }
+  t.m0 = tm * BM;
+  t.n0 = tn * BN;
+  t.rows_alloc = p.rows;
+  return true;
+}
+
+// Raw buffer resource over [base, base + bytes): loads at or past the end
+// return zeros, which is how rows beyond M or N are fed to the MFMAs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+template <class C, int L>
+__global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  constexpr int SM = C::SM, SN = C::SN, CA = C::CA, CB = C::CB;
+  constexpr int NT = C::THREADS;
+  constexpr int Q = WN / 4;
+  constexpr int ROWS_PER_PASS = NT / 8;  // loader rows covered by one pass of the workgroup
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
+  const int l16 = lane & 15;
+  const int kq = lane >> 4;  // which 32-byte quarter of the slice this lane feeds
+
+  // loader: thread -> (row, chunk); passes add ROWS_PER_PASS rows
+  const int ld_row = tid >> 3, ld_c = tid & 7;
+  // swizzles depend on row & 7 (A) and row bits 0,1,log2(Q) (B); ROWS_PER_PASS
+  // is a multiple of 8 and of 2Q, so they are the same on every pass.
+  static_assert(ROWS_PER_PASS % 8 == 0 && ROWS_PER_PASS % (2 * Q) == 0, "loader swizzle invariance");
+  const int a_dst0 = ld_row * 128 + ((ld_c ^ swz_a(ld_row)) << 4);
+  const int b_dst0 = C::A_BYTES + ld_row * 128 + ((ld_c ^ swz_b<Q>(ld_row)) << 4);
+
+  // fragment reads: the swizzle of a fragment row does not depend on the
+  // subtile index, so one base offset per half suffices.
+  const int a_row0 = wm * WM + l16;
+  const int b_row0 = wn * WN + Q * (l16 >> 2) + (lane & 3);
+  int a_frag0[2], b_frag0[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    a_frag0[h] = a_row0 * 128 + (((2 * kq + h) ^ swz_a(a_row0)) << 4);
+    b_frag0[h] = C::A_BYTES + b_row0 * 128 + (((2 * kq + h) ^ swz_b<Q>(b_row0)) << 4);
+  }
+
+  const int grid = gridDim.x;
+  const int local = xcd_local_id(blockIdx.x, grid);
+
+  for (int it = 0;; ++it) {
+    const int w = it * grid + local;
+    if (w >= p.num_tiles) break;
+    Tile t;
+    if (!resolve_tile<L>(p, w, BM, BN, t)) continue;
+
+    __syncthreads();  // the previous tile's last LDS stage is no longer read
+
+    // A rows [m0, rows_alloc) and B rows [n0, N) as buffer ranges
+    const uint8_t* a_base = t.A + (int64_t)t.m0 * p.lda;
+    const uint8_t* b_base = t.B + (int64_t)t.n0 * p.ldb;
+    const int64_t a_bytes = (int64_t)(t.rows_alloc - t.m0 - 1) * p.lda + p.K;
+    const int64_t b_bytes = (int64_t)(p.N - t.n0 - 1) * p.ldb + p.K;
+    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a_base, a_bytes);
+    const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(b_base, b_bytes);
+    const int a_voff = ld_row * (int)p.lda + ld_c * 16;
+    const int b_voff = ld_row * (int)p.ldb + ld_c * 16;
+    const int a_pass = ROWS_PER_PASS * (int)p.lda;
+    const int b_pass = ROWS_PER_PASS * (int)p.ldb;
+
+    // this lane's activation rows for the scales (clamped: scales of rows
+    // past the end only multiply zeros)
+    int sa_row[SM];
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) sa_row[ms] = min(t.m0 + a_row0 + ms * 16, t.rows_alloc - 1);
+    const int nb_wave = min((t.n0 + wn * WN) >> 7, p.Nb - 1);
+    const float* sb_wave = t.sb + (int64_t)nb_wave * p.Kb;
+
+    float acc[SM][SN][4];
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms)
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
+
+    const int Kb = p.Kb;
+    i32x4 ra[CA], rb[CB];
+    if (Kb > 0) {
+#pragma unroll
+      for (int i = 0; i < CA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, a_voff + i * a_pass, 0, 0);
+#pragma unroll
+      for (int i = 0; i < CB; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, b_voff + i * b_pass, 0, 0);
+#pragma unroll
+      for (int i = 0; i < CA; ++i) *(i32x4*)(smem + a_dst0 + i * ROWS_PER_PASS * 128) = ra[i];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) *(i32x4*)(smem + b_dst0 + i * ROWS_PER_PASS * 128) = rb[i];
+      __syncthreads();
+    }
+
+    for (int kb = 0; kb < Kb; ++kb) {
+      const bool more = kb + 1 < Kb;
+      if (more) {
+        const int ko = (kb + 1) * 128;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, a_voff + i * a_pass, ko, 0);
+#pragma unroll
+        for (int i = 0; i < CB; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, b_voff + i * b_pass, ko, 0);
+      }
+      // slice scales: s = sa[kb][m] * sb[nb][kb]
+      const float sbv = sb_wave[kb];
+      const float* sa_k = t.sa + (int64_t)kb * p.ld_sa;
+      float s[SM];
+#pragma unroll
+      for (int ms = 0; ms < SM; ++ms) s[ms] = sa_k[sa_row[ms]] * sbv;
+
+      const uint8_t* st = smem + (kb & 1) * C::STAGE;
+      i32x8 af[SM];
+#pragma unroll
+      for (int ms = 0; ms < SM; ++ms) {
+        const i32x4 lo = *(const i32x4*)(st + a_frag0[0] + ms * 16 * 128);
+        const i32x4 hi = *(const i32x4*)(st + a_frag0[1] + ms * 16 * 128);
+        af[ms] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt) {
+        const i32x4 lo = *(const i32x4*)(st + b_frag0[0] + tt * 4 * 128);
+        const i32x4 hi = *(const i32x4*)(st + b_frag0[1] + tt * 4 * 128);
+        const i32x8 bf = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int ms = 0; ms < SM; ++ms) {
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ms][tt][r] = __builtin_fmaf(P[r], s[ms], acc[ms][tt][r]);
+        }
+      }
+      if (more) {
+        uint8_t* nx = smem + ((kb + 1) & 1) * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) *(i32x4*)(nx + a_dst0 + i * ROWS_PER_PASS * 128) = ra[i];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) *(i32x4*)(nx + b_dst0 + i * ROWS_PER_PASS * 128) = rb[i];
+      }
+      __syncthreads();
+    }
+
+    // ---- epilogue: each lane owns Q consecutive columns of SM rows ----
+    const int n_base = t.n0 + wn * WN + Q * kq;
+    const bool vec = (p.ldd & 7) == 0 && ((uintptr_t)p.D & 15) == 0;
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) {
+      const int m = t.m0 + a_row0 + ms * 16;
+      bool ok;
+      if (L == kContiguous) {
+        ok = m < t.rows_alloc && p.m_indices[m] == t.expert;
+      } else {
+        ok = m < t.rows_valid;
+      }
+      if (!ok) continue;
+      uint16_t* drow = t.D + (int64_t)m * p.ldd;
+      uint32_t pk[Q / 2];
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt) {
+        pk[2 * tt] = pack_bf16x2(acc[ms][tt][0], acc[ms][tt][1]);
+        pk[2 * tt + 1] = pack_bf16x2(acc[ms][tt][2], acc[ms][tt][3]);
+      }
+      if (vec && n_base + Q <= p.N) {
+#pragma unroll
+        for (int v = 0; v < Q / 8; ++v) {
+          const i32x4 o = {(int)pk[4 * v], (int)pk[4 * v + 1], (int)pk[4 * v + 2], (int)pk[4 * v + 3]};
+          *(i32x4*)(drow + n_base + 8 * v) = o;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          if (n_base + j < p.N) drow[n_base + j] = (uint16_t)(pk[j >> 1] >> ((j & 1) * 16));
+        }
+      }
+    }
+  }
+}
+
+
+// ===========================================================================
+// Large-tile kernel: BM x BN workgroup tile, WAVES_M x WAVES_N waves (two per
+// SIMD), operands fetched straight into LDS by buffer loads (no VGPR staging),
+// double-buffered stages.  The persistent loop is flattened over (tile,
+// segment, K slice) so the first slice of the next tile is already in flight
+// while the current tile finishes and stores.  A contiguous-layout tile whose
+// two 128-row halves belong to different experts is computed as two segments
+// (one per expert, the other half's waves idle); every other tile is one
+// segment.
+// ===========================================================================
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct BigCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = NWAVES * 64;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int SM = WM / 16, SN = WN / 16;
+  static constexpr int STAGE = (BM + BN) * 128;
+  static constexpr int LOADS = (BM + BN) / 8;      // 1 KiB (8-row) loads per slice
+  static constexpr int LOADS_PER_WAVE = LOADS / NWAVES;
+  static_assert(LOADS % NWAVES == 0, "loads per wave");
+  static_assert(BM % (8 * LOADS_PER_WAVE) == 0, "a wave loads A rows or B rows, not both");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
+  static_assert(BN % 128 == 0 && 128 % WN == 0 || WN % 128 == 0, "a wave's columns share one weight-scale block");
+  static_assert(WN <= 128, "wave columns within one 128 block");
+  static_assert(BM % 128 == 0 || BM <= 128, "row halves");
+};
+
+// 16-byte chunk swizzle inside a 128-byte LDS row for the large kernel:
+// fragment reads touch 16 consecutive rows at one logical chunk.
+__device__ __forceinline__ int swz16(int row) { return (row >> 1) & 7; }
+
+struct Work {
+  const uint8_t* A;
+  const float* sa;
+  const uint8_t* B;
+  const float* sb;
+  uint16_t* D;
+  int m0, n0;
+  int rows_alloc, rows_valid;
+  int seg, nseg;      // segment of the tile and how many it has
+  int half_mask;      // contiguous: 128-row halves computed in this segment
+  int e_lo, e_hi;     // contiguous: expert of each half (-1 = padding only)
+  int w;              // tile id (< 0: no more work)
+};
+
+__device__ __forceinline__ int block_max_index(const int32_t* idx, int from, int count, int rows) {
+  const int lane = threadIdx.x & 63;
+  int e = -1;
+  for (int r = lane; r < count; r += 64) {
+    const int m = from + r;
+    if (m < rows) e = max(e, idx[m]);
+  }
+  e = wave_max(e);
+  return __builtin_amdgcn_readfirstlane(e);
+}
+
+// Resolve tile id w into its first segment; false if the tile has no work.
+template <int L, int BM, int BN>
+__device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t) {
+  int tm, tn;
+  t.w = w;
+  t.seg = 0;
+  t.nseg = 1;
+  t.half_mask = 3;
+  t.e_lo = t.e_hi = 0;
+  if (L == kMasked) {
+    const int per_group = p.tiles_m * p.tiles_n;
+    const int g = w / per_group;
+    raster(w - g * per_group, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int valid = min(max(p.masked_m[g], 0), p.rows);
+    if (tm * BM >= valid) return false;
+    const int64_t Kb = p.Kb;
+    t.A = p.A + (int64_t)g * p.rows * p.K;
+    t.sa = p.sa + (int64_t)g * Kb * p.ld_sa;
+    t.B = p.B + (int64_t)g * p.N * p.K;
+    t.sb = p.sb + (int64_t)g * p.Nb * Kb;
+    t.D = p.D + (int64_t)g * p.rows * p.ldd;
+    t.rows_valid = valid;
+  } else {
+    raster(w, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    t.A = p.A;
+    t.sa = p.sa;
+    t.D = p.D;
+    t.rows_valid = p.rows;
+    t.B = p.B;
+    t.sb = p.sb;
+    if (L == kContiguous) {
+      const int m0 = tm * BM;
+      const int half = BM >= 256 ? BM / 2 : BM;
+      const int lo = block_max_index(p.m_indices, m0, half, p.rows);
+      const int hi = BM >= 256 ? block_max_index(p.m_indices, m0 + half, half, p.rows) : -1;
+      if (lo < 0 && hi < 0) return false;
+      t.e_lo = lo;
+      t.e_hi = hi;
+      if (lo >= 0 && hi >= 0 && lo != hi) {
+        t.nseg = 2;
+        t.half_mask = 1;
+      } else {
+        t.half_mask = (lo >= 0 ? 1 : 0) | (hi >= 0 ? 2 : 0);
+      }
+      const int e = lo >= 0 ? lo : hi;
+      t.B = p.B + (int64_t)e * p.N * p.K;
+      t.sb = p.sb + (int64_t)e * p.Nb * p.Kb;
+    }
+  }
+  t.m0 = tm * BM;
+  t.n0 = tn * BN;
+  t.rows_alloc = p.rows;
+  return true;
+}
+
+// Next segment of the same tile, or the next tile with work for this workgroup.
+template <int L, int BM, int BN>
+__device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& it, int local, int grid) {
+  if (L == kContiguous && t.seg + 1 < t.nseg) {
+    t.seg += 1;
+    t.half_mask = 2;
+    t.B = p.B + (int64_t)t.e_hi * p.N * p.K;
+    t.sb = p.sb + (int64_t)t.e_hi * p.Nb * p.Kb;
+    return;
+  }
+  for (;;) {
+    ++it;
+    const int w = it * grid + local;
+    if (w >= p.num_tiles) {
+      t.w = -1;
+      return;
+    }
+    if (resolve_big<L, BM, BN>(p, w, t)) return;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Work& t, int kb, uint8_t* stage,
+                                                  int wave, int lane) {
+  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int IPW = C::LOADS_PER_WAVE;
+  const int q0 = wave * IPW;             // first 8-row load of this wave
+  const bool is_a = q0 * 8 < BM;         // wave-uniform
+  const int row0 = is_a ? q0 * 8 : q0 * 8 - BM;
+  const uint8_t* base = is_a ? t.A + (int64_t)t.m0 * p.lda : t.B + (int64_t)t.n0 * p.ldb;
+  const int64_t ld = is_a ? p.lda : p.ldb;
+  const int rows_left = is_a ? t.rows_alloc - t.m0 : p.N - t.n0;
+  const int64_t bytes = (int64_t)(rows_left - 1) * ld + p.K;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+  const int comb0 = q0 * 8 + (lane >> 3);  // combined (A|B) row of this lane in load 0
+  const int p_chunk = lane & 7;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int comb = comb0 + 8 * j;
+    const int r = row0 + 8 * j + (lane >> 3);
+    const int c = p_chunk ^ swz16(comb);
+    const int voff = r * (int)ld + c * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (q0 + j) * 1024),
+                                             16, voff, kb * 128, 0, 0);
+  }
+}
+
+template <class C, int L>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  constexpr int SM = C::SM, SN = C::SN;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
+  const int l16 = lane & 15;
+  const int kq = lane >> 4;
+  const int half = (wm * WM) / 128;  // 128-row half of the tile this wave's rows lie in
+
+  // fragment read offsets (the swizzle depends only on the row's low 4 bits)
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ra = wm * WM + l16;
+    const int rb = BM + wn * WN + l16;
+    a_off[h] = ra * 128 + (((2 * kq + h) ^ swz16(ra)) << 4);
+    b_off[h] = rb * 128 + (((2 * kq + h) ^ swz16(rb)) << 4);
+  }
+
+  const int grid = gridDim.x;
+  const int local = xcd_local_id(blockIdx.x, grid);
+  const int Kb = p.Kb;
+
+  Work cur;
+  int it = 0;
+  cur.w = -1;
+  {
+    const int w = local;
+    if (w < p.num_tiles && resolve_big<L, BM, BN>(p, w, cur)) {
+    } else {
+      advance_big<L, BM, BN>(p, cur, it, local, grid);
+    }
+  }
+  if (cur.w < 0) return;
+  Work nxt = cur;
+  int it_n = it;
+
+  issue_slice_loads<C>(p, cur, 0, smem[0], wave, lane);
+
+  float acc[SM][SN][4];
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms)
+#pragma unroll
+    for (int tt = 0; tt < SN; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  int kb = 0;
+  int stage = 0;
+  for (;;) {
+    // ---- what comes after (cur, kb): prefetch it into the other stage ----
+    int kb_n = kb + 1;
+    if (kb_n == Kb) {
+      kb_n = 0;
+      advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
+    }
+    const bool have_next = nxt.w >= 0;
+    if (have_next) issue_slice_loads<C>(p, nxt, kb_n, smem[stage ^ 1], wave, lane);
+
+    // ---- compute slice kb of cur ----
+    const bool active = (L == kContiguous) ? (((cur.half_mask >> half) & 1) != 0)
+                                           : (cur.m0 + wm * WM < cur.rows_valid);
+    if (active) {
+      const int nb = min((cur.n0 + wn * WN) >> 7, p.Nb - 1);
+      const float sbv = cur.sb[(int64_t)nb * Kb + kb];
+      const float* sa_k = cur.sa + (int64_t)kb * p.ld_sa;
+      float s[SM];
+#pragma unroll
+      for (int ms = 0; ms < SM; ++ms) {
+        const int m = min(cur.m0 + wm * WM + ms * 16 + l16, cur.rows_alloc - 1);
+        s[ms] = sa_k[m] * sbv;
+      }
+      const uint8_t* st = smem[stage];
+      i32x8 af[SM];
+#pragma unroll
+      for (int ms = 0; ms < SM; ++ms) {
+        const i32x4 lo = *(const i32x4*)(st + a_off[0] + ms * 2048);
+        const i32x4 hi = *(const i32x4*)(st + a_off[1] + ms * 2048);
+        af[ms] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt) {
+        const i32x4 lo = *(const i32x4*)(st + b_off[0] + tt * 2048);
+        const i32x4 hi = *(const i32x4*)(st + b_off[1] + tt * 2048);
+        const i32x8 bf = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int ms = 0; ms < SM; ++ms) {
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ms][tt][r] = __builtin_fmaf(P[r], s[ms], acc[ms][tt][r]);
+        }
+      }
+    }
+
+    // ---- tile done: store its rows and reset the accumulators ----
+    if (kb == Kb - 1 && cur.seg == cur.nseg - 1) {
+      int e_w = 0;
+      if (L == kContiguous) e_w = half == 0 ? cur.e_lo : cur.e_hi;
+      const bool vec = (p.ldd & 3) == 0 && ((uintptr_t)p.D & 7) == 0;
+#pragma unroll
+      for (int ms = 0; ms < SM; ++ms) {
+        const int m = cur.m0 + wm * WM + ms * 16 + l16;
+        bool ok;
+        if (L == kContiguous) {
+          ok = e_w >= 0 && m < cur.rows_alloc && p.m_indices[m] == e_w;
+        } else {
+          ok = m < cur.rows_valid;
+        }
+        if (ok) {
+          uint16_t* drow = cur.D + (int64_t)m * p.ldd;
+#pragma unroll
+          for (int tt = 0; tt < SN; ++tt) {
+            const int n = cur.n0 + wn * WN + tt * 16 + 4 * kq;
+            const uint32_t lo = pack_bf16x2(acc[ms][tt][0], acc[ms][tt][1]);
+            const uint32_t hi = pack_bf16x2(acc[ms][tt][2], acc[ms][tt][3]);
+            if (vec && n + 4 <= p.N) {
+              *(uint2*)(drow + n) = make_uint2(lo, hi);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                if (n + j < p.N) drow[n + j] = (uint16_t)((j < 2 ? lo : hi) >> ((j & 1) * 16));
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < SN; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
+      }
+    }
+
+    if (!have_next) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    cur = nxt;
+    kb = kb_n;
+    stage ^= 1;
+  }
+}
+
+}  // namespace fg

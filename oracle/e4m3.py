@@ -49,6 +49,7 @@ def decode(codes) -> np.ndarray:
 # neighbour above 448 so that the rounding boundary 464 is placed correctly;
 # landing on it means the value is not representable.
 _POS_GRID = np.concatenate([DECODE_TABLE[:0x7F], [480.0]])
+_CHUNK = 1 << 20
 
 
 def encode_rne(values) -> np.ndarray:
@@ -60,7 +61,14 @@ def encode_rne(values) -> np.ndarray:
     past it) has no finite e4m3fn neighbour: it raises, since the method never
     produces one (|x/s| <= 448 * (1 + 2^-23) by construction of s).
     """
-    v = np.asarray(values, dtype=np.float64)
+    v = np.asarray(values)
+    if v.size > _CHUNK:  # same element-wise rule, evaluated in cache-sized pieces
+        flat = v.reshape(-1)
+        out = np.empty(flat.shape, np.uint8)
+        for i in range(0, flat.size, _CHUNK):
+            out[i:i + _CHUNK] = encode_rne(flat[i:i + _CHUNK])
+        return out.reshape(v.shape)
+    v = v.astype(np.float64)
     if np.isnan(v).any():
         raise ValueError("NaN input to e4m3 encode")
     mag = np.abs(v)

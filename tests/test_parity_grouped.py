@@ -1,0 +1,214 @@
+"""Contiguous and masked M-grouped GEMMs on the GPU against the CPU oracle.
+
+Indexing and masking are checked bit for bit: D is pre-filled with a NaN
+sentinel and every row the oracle marks invalid must still hold it."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gemm as ogemm, quant
+from tests.helpers import (
+    SENTINEL_BF16, announce, assert_close, bf16_bits, bf16_to_f64, dev_f32, dev_sa, dev_u8,
+    exact_regime, sentinel_like,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize_grouped_B(B32: np.ndarray):
+    qs, ss = zip(*(quant.quantize_per_block(b) for b in B32))
+    return np.stack(qs), np.stack(ss)
+
+
+def run_contig(fg, qa, sa, qb, sb, idx):
+    M, N = qa.shape[0], qb.shape[1]
+    D = sentinel_like((M, N))
+    fg.gemm_fp8_grouped_contiguous(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb),
+                                   torch.from_numpy(np.asarray(idx, np.int32)).cuda(), D)
+    torch.cuda.synchronize()
+    return D
+
+
+def run_masked(fg, qa, sa, qb, sb, mask, expected_m=0):
+    G, Mc, K = qa.shape
+    N = qb.shape[1]
+    D = sentinel_like((G, Mc, N))
+    fg.gemm_fp8_grouped_masked(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb),
+                               torch.from_numpy(np.asarray(mask, np.int32)).cuda(), D, expected_m=expected_m)
+    torch.cuda.synchronize()
+    return D
+
+
+# ---------------------------------------------------------------- contiguous
+
+
+@pytest.mark.parametrize("rows,N,K", [([130, 0, 100], 256, 256), ([1, 255, 128, 64], 520, 384), ([384], 136, 1024)])
+def test_contiguous_uneven_groups(gpu_lib, rows, N, K):
+    announce(f"contiguous rows={rows} N={N} K={K}")
+    A32, B32, idx = synth.contiguous_problem(rows, N, K, seed=len(rows) + N)
+    qa, sa = quant.quantize_per_token(A32.numpy())
+    qb, sb = quantize_grouped_B(B32.numpy())
+    D = run_contig(gpu_lib, qa, sa, qb, sb, idx)
+    X, valid, S = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, idx, with_magnitude=True)
+    y = bf16_to_f64(D)
+    assert_close(y[valid], X[valid], S[valid], K // 128, "contiguous")
+    assert (bf16_bits(D)[~valid] == SENTINEL_BF16).all()
+
+
+def test_contiguous_exact_regime_bitwise(gpu_lib):
+    announce("contiguous exact regime")
+    rng = np.random.default_rng(3)
+    idx = synth.contiguous_indices([200, 60, 0, 128], pad_to=128)
+    M, N, K, G = idx.shape[0], 264, 512, 4
+    qa, sa, _, _ = exact_regime(rng, M, N, K)
+    _, _, qb, sb = exact_regime(rng, 1, N, K, groups=(1, G))
+    D = run_contig(gpu_lib, qa, sa, qb, sb, idx)
+    X, valid = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, idx)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
+def test_contiguous_equals_dense_per_group(gpu_lib):
+    announce("contiguous vs dense per group")
+    A32, B32, idx = synth.contiguous_problem([256, 128, 384], 384, 768, seed=8)
+    qa, sa = quant.quantize_per_token(A32.numpy())
+    qb, sb = quantize_grouped_B(B32.numpy())
+    Dc = bf16_bits(run_contig(gpu_lib, qa, sa, qb, sb, idx))
+    for e in range(3):
+        rows = np.nonzero(idx == e)[0]
+        Dd = torch.empty(len(rows), 384, dtype=torch.bfloat16, device="cuda")
+        gpu_lib.gemm_fp8_nt(dev_u8(qa[rows]), dev_sa(sa[:, rows]), dev_u8(qb[e]), dev_f32(sb[e]), Dd)
+        torch.cuda.synchronize()
+        assert np.array_equal(Dc[rows], bf16_bits(Dd))
+
+
+def test_contiguous_8_experts_full_size_sampled(gpu_lib):
+    """8 experts x 4096 rows, N=4096, K=7168: GPU cast + grouped GEMM; the
+    oracle checks sampled rows of every expert against sampled column blocks."""
+    G, R, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
+    announce(f"contiguous full-size {G}x{R} N={N} K={K}")
+    A32, B32, idx = synth.contiguous_problem([R] * G, N, K, seed=0)
+    qa_d, sa_d = gpu_lib.fp8_cast_per_token(A32.cuda())
+    qb_d, sb_d = gpu_lib.fp8_cast_per_block(B32.cuda().view(G * N, K))
+    qb_d = qb_d.view(G, N, K)
+    sb_d = sb_d.view(G, N // 128, K // 128)
+    D = torch.empty(G * R, N, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.gemm_fp8_grouped_contiguous(qa_d, sa_d, qb_d, sb_d, torch.from_numpy(idx).cuda(), D)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    blocks = [0, N // 128 - 1, int(rng.integers(1, N // 128 - 1))]
+    for e in range(G):
+        rows = np.sort(rng.choice(np.arange(e * R, (e + 1) * R), 6, replace=False))
+        qa, sa = quant.quantize_per_token(A32.numpy()[rows])
+        assert np.array_equal(qa_d[torch.from_numpy(rows).cuda()].cpu().numpy(), qa)
+        Dr = D[torch.from_numpy(rows).cuda()]
+        for nb in blocks:
+            cols = slice(nb * 128, nb * 128 + 128)
+            qb, sb = quant.quantize_per_block(B32.numpy()[e, cols])
+            assert np.array_equal(qb_d[e, cols].cpu().numpy(), qb)
+            X, S = ogemm.gemm_nt(qa, sa, qb, sb, with_magnitude=True)
+            assert_close(bf16_to_f64(Dr[:, cols]), X, S, K // 128, f"expert {e} block {nb}")
+
+
+# -------------------------------------------------------------------- masked
+
+
+@pytest.mark.parametrize(
+    "mask,Mc,N,K",
+    [
+        ([0, 1, 127, 128, 129, 255, 256, 64], 256, 256, 256),
+        ([300, -4, 40, 0], 100, 136, 384),
+        ([0, 0, 0], 64, 128, 128),
+    ],
+)
+def test_masked_edges(gpu_lib, mask, Mc, N, K):
+    announce(f"masked mask={mask} Mc={Mc} N={N} K={K}")
+    G = len(mask)
+    g = torch.Generator().manual_seed(G + Mc)
+    A32 = torch.randn(G, Mc, K, generator=g).numpy()
+    B32 = torch.randn(G, N, K, generator=g).numpy()
+    qs = [quant.quantize_per_token(a) for a in A32]
+    qa = np.stack([q for q, _ in qs])
+    sa = np.stack([s for _, s in qs])
+    qb, sb = quantize_grouped_B(B32)
+    D = run_masked(gpu_lib, qa, sa, qb, sb, mask)
+    X, valid, S = ogemm.gemm_grouped_masked(qa, sa, qb, sb, mask, with_magnitude=True)
+    bits = bf16_bits(D)
+    assert (bits[~valid] == SENTINEL_BF16).all()
+    if valid.any():
+        y = bf16_to_f64(D)
+        assert_close(y[valid], X[valid], S[valid], K // 128, "masked")
+
+
+def test_masked_exact_regime_bitwise(gpu_lib):
+    announce("masked exact regime")
+    rng = np.random.default_rng(4)
+    G, Mc, N, K = 5, 96, 200, 640
+    qa, sa, qb, sb = exact_regime(rng, Mc, N, K, groups=(G, G))
+    mask = [96, 0, 33, 95, 1]
+    D = run_masked(gpu_lib, qa, sa, qb, sb, mask)
+    X, valid = ogemm.gemm_grouped_masked(qa, sa, qb, sb, mask)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
+def test_masked_full_equals_dense(gpu_lib):
+    announce("masked mask==M_cap vs dense")
+    rng = np.random.default_rng(6)
+    G, Mc, N, K = 3, 130, 264, 512
+    g = torch.Generator().manual_seed(6)
+    A32 = torch.randn(G, Mc, K, generator=g).numpy()
+    B32 = torch.randn(G, N, K, generator=g).numpy()
+    qs = [quant.quantize_per_token(a) for a in A32]
+    qa = np.stack([q for q, _ in qs])
+    sa = np.stack([s for _, s in qs])
+    qb, sb = quantize_grouped_B(B32)
+    Dm = bf16_bits(run_masked(gpu_lib, qa, sa, qb, sb, [Mc] * G))
+    for e in range(G):
+        Dd = torch.empty(Mc, N, dtype=torch.bfloat16, device="cuda")
+        gpu_lib.gemm_fp8_nt(dev_u8(qa[e]), dev_sa(sa[e]), dev_u8(qb[e]), dev_f32(sb[e]), Dd)
+        torch.cuda.synchronize()
+        assert np.array_equal(Dm[e], bf16_bits(Dd))
+
+
+@pytest.mark.parametrize("shape", synth.MASKED_16x256.shapes, ids=lambda s: "x".join(map(str, s)))
+def test_masked_decode_full_size(gpu_lib, shape):
+    """16 experts x capacity 256, seed-0 counts; GPU cast + masked GEMM; the
+    oracle checks sampled valid rows of every group (all column blocks of a
+    few groups, sampled blocks of the rest) and every invalid row is untouched."""
+    G, Mc, N, K = shape
+    announce(f"masked full-size {G}x{Mc} N={N} K={K}")
+    A32, B32, mask = synth.masked_problem(G, Mc, N, K, seed=0)
+    qa_d, sa_d = gpu_lib.fp8_cast_per_token(A32.cuda().view(G * Mc, K))
+    qa_d = qa_d.view(G, Mc, K)
+    sa_full = sa_d  # [Kb, G*Mc] view: regroup per expert into [G, Kb, ld]
+    sa_g = torch.empty(G, K // 128, Mc, dtype=torch.float32, device="cuda")
+    sa_g.copy_(sa_full.reshape(K // 128, G, Mc).permute(1, 0, 2))
+    qb_d, sb_d = gpu_lib.fp8_cast_per_block(B32.cuda().view(G * N, K))
+    qb_d, sb_d = qb_d.view(G, N, K), sb_d.view(G, N // 128, K // 128)
+    D = sentinel_like((G, Mc, N))
+    gpu_lib.gemm_fp8_grouped_masked(qa_d, sa_g, qb_d, sb_d, torch.from_numpy(mask).cuda(), D, expected_m=int(mask.mean()))
+    torch.cuda.synchronize()
+    bits = bf16_bits(D)
+    rng = np.random.default_rng(2)
+    for g in range(G):
+        v = int(mask[g])
+        assert (bits[g, v:] == SENTINEL_BF16).all(), g
+        if v == 0:
+            continue
+        rows = np.unique(np.concatenate([[0, v - 1], rng.choice(v, min(v, 4), replace=False)]))
+        qa, sa = quant.quantize_per_token(A32.numpy()[g, rows])
+        assert np.array_equal(qa_d[g, torch.from_numpy(rows).cuda()].cpu().numpy(), qa)
+        nbs = range(N // 128) if g < 2 else rng.choice(N // 128, 2, replace=False)
+        for nb in nbs:
+            cols = slice(nb * 128, nb * 128 + 128)
+            qb, sb = quant.quantize_per_block(B32.numpy()[g, cols])
+            X, S = ogemm.gemm_nt(qa, sa, qb, sb, with_magnitude=True)
+            y = bf16_to_f64(D[g, torch.from_numpy(rows).cuda(), cols])
+            assert_close(y, X, S, K // 128, f"group {g} block {nb}")
