@@ -385,9 +385,12 @@ struct BigCfg {
   static_assert(BM % 128 == 0 || BM <= 128, "row halves");
 };
 
-// 16-byte chunk swizzle inside a 128-byte LDS row for the large kernel:
-// fragment reads touch 16 consecutive rows at one logical chunk.
-__device__ __forceinline__ int swz16(int row) { return (row >> 1) & 7; }
+// 16-byte chunk swizzle inside a 128-byte LDS row for the large kernel.
+// A fragment read touches 16 consecutive rows at one logical chunk; the
+// chunk index is XORed with the row's low 3 bits (8 consecutive rows land in
+// 8 different 16-byte bank groups) and with bit 3 (rows r and r+8 of the same
+// parity also differ, for 16-lane service over 256 bytes).
+__device__ __forceinline__ int swz16(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 struct Work {
   const uint8_t* A;
@@ -516,12 +519,78 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
   }
 }
 
+// Scales of one K slice for this lane's SM rows: sa[kb][m] per row and the
+// wave's weight-block scale sb[nb][kb].  Issued one slice ahead, before that
+// slice's operand loads, so the compute never waits on them.
+template <class C>
+__device__ __forceinline__ void load_scales(const GemmParams& p, const Work& t, int kb, int wm, int wn, int l16,
+                                            float (&sa_r)[C::SM], float& sb_r) {
+  const int nb = min((t.n0 + wn * C::WN) >> 7, p.Nb - 1);
+  sb_r = t.sb[(int64_t)nb * p.Kb + kb];
+  const float* sa_k = t.sa + (int64_t)kb * p.ld_sa;
+#pragma unroll
+  for (int ms = 0; ms < C::SM; ++ms) {
+    const int m = min(t.m0 + wm * C::WM + ms * 16 + l16, t.rows_alloc - 1);
+    sa_r[ms] = sa_k[m];
+  }
+}
+
+__device__ __forceinline__ i32x8 lds_frag(const uint8_t* st, int off0, int off1) {
+  const i32x4 lo = *(const i32x4*)(st + off0);
+  const i32x4 hi = *(const i32x4*)(st + off1);
+  return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// One 128-deep K slice of the wave tile: SM x SN MFMAs, each a fresh partial
+// P, promoted into acc with s = sa * sb.  Software-pipelined by weight subtile:
+// step (tt, ms) issues the MFMA of (tt, ms) and the four promotion FMAs of
+// (tt-1, ms), so an MFMA result is read SM MFMAs after it was issued (its
+// latency and the MFMA->VALU hazard are hidden behind other MFMAs) and the
+// matrix core never waits for the promotion.  Scheduling fences keep the
+// compiler from pulling each MFMA down next to its consumers.
+template <class C>
+__device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[2], const int (&b_off)[2],
+                                          const float (&s)[C::SM], float (&acc)[C::SM][C::SN][4]) {
+  constexpr int SM = C::SM, SN = C::SN;
+  i32x8 af[SM];
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms) af[ms] = lds_frag(st, a_off[0] + ms * 2048, a_off[1] + ms * 2048);
+  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
+  f32x4 prev[SM];
+#pragma unroll
+  for (int tt = 0; tt < SN; ++tt) {
+    i32x8 bn = bf;
+    if (tt + 1 < SN) bn = lds_frag(st, b_off[0] + (tt + 1) * 2048, b_off[1] + (tt + 1) * 2048);
+    f32x4 cur[SM];
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) {
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      cur[ms] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
+      if (tt > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ms][tt - 1][r] = __builtin_fmaf(prev[ms][r], s[ms], acc[ms][tt - 1][r]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) prev[ms] = cur[ms];
+    bf = bn;
+  }
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[ms][SN - 1][r] = __builtin_fmaf(prev[ms][r], s[ms], acc[ms][SN - 1][r]);
+}
+
 template <class C, int L>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][C::STAGE];
+  // two operand stages
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+#define FG_STAGE(i) (lds + (i) * C::STAGE)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -549,19 +618,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   Work cur;
   int it = 0;
   cur.w = -1;
-  {
-    const int w = local;
-    if (w < p.num_tiles && resolve_big<L, BM, BN>(p, w, cur)) {
-    } else {
-      advance_big<L, BM, BN>(p, cur, it, local, grid);
-    }
-  }
+  if (!(local < p.num_tiles && resolve_big<L, BM, BN>(p, local, cur))) advance_big<L, BM, BN>(p, cur, it, local, grid);
   if (cur.w < 0) return;
-  Work nxt = cur;
-  int it_n = it;
 
-  issue_slice_loads<C>(p, cur, 0, smem[0], wave, lane);
+  float sa_c[SM], sb_c;
+  load_scales<C>(p, cur, 0, wm, wn, l16, sa_c, sb_c);
+  issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
+  // accumulators live across the segments of a tile; zeroed after each store
   float acc[SM][SN][4];
 #pragma unroll
   for (int ms = 0; ms < SM; ++ms)
@@ -570,59 +636,49 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
 
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  int kb = 0;
   int stage = 0;
-  for (;;) {
-    // ---- what comes after (cur, kb): prefetch it into the other stage ----
-    int kb_n = kb + 1;
-    if (kb_n == Kb) {
-      kb_n = 0;
-      advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
-    }
-    const bool have_next = nxt.w >= 0;
-    if (have_next) issue_slice_loads<C>(p, nxt, kb_n, smem[stage ^ 1], wave, lane);
-
-    // ---- compute slice kb of cur ----
+  while (cur.w >= 0) {
+    Work nxt = cur;
+    int it_n = it;
+    advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
     const bool active = (L == kContiguous) ? (((cur.half_mask >> half) & 1) != 0)
                                            : (cur.m0 + wm * WM < cur.rows_valid);
-    if (active) {
-      const int nb = min((cur.n0 + wn * WN) >> 7, p.Nb - 1);
-      const float sbv = cur.sb[(int64_t)nb * Kb + kb];
-      const float* sa_k = cur.sa + (int64_t)kb * p.ld_sa;
-      float s[SM];
+
+    for (int kb = 0; kb < Kb; ++kb) {
+      // prefetch the following slice: this tile's next one, or the first of the next work item
+      const bool last = kb + 1 == Kb;
+      float sa_n[SM], sb_n = 0.f;
 #pragma unroll
-      for (int ms = 0; ms < SM; ++ms) {
-        const int m = min(cur.m0 + wm * WM + ms * 16 + l16, cur.rows_alloc - 1);
-        s[ms] = sa_k[m] * sbv;
+      for (int ms = 0; ms < SM; ++ms) sa_n[ms] = 0.f;
+      if (!last) {
+        load_scales<C>(p, cur, kb + 1, wm, wn, l16, sa_n, sb_n);
+        issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), wave, lane);
+      } else if (nxt.w >= 0) {
+        load_scales<C>(p, nxt, 0, wm, wn, l16, sa_n, sb_n);
+        issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), wave, lane);
       }
-      const uint8_t* st = smem[stage];
-      i32x8 af[SM];
+
+      if (active) {
+        float s[SM];
 #pragma unroll
-      for (int ms = 0; ms < SM; ++ms) {
-        const i32x4 lo = *(const i32x4*)(st + a_off[0] + ms * 2048);
-        const i32x4 hi = *(const i32x4*)(st + a_off[1] + ms * 2048);
-        af[ms] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int ms = 0; ms < SM; ++ms) s[ms] = sa_c[ms] * sb_c;
+        slice_mma<C>(FG_STAGE(stage), a_off, b_off, s, acc);
       }
+
+      // This wave's operand loads have landed in LDS; the barrier publishes
+      // them to the other waves (and frees the stage just read).
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      stage ^= 1;
 #pragma unroll
-      for (int tt = 0; tt < SN; ++tt) {
-        const i32x4 lo = *(const i32x4*)(st + b_off[0] + tt * 2048);
-        const i32x4 hi = *(const i32x4*)(st + b_off[1] + tt * 2048);
-        const i32x8 bf = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int ms = 0; ms < SM; ++ms) {
-          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ms][tt][r] = __builtin_fmaf(P[r], s[ms], acc[ms][tt][r]);
-        }
-      }
+      for (int ms = 0; ms < SM; ++ms) sa_c[ms] = sa_n[ms];
+      sb_c = sb_n;
     }
 
-    // ---- tile done: store its rows and reset the accumulators ----
-    if (kb == Kb - 1 && cur.seg == cur.nseg - 1) {
+    // ---- last segment of the tile: store its rows ----
+    if (cur.seg == cur.nseg - 1) {
       int e_w = 0;
       if (L == kContiguous) e_w = half == 0 ? cur.e_lo : cur.e_hi;
       const bool vec = (p.ldd & 3) == 0 && ((uintptr_t)p.D & 7) == 0;
@@ -658,14 +714,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
           for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
       }
     }
-
-    if (!have_next) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
     cur = nxt;
-    kb = kb_n;
-    stage ^= 1;
+    it = it_n;
   }
+  // no LDS-direct load may still be in flight when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
+#undef FG_STAGE
 }
 
 }  // namespace fg
