@@ -1,0 +1,262 @@
+"""Benchmark of the FP8 fine-grained-scaled GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the dense inference GEMMs at M=4096 with (N, K) in
+{(2112,7168), (24576,1536), (7168,16384), (4096,7168), (7168,2048)}.
+Inputs are seeded synthetic N(0,1) fp32 matrices (``synth``), cast to e4m3
+with the library's own per-token / per-block cast kernels and kept resident in
+HBM; a *step* is one pass over every GEMM of the workload (the activation cast
+is timed separately and reported under ``cast``).  Every GEMM launch is timed
+with HIP events on the stream it is launched on.
+
+One JSON line is printed with the aggregate throughput (TFLOPS = total
+algorithmic flops / total GEMM time), per-shape TFLOPS / GB/s / roofline
+fractions, a ``roofline`` object for the GEMM kernel (MFMA-bound, against the
+published 5.0 PFLOP/s dense FP8 peak; ``traffic`` is the HBM bytes per launch
+measured with rocprofv3 counters when the committed counter summary matches
+the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
+oracle timed on a bounded sample of output blocks of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import moe_grouped_gemm_e4m3_amd as fg  # noqa: E402
+import synth  # noqa: E402
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "FP8 GEMM TFLOPS & GB/s (% of MI355X FP8 MFMA / HBM roofline) per shape"
+CSRC = os.path.join(ROOT, "moe_grouped_gemm_e4m3_amd", "csrc")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_dense_m4096_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def dense_bytes(M, N, K) -> int:
+    """Algorithmic HBM bytes of one dense GEMM: A, B once, scales, D once."""
+    Kb, Nb = K // 128, -(-N // 128)
+    return M * K + N * K + 4 * (M * Kb + Nb * Kb) + 2 * M * N
+
+
+class Problem:
+    """One resident dense problem: fp32 source -> device casts -> e4m3 operands."""
+
+    def __init__(self, M, N, K, seed=0):
+        self.M, self.N, self.K = M, N, K
+        A32, B32 = synth.dense_problem(M, N, K, seed=seed)
+        self.A32_cpu, self.B32_cpu = A32, B32
+        self.a32 = A32.cuda()
+        self.qa, self.sa = fg.fp8_cast_per_token(self.a32)
+        b32 = B32.cuda()
+        self.qb, self.sb = fg.fp8_cast_per_block(b32)
+        del b32
+        self.D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        self.flops = 2 * M * N * K
+        self.bytes = dense_bytes(M, N, K)
+
+    def run(self, stream):
+        fg.gemm_fp8_nt(self.qa, self.sa, self.qb, self.sb, self.D, stream=stream)
+
+    def cast(self, stream):
+        fg.fp8_cast_per_token(self.a32, self.qa, self.sa, stream=stream)
+
+
+def time_steps(problems, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for pb in problems:
+            pb.run(stream)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in problems]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, pb in enumerate(problems):
+            ev[s][i][0].record(stream)
+            pb.run(stream)
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[a.elapsed_time(b) for (a, b) in row] for row in ev])  # ms [steps, shapes]
+    return wall, per
+
+
+def time_casts(problems, reps=10):
+    stream = torch.cuda.current_stream()
+    out = []
+    for pb in problems:
+        pb.cast(stream)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            pb.cast(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.median(ts))
+        nbytes = pb.M * pb.K * 5 + 4 * pb.M * (pb.K // 128)
+        out.append({"M": pb.M, "K": pb.K, "us": round(ms * 1e3, 2), "gbs": round(nbytes / ms / 1e6, 1),
+                    "pct_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS * 100, 1)})
+    return out
+
+
+def cpu_baseline(problems, budget_s: float = 15.0):
+    """The CPU oracle (fp64 blockwise GEMM) on a bounded sample of output
+    blocks of every shape: rows [0, ms) x columns [0, ns) at full K, with the
+    sample operands quantised by the oracle's own quantiser."""
+    from oracle import gemm as ogemm, quant
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([t.get("num_threads", 0) for t in threadpool_info() if t.get("user_api") == "blas"] or [0])
+    except Exception:  # pragma: no cover
+        cores = 0
+    cores = cores or len(os.sched_getaffinity(0))
+    # calibrate on the first shape, then size the sample to the budget
+    ms, ns = 64, 256
+    samples = []
+    for pb in problems:
+        qa, sa = quant.quantize_per_token(pb.A32_cpu[:ms].numpy())
+        qb, sb = quant.quantize_per_block(pb.B32_cpu[:ns].numpy())
+        samples.append((qa, sa, qb, sb, pb.K))
+    t0 = time.perf_counter()
+    flops = 0
+    for qa, sa, qb, sb, K in samples:
+        ogemm.gemm_nt(qa, sa, qb, sb)
+        flops += 2 * ms * ns * K
+    dt = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(dt, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for qa, sa, qb, sb, K in samples:
+            ogemm.gemm_nt(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops * reps / dt / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 blockwise oracle on D[0:{ms}, 0:{ns}] at full K of each of the {len(problems)} shapes, "
+                  f"{reps} passes, {dt:.1f} s",
+    }
+
+
+def traffic_per_launch():
+    """HBM bytes per GEMM launch from the committed counter summary, if it
+    was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            summ = json.load(f)
+    except OSError:
+        return None
+    if summ.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return summ.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_m4096", choices=["dense_m4096", "dense_small_m"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 3 times (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4}))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    fg.load_library()
+    wl = synth.WORKLOADS[args.workload]
+    problems = [Problem(*s, seed=0) for s in wl.shapes]
+    torch.cuda.synchronize()
+
+    wall, per = time_steps(problems, args.steps, args.warmup)
+    casts = time_casts(problems)
+    gemm_ms = per.sum(axis=1)  # GEMM time per step (sum of launch durations)
+    total_flops = sum(pb.flops for pb in problems)
+    total_bytes = sum(pb.bytes for pb in problems)
+    step_ms = float(np.mean(gemm_ms))
+    value = total_flops / (step_ms * 1e-3) / 1e12
+    shapes = []
+    for i, pb in enumerate(problems):
+        ms = float(np.mean(per[:, i]))
+        tf = pb.flops / ms / 1e9
+        gbs = pb.bytes / ms / 1e6
+        shapes.append({"M": pb.M, "N": pb.N, "K": pb.K, "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                       "pct_mfma": round(tf / PEAK_FP8_TFLOPS * 100, 1), "gbs": round(gbs, 1),
+                       "pct_hbm": round(gbs / PEAK_HBM_GBS * 100, 1)})
+    achieved = total_flops / (float(np.sum(per)) / args.steps * 1e-3) / 1e12  # flops / mean launch time, aggregated
+    launches = len(problems)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "shapes": [list(s) for s in wl.shapes], "gemm_ms_per_step": round(step_ms, 4),
+                   "gbs": round(total_bytes / (step_ms * 1e-3) / 1e9, 1)},
+        "shapes": shapes,
+        "cast": casts,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic_per_launch(),
+            "kernel": "gemm_fp8_big_kernel (dense)",
+            "flops_per_launch": total_flops / launches,
+            "launch_us": round(float(np.sum(per)) / args.steps / launches * 1e3, 2),
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(problems),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
