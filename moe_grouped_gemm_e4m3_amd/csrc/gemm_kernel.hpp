@@ -583,6 +583,87 @@ __device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[
     for (int r = 0; r < 4; ++r) acc[ms][SN - 1][r] = __builtin_fmaf(prev[ms][r], s[ms], acc[ms][SN - 1][r]);
 }
 
+// Workgroup barrier that waits only for this wave's LDS traffic (not for
+// outstanding global stores or operand prefetches).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Epilogue: the finished tile is converted to bf16 and staged through the LDS
+// stage that was just consumed, half a tile at a time, so that the global
+// stores are whole 512-byte row segments (16 bytes per lane) instead of
+// 32-byte pieces of 16 rows.  Staging rows are 512 bytes; the 16-byte chunk
+// index is XORed with the row's low 4 bits, which keeps both the 8-byte
+// fragment writes (16 rows at one chunk) and the row reads conflict-free.
+template <class C, int L>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, const float (&acc)[C::SM][C::SN][4],
+                                           uint8_t* stg, int wave, int lane) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, SM = C::SM, SN = C::SN;
+  constexpr int ROWB = BN * 2;                  // staging row bytes
+  constexpr int CHUNKS = ROWB / 16;             // 16-byte chunks per row
+  constexpr int PASS_ROWS = C::STAGE / ROWB;    // tile rows staged per pass
+  constexpr int PASSES = BM / PASS_ROWS;
+  constexpr int MS_PER_PASS = SM / PASSES;      // fragment rows (of 16) per wave per pass
+  static_assert(BM % PASS_ROWS == 0 && SM % PASSES == 0 && CHUNKS <= 64 && 64 % CHUNKS == 0, "staging");
+  constexpr int ROWS_PER_READ = 64 / CHUNKS;    // rows one wave-wide read covers
+  constexpr int READS = PASS_ROWS / (C::NWAVES * ROWS_PER_READ);
+  static_assert(PASS_ROWS % (C::NWAVES * ROWS_PER_READ) == 0, "reads");
+
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const bool vec = (p.ldd & 7) == 0 && ((uintptr_t)p.D & 15) == 0;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    // write this wave's fragment rows of the pass
+#pragma unroll
+    for (int j = 0; j < MS_PER_PASS; ++j) {
+      const int ms = pass * MS_PER_PASS + j;
+      const int srow = wm * (WM / PASSES) + j * 16 + l16;
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt) {
+        const int byte = (wn * WN + tt * 16 + 4 * kq) * 2;
+        const int c = byte >> 4;
+        const int off = srow * ROWB + ((c ^ (srow & 15)) << 4) + (byte & 15);
+        *(uint2*)(stg + off) = make_uint2(pack_bf16x2(acc[ms][tt][0], acc[ms][tt][1]),
+                                          pack_bf16x2(acc[ms][tt][2], acc[ms][tt][3]));
+      }
+    }
+    lds_barrier();
+    // read whole rows back and store them
+#pragma unroll
+    for (int rd = 0; rd < READS; ++rd) {
+      const int srow = (wave * READS + rd) * ROWS_PER_READ + lane / CHUNKS;
+      const int c = lane % CHUNKS;
+      const i32x4 v = *(const i32x4*)(stg + srow * ROWB + ((c ^ (srow & 15)) << 4));
+      // staging row -> tile row: each wave-row group of WM/PASSES rows came from rows wm*WM + pass*WM/PASSES ...
+      const int trow = (srow / (WM / PASSES)) * WM + pass * (WM / PASSES) + srow % (WM / PASSES);
+      const int m = t.m0 + trow;
+      bool ok;
+      if (L == kContiguous) {
+        const int e = trow < BM / 2 || BM < 256 ? t.e_lo : t.e_hi;
+        ok = e >= 0 && m < t.rows_alloc && p.m_indices[m] == e;
+      } else {
+        ok = m < t.rows_valid;
+      }
+      const int n = t.n0 + c * 8;
+      if (ok && n < p.N) {
+        uint16_t* dst = t.D + (int64_t)m * p.ldd + n;
+        if (vec && n + 8 <= p.N) {
+          *(i32x4*)dst = v;
+        } else {
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2)
+            if (n + e2 < p.N) dst[e2] = (uint16_t)((uint32_t)v[e2 >> 1] >> ((e2 & 1) * 16));
+        }
+      }
+    }
+    lds_barrier();  // staging free again (next pass, or the next tile's operand loads)
+  }
+}
+
 template <class C, int L>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
@@ -679,40 +760,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 
     // ---- last segment of the tile: store its rows ----
     if (cur.seg == cur.nseg - 1) {
-      int e_w = 0;
-      if (L == kContiguous) e_w = half == 0 ? cur.e_lo : cur.e_hi;
-      const bool vec = (p.ldd & 3) == 0 && ((uintptr_t)p.D & 7) == 0;
+      store_tile<C, L>(p, cur, acc, FG_STAGE(stage ^ 1), wave, lane);
 #pragma unroll
-      for (int ms = 0; ms < SM; ++ms) {
-        const int m = cur.m0 + wm * WM + ms * 16 + l16;
-        bool ok;
-        if (L == kContiguous) {
-          ok = e_w >= 0 && m < cur.rows_alloc && p.m_indices[m] == e_w;
-        } else {
-          ok = m < cur.rows_valid;
-        }
-        if (ok) {
-          uint16_t* drow = cur.D + (int64_t)m * p.ldd;
-#pragma unroll
-          for (int tt = 0; tt < SN; ++tt) {
-            const int n = cur.n0 + wn * WN + tt * 16 + 4 * kq;
-            const uint32_t lo = pack_bf16x2(acc[ms][tt][0], acc[ms][tt][1]);
-            const uint32_t hi = pack_bf16x2(acc[ms][tt][2], acc[ms][tt][3]);
-            if (vec && n + 4 <= p.N) {
-              *(uint2*)(drow + n) = make_uint2(lo, hi);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                if (n + j < p.N) drow[n + j] = (uint16_t)((j < 2 ? lo : hi) >> ((j & 1) * 16));
-              }
-            }
-          }
-        }
+      for (int ms = 0; ms < SM; ++ms)
 #pragma unroll
         for (int tt = 0; tt < SN; ++tt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
-      }
     }
     cur = nxt;
     it = it_n;
