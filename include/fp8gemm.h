@@ -66,6 +66,13 @@ typedef enum {
  *       16-byte aligned get vector stores); written
  * M, N >= 0 arbitrary; K % 128 == 0.  K == 0 writes D = 0 (sa, sb may then be NULL).
  * Only D[0:M, 0:N] is written.
+ * Optional stream-K (environment FG_STREAM_K=1; off by default): the K
+ * slices of all tiles are split evenly over the workgroups and fp32 partial
+ * tiles are exchanged through a workspace that the library allocates on the
+ * first such call for a (device, stream) pair (64 MiB of partials plus
+ * 256 KiB of counters) and keeps until the process ends.  That first call
+ * must not be inside a HIP graph capture; later calls allocate nothing.
+ * Different streams get different workspaces.
  */
 fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const uint8_t* B, int64_t ldb, const float* sb,
@@ -143,9 +150,11 @@ fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
 int fg_get_mk_alignment_for_contiguous_layout(void);
 
 /* Cap on the compute units the GEMM kernels spread their persistent workgroups
- * over (the digest's set_num_sms); 0 (the default) means all of them.  The
- * result bits do not depend on this value.  Process-wide, not thread-safe
- * against concurrent launches. */
+ * over (the digest's set_num_sms); 0 (the default) means all of them.
+ * Results are bit-for-bit reproducible for a fixed cap.  With whole-tile
+ * scheduling (the default) they do not depend on the cap at all; with the
+ * optional stream-K split the cap sets the split and so the fp32 summation
+ * order.  Process-wide, not thread-safe against concurrent launches. */
 void fg_set_num_cus(int n);
 int fg_get_num_cus(void);
 

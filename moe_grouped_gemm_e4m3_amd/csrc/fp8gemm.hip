@@ -141,6 +141,77 @@ fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
   return FG_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K workspace: fp32 partial-tile slots (one per workgroup) and one
+// arrival counter per tile.  Allocated on the first stream-K call for a
+// (device, stream) pair and kept for the life of the process; the counters
+// are zeroed once at allocation and every launch leaves them zero.  Later
+// calls allocate nothing.
+
+struct SkWorkspace {
+  int dev = -1;
+  void* stream = nullptr;
+  float* partials = nullptr;
+  int* flags = nullptr;
+};
+constexpr int kSkSlots = 32;
+constexpr int kSkMaxTiles = 1 << 16;
+SkWorkspace g_sk[kSkSlots];
+std::mutex g_sk_mu;
+
+template <class C>
+SkWorkspace* sk_workspace(void* stream, int grid) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_sk_mu);
+  for (auto& w : g_sk)
+    if (w.partials && w.dev == dev && w.stream == stream) return &w;
+  for (auto& w : g_sk) {
+    if (w.partials) continue;
+    const size_t pbytes = (size_t)grid * C::THREADS * C::SM * C::SN * 4 * sizeof(float);
+    if (hipMalloc(&w.partials, pbytes) != hipSuccess) { w.partials = nullptr; return nullptr; }
+    if (hipMalloc(&w.flags, kSkMaxTiles * sizeof(int)) != hipSuccess ||
+        hipMemset(w.flags, 0, kSkMaxTiles * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      hipFree(w.partials);
+      w.partials = nullptr;
+      return nullptr;
+    }
+    w.dev = dev;
+    w.stream = stream;
+    return &w;
+  }
+  return nullptr;
+}
+
+// Stream-K pays off when whole-tile rounds would leave CUs idle: the tile
+// count is not a multiple of the grid and there are few rounds.  Each XCD's
+// block of tiles must give every one of its workgroups at least one K slice.
+// Opt-in (FG_STREAM_K=1).  Measured on MI355X it loses to whole-tile rounds
+// on the M=4096 shapes: an XCD's workgroups then work on different K offsets
+// of different tiles, so they stop sharing A/B in L2, and the fp32 partial
+// tiles add traffic.  Tile widths that fill whole rounds are used instead.
+bool want_stream_k(int64_t tiles, int Kb, int grid) {
+  const char* f = getenv("FG_STREAM_K");
+  if (!(f && strcmp(f, "1") == 0)) return false;
+  if (grid % 8 || tiles < 8 || tiles > kSkMaxTiles) return false;
+  const int nx = grid / 8;
+  if ((tiles / 8) * (int64_t)Kb < nx) return false;
+  if ((tiles / 8 + 1) * (int64_t)Kb * (nx + 1) >= ((int64_t)1 << 31)) return false;  // 32-bit bookkeeping
+  return true;
+}
+
+template <class C>
+fg_status launch_stream_k(fg::GemmParams& p, hipStream_t stream, int grid, SkWorkspace* ws, const char* what) {
+  p.group_m = 8;
+  p.sk_partials = ws->partials;
+  p.sk_flags = ws->flags;
+  print_config(what, p, C::BM, C::BN, C::THREADS, grid, -1);
+  hipLaunchKernelGGL((fg::gemm_fp8_sk_kernel<C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return FG_OK;
+}
+
 // Tiles the large kernel would have; it is used when they cover at least
 // half of the device, otherwise the 128x128 kernel spreads the work wider.
 // FG_FORCE_CONFIG=big|small overrides the choice (tuning and tests).
@@ -208,6 +279,15 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
       p.tiles_m = (int)tm;
       p.tiles_n = (int)tn;
       p.num_tiles = (int)(tm * tn);
+      int cus = 0;
+      FG_TRY(device_cus(&cus));
+      if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
+      if (want_stream_k(tm * tn, p.Kb, cus)) {
+        int all_cus = 0;
+        FG_TRY(device_cus(&all_cus));
+        SkWorkspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
+        if (ws) return launch_stream_k<C>(p, (hipStream_t)stream, cus, ws, "gemm_fp8_nt[stream-k]");
+      }
       return launch_big<C, fg::kDense>(p, (hipStream_t)stream, "gemm_fp8_nt");
     }
   }
