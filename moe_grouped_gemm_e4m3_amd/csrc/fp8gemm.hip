@@ -83,6 +83,8 @@ bool env_flag(const char* name) {
 
 using CfgDefault = fg::TileCfg<128, 128, 64, 64>;
 using CfgBig = fg::BigCfg<256, 256, 4, 2>;
+using CfgBig224 = fg::BigCfg<256, 224, 4, 2>;
+using CfgBig160 = fg::BigCfg<256, 160, 4, 2>;
 
 template <class K>
 int occupancy_of(K kernel, int threads, int* cache) {
@@ -212,6 +214,62 @@ fg_status launch_stream_k(fg::GemmParams& p, hipStream_t stream, int grid, SkWor
   return FG_OK;
 }
 
+// Width of the large kernel's 256-row tile.  The persistent grid runs whole
+// tiles in rounds and a tile's time grows with its width, so the width with
+// the least (rounds x width) finishes first: narrower tiles fill a last round
+// that 256-wide tiles would leave mostly idle (N = 7168 on 16 row tiles:
+// 448 tiles of 256 are 1.75 rounds of 256 CUs, 512 tiles of 224 are two
+// full ones).  A fixed per-tile cost (prologue and epilogue), worth about 16
+// columns, keeps near-ties on the wider tile.  FG_FORCE_BN=256|224|160
+// overrides the choice (tuning and tests).
+constexpr int kTileCostCols = 16;
+
+int pick_bn(int64_t row_tiles, int N) {
+  const char* f = getenv("FG_FORCE_BN");
+  if (f && *f) {
+    const int v = atoi(f);
+    if (v == 256 || v == 224 || v == 160) return v;
+  }
+  int cus = 0;
+  if (device_cus(&cus) != FG_OK) return 256;
+  if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
+  static const int widths[] = {256, 224, 160};
+  int best = 256;
+  int64_t best_cost = -1;
+  for (int bn : widths) {
+    const int64_t tiles = row_tiles * ((N + bn - 1) / bn);
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const int64_t cost = rounds * (bn + kTileCostCols);
+    if (best_cost < 0 || cost < best_cost) {
+      best = bn;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+// Large-kernel launch for `groups` independent [rows, N] outputs (1 for the
+// dense and contiguous forms, G for the masked one) with tile width BN.
+template <class C, int L>
+fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream, const char* what) {
+  p.tiles_m = (p.rows + C::BM - 1) / C::BM;
+  p.tiles_n = (p.N + C::BN - 1) / C::BN;
+  const int64_t slots = groups * p.tiles_m * p.tiles_n;
+  if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
+  p.num_tiles = (int)slots;
+  return launch_big<C, L>(p, stream, what);
+}
+
+template <int L>
+fg_status launch_big_width(fg::GemmParams& p, int64_t groups, hipStream_t stream, const char* what) {
+  const int64_t row_tiles = groups * ((p.rows + CfgBig::BM - 1) / CfgBig::BM);
+  switch (pick_bn(row_tiles, p.N)) {
+    case 224: return launch_big_tiled<CfgBig224, L>(p, groups, stream, what);
+    case 160: return launch_big_tiled<CfgBig160, L>(p, groups, stream, what);
+    default: return launch_big_tiled<CfgBig, L>(p, groups, stream, what);
+  }
+}
+
 // Tiles the large kernel would have; it is used when they cover at least
 // half of the device, otherwise the 128x128 kernel spreads the work wider.
 // FG_FORCE_CONFIG=big|small overrides the choice (tuning and tests).
@@ -288,7 +346,7 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
         SkWorkspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
         if (ws) return launch_stream_k<C>(p, (hipStream_t)stream, cus, ws, "gemm_fp8_nt[stream-k]");
       }
-      return launch_big<C, fg::kDense>(p, (hipStream_t)stream, "gemm_fp8_nt");
+      return launch_big_width<fg::kDense>(p, 1, (hipStream_t)stream, "gemm_fp8_nt");
     }
   }
   using C = CfgDefault;
@@ -324,11 +382,7 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
   p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128;
   if (K > 0) {
     // 256-row tiles: a tile whose halves hold different experts runs as two segments
-    using C = CfgBig;
-    p.tiles_m = (M_total + C::BM - 1) / C::BM;
-    p.tiles_n = (N + C::BN - 1) / C::BN;
-    p.num_tiles = p.tiles_m * p.tiles_n;
-    return launch_big<C, fg::kContiguous>(p, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
+    return launch_big_width<fg::kContiguous>(p, 1, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
   }
   using C = CfgDefault;
   static_assert(128 % C::BM == 0, "contiguous tiles must not straddle a 128-row expert block");
@@ -363,13 +417,7 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
   p.masked_m = masked_m;
   p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128;
   if (K > 0) {
-    using C = CfgBig;
-    p.tiles_m = (M_cap + C::BM - 1) / C::BM;
-    p.tiles_n = (N + C::BN - 1) / C::BN;
-    const int64_t slots = (int64_t)G * p.tiles_m * p.tiles_n;
-    if (slots > (int64_t)1 << 30) return fail(FG_EUNSUPPORTED, "too many tiles");
-    p.num_tiles = (int)slots;
-    return launch_big<C, fg::kMasked>(p, (hipStream_t)stream, "gemm_fp8_grouped_masked");
+    return launch_big_width<fg::kMasked>(p, G, (hipStream_t)stream, "gemm_fp8_grouped_masked");
   }
   using C = CfgDefault;
   p.tiles_m = (M_cap + C::BM - 1) / C::BM;

@@ -379,13 +379,16 @@ struct BigCfg {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int SM = WM / 16, SN = WN / 16;
   static constexpr int STAGE = (BM + BN) * 128;
-  static constexpr int LOADS = (BM + BN) / 8;      // 1 KiB (8-row) loads per slice
-  static constexpr int LOADS_PER_WAVE = LOADS / NWAVES;
-  static_assert(LOADS % NWAVES == 0, "loads per wave");
-  static_assert(BM % (8 * LOADS_PER_WAVE) == 0, "a wave loads A rows or B rows, not both");
-  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
-  static_assert(BN % 128 == 0 && 128 % WN == 0 || WN % 128 == 0, "a wave's columns share one weight-scale block");
-  static_assert(WN <= 128, "wave columns within one 128 block");
+  // 1 KiB (8-row) loads per slice: half of the waves load the A rows, the
+  // other half the B rows, consecutive loads per wave
+  static constexpr int LOADS_A = BM / 8 / (NWAVES / 2), LOADS_B = BN / 8 / (NWAVES / 2);
+  // A wave's columns lie in one 128-wide weight-scale block when the tile
+  // width is a multiple of 128 and the wave width divides 128; otherwise a
+  // wave may straddle one block boundary and picks the scale per subtile.
+  static constexpr bool SCALE_PER_WAVE = (BN % 128 == 0) && (128 % WN == 0);
+  static_assert(NWAVES % 2 == 0 && BM % (4 * NWAVES) == 0 && BN % (4 * NWAVES) == 0, "loads");
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && WN <= 128, "wave tile");
+  static_assert(BN <= 256, "epilogue staging rows are 512 bytes");
   static_assert(BM % 128 == 0 || BM <= 128, "row halves");
 };
 
@@ -500,10 +503,11 @@ __device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& i
 template <class C>
 __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Work& t, int kb, uint8_t* stage,
                                                   int wave, int lane) {
-  constexpr int BM = C::BM, BN = C::BN;
-  constexpr int IPW = C::LOADS_PER_WAVE;
-  const int q0 = wave * IPW;             // first 8-row load of this wave
-  const bool is_a = q0 * 8 < BM;         // wave-uniform
+  constexpr int BM = C::BM;
+  constexpr int HALF = C::NWAVES / 2, LA = C::LOADS_A, LB = C::LOADS_B;
+  const bool is_a = wave < HALF;  // wave-uniform: the first half of the waves loads A, the second B
+  const int n = is_a ? LA : LB;
+  const int q0 = is_a ? wave * LA : BM / 8 + (wave - HALF) * LB;  // first 8-row load of this wave
   const int row0 = is_a ? q0 * 8 : q0 * 8 - BM;
   const uint8_t* base = is_a ? t.A + (int64_t)t.m0 * p.lda : t.B + (int64_t)t.n0 * p.ldb;
   const int64_t ld = is_a ? p.lda : p.ldb;
@@ -513,30 +517,49 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
   const int comb0 = q0 * 8 + (lane >> 3);  // combined (A|B) row of this lane in load 0
   const int p_chunk = lane & 7;
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int comb = comb0 + 8 * j;
-    const int r = row0 + 8 * j + (lane >> 3);
-    const int c = p_chunk ^ swz16(comb);
-    const int voff = r * (int)ld + c * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (q0 + j) * 1024),
-                                             16, voff, kb * 128, 0, 0);
+  for (int j = 0; j < (LA > LB ? LA : LB); ++j) {
+    if (LA == LB || j < n) {
+      const int comb = comb0 + 8 * j;
+      const int r = row0 + 8 * j + (lane >> 3);
+      const int c = p_chunk ^ swz16(comb);
+      const int voff = r * (int)ld + c * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (q0 + j) * 1024),
+                                               16, voff, kb * 128, 0, 0);
+    }
   }
 }
 
 // Scales of one K slice for this lane's SM rows: sa[kb][m] per row and the
-// wave's weight-block scale sb[nb][kb].  Issued one slice ahead, before that
-// slice's operand loads, so the compute never waits on them.
+// weight-block scales sb[nb][kb] of the (at most two) 128-column blocks the
+// wave's columns touch.  Issued one slice ahead, before that slice's operand
+// loads, so the compute never waits on them.
 template <class C>
 __device__ __forceinline__ void load_scales(const GemmParams& p, const Work& t, int kb, int wm, int wn, int l16,
-                                            float (&sa_r)[C::SM], float& sb_r) {
-  const int nb = min((t.n0 + wn * C::WN) >> 7, p.Nb - 1);
-  sb_r = t.sb[(int64_t)nb * p.Kb + kb];
+                                            float (&sa_r)[C::SM], float (&sb_r)[2]) {
+  const int nw = t.n0 + wn * C::WN;
+  const int nb0 = min(nw >> 7, p.Nb - 1);
+  sb_r[0] = t.sb[(int64_t)nb0 * p.Kb + kb];
+  if (!C::SCALE_PER_WAVE) {
+    const int nb1 = min(nb0 + 1, p.Nb - 1);
+    sb_r[1] = t.sb[(int64_t)nb1 * p.Kb + kb];
+  } else {
+    sb_r[1] = sb_r[0];
+  }
   const float* sa_k = t.sa + (int64_t)kb * p.ld_sa;
 #pragma unroll
   for (int ms = 0; ms < C::SM; ++ms) {
     const int m = min(t.m0 + wm * C::WM + ms * 16 + l16, t.rows_alloc - 1);
     sa_r[ms] = sa_k[m];
   }
+}
+
+// First weight subtile of the wave that lies in the second 128-column block
+// (SN or more when the wave stays inside one block).
+template <class C>
+__device__ __forceinline__ int second_block_subtile(const Work& t, int wn) {
+  if (C::SCALE_PER_WAVE) return C::SN;
+  const int nw = t.n0 + wn * C::WN;
+  return (128 - (nw & 127)) >> 4;
 }
 
 __device__ __forceinline__ i32x8 lds_frag(const uint8_t* st, int off0, int off1) {
@@ -551,10 +574,12 @@ __device__ __forceinline__ i32x8 lds_frag(const uint8_t* st, int off0, int off1)
 // (tt-1, ms), so an MFMA result is read SM MFMAs after it was issued (its
 // latency and the MFMA->VALU hazard are hidden behind other MFMAs) and the
 // matrix core never waits for the promotion.  Scheduling fences keep the
-// compiler from pulling each MFMA down next to its consumers.
+// compiler from pulling each MFMA down next to its consumers.  s[ms][0]
+// applies to subtiles before `tb`, s[ms][1] from `tb` on (the wave's columns
+// may cross one 128-column weight-scale block boundary).
 template <class C>
 __device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[2], const int (&b_off)[2],
-                                          const float (&s)[C::SM], float (&acc)[C::SM][C::SN][4]) {
+                                          const float (&s)[C::SM][2], int tb, float (&acc)[C::SM][C::SN][4]) {
   constexpr int SM = C::SM, SN = C::SN;
   i32x8 af[SM];
 #pragma unroll
@@ -572,8 +597,9 @@ __device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       cur[ms] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
       if (tt > 0) {
+        const float sc = C::SCALE_PER_WAVE ? s[ms][0] : (tt - 1 < tb ? s[ms][0] : s[ms][1]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ms][tt - 1][r] = __builtin_fmaf(prev[ms][r], s[ms], acc[ms][tt - 1][r]);
+        for (int r = 0; r < 4; ++r) acc[ms][tt - 1][r] = __builtin_fmaf(prev[ms][r], sc, acc[ms][tt - 1][r]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -582,9 +608,11 @@ __device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[
     bf = bn;
   }
 #pragma unroll
-  for (int ms = 0; ms < SM; ++ms)
+  for (int ms = 0; ms < SM; ++ms) {
+    const float sc = C::SCALE_PER_WAVE ? s[ms][0] : (SN - 1 < tb ? s[ms][0] : s[ms][1]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[ms][SN - 1][r] = __builtin_fmaf(prev[ms][r], s[ms], acc[ms][SN - 1][r]);
+    for (int r = 0; r < 4; ++r) acc[ms][SN - 1][r] = __builtin_fmaf(prev[ms][r], sc, acc[ms][SN - 1][r]);
+  }
 }
 
 // Workgroup barrier that waits only for this wave's LDS traffic (not for
@@ -602,19 +630,27 @@ __device__ __forceinline__ void lds_barrier() {
 // 32-byte pieces of 16 rows.  Staging rows are 512 bytes; the 16-byte chunk
 // index is XORed with the row's low 4 bits, which keeps both the 8-byte
 // fragment writes (16 rows at one chunk) and the row reads conflict-free.
+template <class C>
+struct StoreGeom {
+  static constexpr int ROWB = 512;                 // staging row bytes (BN <= 256 bf16)
+  static constexpr int CHUNKS = ROWB / 16;          // 16-byte chunks per staging row
+  static constexpr int USED = C::BN / 8;            // chunks holding the tile's columns
+  static constexpr int PASSES = (C::BM / 2) * ROWB <= C::STAGE ? 2 : 4;
+  static constexpr int PASS_ROWS = C::BM / PASSES;
+  static constexpr int MS_PER_PASS = C::SM / PASSES;
+  static constexpr int ROWS_PER_READ = 64 / CHUNKS;
+  static constexpr int READS = PASS_ROWS / (C::NWAVES * ROWS_PER_READ);
+  static_assert(PASS_ROWS * ROWB <= C::STAGE && C::SM % PASSES == 0, "staging");
+  static_assert(PASS_ROWS % (C::NWAVES * ROWS_PER_READ) == 0, "reads");
+};
+
 template <class C, int L>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, const float (&acc)[C::SM][C::SN][4],
                                            uint8_t* stg, int wave, int lane) {
-  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, SM = C::SM, SN = C::SN;
-  constexpr int ROWB = BN * 2;                  // staging row bytes
-  constexpr int CHUNKS = ROWB / 16;             // 16-byte chunks per row
-  constexpr int PASS_ROWS = C::STAGE / ROWB;    // tile rows staged per pass
-  constexpr int PASSES = BM / PASS_ROWS;
-  constexpr int MS_PER_PASS = SM / PASSES;      // fragment rows (of 16) per wave per pass
-  static_assert(BM % PASS_ROWS == 0 && SM % PASSES == 0 && CHUNKS <= 64 && 64 % CHUNKS == 0, "staging");
-  constexpr int ROWS_PER_READ = 64 / CHUNKS;    // rows one wave-wide read covers
-  constexpr int READS = PASS_ROWS / (C::NWAVES * ROWS_PER_READ);
-  static_assert(PASS_ROWS % (C::NWAVES * ROWS_PER_READ) == 0, "reads");
+  using G = StoreGeom<C>;
+  constexpr int BM = C::BM, WM = C::WM, WN = C::WN, SN = C::SN;
+  constexpr int ROWB = G::ROWB, CHUNKS = G::CHUNKS, PASSES = G::PASSES;
+  constexpr int WROWS = WM / PASSES;  // staging rows per wave-row per pass
 
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int l16 = lane & 15, kq = lane >> 4;
@@ -623,9 +659,9 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
   for (int pass = 0; pass < PASSES; ++pass) {
     // write this wave's fragment rows of the pass
 #pragma unroll
-    for (int j = 0; j < MS_PER_PASS; ++j) {
-      const int ms = pass * MS_PER_PASS + j;
-      const int srow = wm * (WM / PASSES) + j * 16 + l16;
+    for (int j = 0; j < G::MS_PER_PASS; ++j) {
+      const int ms = pass * G::MS_PER_PASS + j;
+      const int srow = wm * WROWS + j * 16 + l16;
 #pragma unroll
       for (int tt = 0; tt < SN; ++tt) {
         const int byte = (wn * WN + tt * 16 + 4 * kq) * 2;
@@ -638,29 +674,31 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
     lds_barrier();
     // read whole rows back and store them
 #pragma unroll
-    for (int rd = 0; rd < READS; ++rd) {
-      const int srow = (wave * READS + rd) * ROWS_PER_READ + lane / CHUNKS;
+    for (int rd = 0; rd < G::READS; ++rd) {
+      const int srow = (wave * G::READS + rd) * G::ROWS_PER_READ + lane / CHUNKS;
       const int c = lane % CHUNKS;
-      const i32x4 v = *(const i32x4*)(stg + srow * ROWB + ((c ^ (srow & 15)) << 4));
-      // staging row -> tile row: each wave-row group of WM/PASSES rows came from rows wm*WM + pass*WM/PASSES ...
-      const int trow = (srow / (WM / PASSES)) * WM + pass * (WM / PASSES) + srow % (WM / PASSES);
-      const int m = t.m0 + trow;
-      bool ok;
-      if (L == kContiguous) {
-        const int e = trow < BM / 2 || BM < 256 ? t.e_lo : t.e_hi;
-        ok = e >= 0 && m < t.rows_alloc && p.m_indices[m] == e;
-      } else {
-        ok = m < t.rows_valid;
-      }
-      const int n = t.n0 + c * 8;
-      if (ok && n < p.N) {
-        uint16_t* dst = t.D + (int64_t)m * p.ldd + n;
-        if (vec && n + 8 <= p.N) {
-          *(i32x4*)dst = v;
+      if (c < G::USED) {
+        const i32x4 v = *(const i32x4*)(stg + srow * ROWB + ((c ^ (srow & 15)) << 4));
+        // staging row -> tile row
+        const int trow = (srow / WROWS) * WM + pass * WROWS + srow % WROWS;
+        const int m = t.m0 + trow;
+        bool ok;
+        if (L == kContiguous) {
+          const int e = trow < BM / 2 || BM < 256 ? t.e_lo : t.e_hi;
+          ok = e >= 0 && m < t.rows_alloc && p.m_indices[m] == e;
         } else {
+          ok = m < t.rows_valid;
+        }
+        const int n = t.n0 + c * 8;
+        if (ok && n < p.N) {
+          uint16_t* dst = t.D + (int64_t)m * p.ldd + n;
+          if (vec && n + 8 <= p.N) {
+            *(i32x4*)dst = v;
+          } else {
 #pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2)
-            if (n + e2 < p.N) dst[e2] = (uint16_t)((uint32_t)v[e2 >> 1] >> ((e2 & 1) * 16));
+            for (int e2 = 0; e2 < 8; ++e2)
+              if (n + e2 < p.N) dst[e2] = (uint16_t)((uint32_t)v[e2 >> 1] >> ((e2 & 1) * 16));
+          }
         }
       }
     }
@@ -706,7 +744,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   if (!(local < p.num_tiles && resolve_big<L, BM, BN>(p, local, cur))) advance_big<L, BM, BN>(p, cur, it, local, grid);
   if (cur.w < 0) return;
 
-  float sa_c[SM], sb_c;
+  float sa_c[SM], sb_c[2];
   load_scales<C>(p, cur, 0, wm, wn, l16, sa_c, sb_c);
   issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
@@ -728,11 +766,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
     advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
     const bool active = (L == kContiguous) ? (((cur.half_mask >> half) & 1) != 0)
                                            : (cur.m0 + wm * WM < cur.rows_valid);
+    const int tb = second_block_subtile<C>(cur, wn);
 
     for (int kb = 0; kb < Kb; ++kb) {
       // prefetch the following slice: this tile's next one, or the first of the next work item
       const bool last = kb + 1 == Kb;
-      float sa_n[SM], sb_n = 0.f;
+      float sa_n[SM], sb_n[2] = {0.f, 0.f};
 #pragma unroll
       for (int ms = 0; ms < SM; ++ms) sa_n[ms] = 0.f;
       if (!last) {
@@ -744,10 +783,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
       }
 
       if (active) {
-        float s[SM];
+        float s[SM][2];
 #pragma unroll
-        for (int ms = 0; ms < SM; ++ms) s[ms] = sa_c[ms] * sb_c;
-        slice_mma<C>(FG_STAGE(stage), a_off, b_off, s, acc);
+        for (int ms = 0; ms < SM; ++ms) {
+          s[ms][0] = sa_c[ms] * sb_c[0];
+          s[ms][1] = sa_c[ms] * sb_c[1];
+        }
+        slice_mma<C>(FG_STAGE(stage), a_off, b_off, s, tb, acc);
       }
 
       // This wave's operand loads have landed in LDS; the barrier publishes
@@ -759,7 +801,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
       stage ^= 1;
 #pragma unroll
       for (int ms = 0; ms < SM; ++ms) sa_c[ms] = sa_n[ms];
-      sb_c = sb_n;
+      sb_c[0] = sb_n[0];
+      sb_c[1] = sb_n[1];
     }
 
     // ---- last segment of the tile: store its rows ----
@@ -909,7 +952,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
   Work cw;
   sk_tile_work<C>(p, cur.t, cw);
 
-  float sa_c[SM], sb_c;
+  float sa_c[SM], sb_c[2];
   load_scales<C>(p, cw, cur.k0, wm, wn, l16, sa_c, sb_c);
   issue_slice_loads<C>(p, cw, cur.k0, FG_STAGE(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
@@ -933,7 +976,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
 
     for (int kb = cur.k0; kb < cur.k1; ++kb) {
       const bool last = kb + 1 == cur.k1;
-      float sa_n[SM], sb_n = 0.f;
+      float sa_n[SM], sb_n[2] = {0.f, 0.f};
 #pragma unroll
       for (int ms = 0; ms < SM; ++ms) sa_n[ms] = 0.f;
       if (!last) {
@@ -944,10 +987,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
         issue_slice_loads<C>(p, nw, nxt.k0, FG_STAGE(stage ^ 1), wave, lane);
       }
       if (cw.m0 + wm * WM < cw.rows_valid) {
-        float sc[SM];
+        float sc[SM][2];
 #pragma unroll
-        for (int ms = 0; ms < SM; ++ms) sc[ms] = sa_c[ms] * sb_c;
-        slice_mma<C>(FG_STAGE(stage), a_off, b_off, sc, acc);
+        for (int ms = 0; ms < SM; ++ms) {
+          sc[ms][0] = sa_c[ms] * sb_c[0];
+          sc[ms][1] = sa_c[ms] * sb_c[1];
+        }
+        slice_mma<C>(FG_STAGE(stage), a_off, b_off, sc, second_block_subtile<C>(cw, wn), acc);
       }
       __builtin_amdgcn_s_waitcnt(0);
       asm volatile("" ::: "memory");
@@ -956,7 +1002,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
       stage ^= 1;
 #pragma unroll
       for (int ms = 0; ms < SM; ++ms) sa_c[ms] = sa_n[ms];
-      sb_c = sb_n;
+      sb_c[0] = sb_n[0];
+      sb_c[1] = sb_n[1];
     }
 
     // Partial exchange without whole-cache maintenance: partials are written
