@@ -2,7 +2,8 @@
 //
 // Host side: argument validation (nothing is launched on a failed check),
 // tile-configuration choice, persistent-grid sizing and asynchronous launch
-// on the caller's stream.  The library holds no device memory of its own.
+// on the caller's stream.  The only device memory the library holds is the
+// partial-sum workspace of the split-K kernels (see Workspace below).
 // The API mirrors the operations of the DeepGEMM digest (GeekNews topic
 // 19459): "GEMM arayuzu ve yerlesim kisitlari" (NT dense GEMM, fp32 scale
 // factors with a transposed LHS layout), "Dense ve Grouped GEMM" (contiguous
@@ -17,11 +18,13 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <algorithm>
 #include <string>
 
 #include "fp8gemm.h"
 #include "cast_kernel.hpp"
 #include "gemm_kernel.hpp"
+#include "skinny_kernel.hpp"
 
 #define FG_TRY(x)                    \
   do {                               \
@@ -144,45 +147,62 @@ fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
 }
 
 // ---------------------------------------------------------------------------
-// Stream-K workspace: fp32 partial-tile slots (one per workgroup) and one
-// arrival counter per tile.  Allocated on the first stream-K call for a
-// (device, stream) pair and kept for the life of the process; the counters
-// are zeroed once at allocation and every launch leaves them zero.  Later
-// calls allocate nothing.
+// Workspaces of the kernels that exchange fp32 partials between workgroups
+// (stream-K and the split-K skinny kernel): partial slots and arrival
+// counters.  One per (kind, device, stream), allocated on the first call that
+// needs it and kept for the life of the process; the counters are zeroed once
+// at allocation and every launch leaves them zero.  Later calls allocate
+// nothing.  A call made while its stream is being captured into a graph never
+// allocates: it takes a path without a workspace instead.
 
-struct SkWorkspace {
+struct Workspace {
+  int kind = -1;
   int dev = -1;
   void* stream = nullptr;
   float* partials = nullptr;
   int* flags = nullptr;
 };
-constexpr int kSkSlots = 32;
+constexpr int kWsSlots = 64;
 constexpr int kSkMaxTiles = 1 << 16;
-SkWorkspace g_sk[kSkSlots];
-std::mutex g_sk_mu;
+Workspace g_ws[kWsSlots];
+std::mutex g_ws_mu;
 
-template <class C>
-SkWorkspace* sk_workspace(void* stream, int grid) {
+enum { kWsStreamK = 0, kWsSkinny = 1 };
+
+bool stream_capturing(void* stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
+Workspace* workspace(int kind, void* stream, size_t partial_bytes, int nflags) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lk(g_sk_mu);
-  for (auto& w : g_sk)
-    if (w.partials && w.dev == dev && w.stream == stream) return &w;
-  for (auto& w : g_sk) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto& w : g_ws)
+    if (w.partials && w.kind == kind && w.dev == dev && w.stream == stream) return &w;
+  if (stream_capturing(stream)) return nullptr;
+  for (auto& w : g_ws) {
     if (w.partials) continue;
-    const size_t pbytes = (size_t)grid * C::THREADS * C::SM * C::SN * 4 * sizeof(float);
-    if (hipMalloc(&w.partials, pbytes) != hipSuccess) { w.partials = nullptr; return nullptr; }
-    if (hipMalloc(&w.flags, kSkMaxTiles * sizeof(int)) != hipSuccess ||
-        hipMemset(w.flags, 0, kSkMaxTiles * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      hipFree(w.partials);
+    if (hipMalloc(&w.partials, partial_bytes) != hipSuccess) { w.partials = nullptr; return nullptr; }
+    if (hipMalloc(&w.flags, nflags * sizeof(int)) != hipSuccess ||
+        hipMemset(w.flags, 0, nflags * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(w.partials);
       w.partials = nullptr;
       return nullptr;
     }
+    w.kind = kind;
     w.dev = dev;
     w.stream = stream;
     return &w;
   }
   return nullptr;
+}
+
+template <class C>
+Workspace* sk_workspace(void* stream, int grid) {
+  const size_t pbytes = (size_t)grid * C::THREADS * C::SM * C::SN * 4 * sizeof(float);
+  return workspace(kWsStreamK, stream, pbytes, kSkMaxTiles);
 }
 
 // Stream-K pays off when whole-tile rounds would leave CUs idle: the tile
@@ -203,7 +223,7 @@ bool want_stream_k(int64_t tiles, int Kb, int grid) {
 }
 
 template <class C>
-fg_status launch_stream_k(fg::GemmParams& p, hipStream_t stream, int grid, SkWorkspace* ws, const char* what) {
+fg_status launch_stream_k(fg::GemmParams& p, hipStream_t stream, int grid, Workspace* ws, const char* what) {
   p.group_m = 8;
   p.sk_partials = ws->partials;
   p.sk_flags = ws->flags;
@@ -282,6 +302,107 @@ bool prefer_big(int64_t big_tiles) {
   return big_tiles * 2 >= cus;
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel (dense, M <= 128).  The plan picks the column-tile width
+// (16 CF weight rows per workgroup) and the K split from a two-term model:
+// every active CU must pull its operands through its own L1 (about 130 GB/s
+// each: (M + 16 CF) x K / splits bytes per workgroup), and the weights plus
+// any partials must come through HBM (about 6 TB/s).  Narrow tiles spread the
+// weights over more CUs but make every CU read the activations again; a K
+// split spreads both over more workgroups at the cost of fp32 partials.
+// FG_SKINNY="CF,SPLITS" overrides the choice (tuning and tests).
+
+constexpr size_t kSkinnyPartialBytes = (size_t)16 << 20;
+constexpr int kSkinnyMaxTiles = 1 << 14;
+
+struct SkinnyPlan {
+  int mf = 0, cf = 0, splits = 1;
+};
+
+int skinny_occ(int mf, int cf) { return mf * cf <= 8 ? 2 : 1; }
+
+bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool may_split, SkinnyPlan* out) {
+  if (M > 128 || K < 128) return false;
+  const int Kb = K / 128;
+  SkinnyPlan pl;
+  pl.mf = M <= 64 ? 4 : 8;
+  // 32-bit lane offsets
+  if ((int64_t)16 * pl.mf * lda + K >= ((int64_t)1 << 31)) return false;
+  if (((int64_t)(Kb - 1) * ld_sa + M) * 4 >= ((int64_t)1 << 31)) return false;
+  const char* f = getenv("FG_SKINNY");
+  if (f && *f) {
+    int cf = 0, sp = 0;
+    if (sscanf(f, "%d,%d", &cf, &sp) == 2 && (cf == 1 || cf == 2 || cf == 4) && pl.mf * cf <= 16 && sp >= 1 &&
+        (sp == 1 || may_split)) {
+      pl.cf = cf;
+      pl.splits = sp;
+      const int64_t tiles = (N + 16 * cf - 1) / (16 * cf);
+      if (sp > 1 && (tiles > kSkinnyMaxTiles ||
+                     (size_t)sp * tiles * pl.mf * cf * 1024 > kSkinnyPartialBytes))
+        return false;
+      *out = pl;
+      return true;
+    }
+  }
+  double best = -1;
+  for (int cf : {1, 2, 4}) {
+    if (pl.mf * cf > 16) continue;  // registers: at most 16 output blocks per wave
+    const int occ = skinny_occ(pl.mf, cf);
+    const int64_t tiles = (N + 16 * cf - 1) / (16 * cf);
+    for (int sp : {1, 2, 4, 8, 16}) {
+      if (sp > 1 && (!may_split || Kb < 4 * sp || tiles > kSkinnyMaxTiles ||
+                     (size_t)sp * tiles * pl.mf * cf * 1024 > kSkinnyPartialBytes))
+        continue;
+      const int64_t wgs = tiles * sp;
+      const int64_t slots = (int64_t)cus * occ;
+      const int64_t rounds = (wgs + slots - 1) / slots;
+      const int64_t per_cu = std::min<int64_t>(wgs, slots) / std::max<int64_t>(1, std::min<int64_t>(wgs, cus));
+      const double wg_bytes = (double)(M + 16 * cf) * 128.0 * ((Kb + sp - 1) / sp);
+      const double t_cu = rounds * wg_bytes * std::max<int64_t>(1, per_cu) / 130e9;
+      const double hbm = (double)N * K + (sp > 1 ? 2.0 * sp * tiles * pl.mf * cf * 1024 : 0.0);
+      const double t = std::max(t_cu, hbm / 6e12) + (sp > 1 ? 1e-6 : 0.0);
+      if (best < 0 || t < best) {
+        best = t;
+        pl.cf = cf;
+        pl.splits = sp;
+      }
+    }
+  }
+  *out = pl;
+  return pl.cf > 0;
+}
+
+template <int MF, int CF>
+fg_status launch_skinny_cfg(fg::GemmParams& p, int splits, hipStream_t stream, const char* what) {
+  using C = fg::SkinnyCfg<MF, CF>;
+  const int64_t tiles = (p.N + C::COLS - 1) / C::COLS;
+  const int64_t grid = tiles * splits;
+  if (grid >= ((int64_t)1 << 31)) return fail(FG_EUNSUPPORTED, "too many column tiles");
+  p.num_tiles = (int)tiles;
+  if (env_flag("FG_PRINT_CONFIGS"))
+    fprintf(stderr, "[fp8gemm] %s M=%d N=%d K=%d skinny rows=%d cols=%d splits=%d grid=%lld\n", what, p.rows, p.N,
+            p.K, C::ROWS, C::COLS, splits, (long long)grid);
+  hipLaunchKernelGGL((fg::gemm_fp8_skinny_kernel<C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p, splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return FG_OK;
+}
+
+fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, hipStream_t stream, const char* what) {
+  if (pl.splits > 1) {
+    Workspace* ws = workspace(kWsSkinny, (void*)stream, kSkinnyPartialBytes, kSkinnyMaxTiles);
+    if (!ws) return fail(FG_EHIP, "%s: split-K workspace unavailable", what);
+    p.sk_partials = ws->partials;
+    p.sk_flags = ws->flags;
+  }
+#define FG_SKINNY_CASE(MF, CF) \
+  if (pl.mf == MF && pl.cf == CF) return launch_skinny_cfg<MF, CF>(p, pl.splits, stream, what);
+  FG_SKINNY_CASE(4, 1) FG_SKINNY_CASE(4, 2) FG_SKINNY_CASE(4, 4)
+  FG_SKINNY_CASE(8, 1) FG_SKINNY_CASE(8, 2)
+#undef FG_SKINNY_CASE
+  return fail(FG_EUNSUPPORTED, "%s: no skinny configuration", what);
+}
+
 fg_status check_ld(int64_t ld, int64_t row, int64_t mult, const char* name) {
   if (ld < row) return fail(FG_EINVAL, "%s=%lld is smaller than the row length %lld", name, (long long)ld, (long long)row);
   if (ld % mult) return fail(FG_EALIGN, "%s=%lld is not a multiple of %lld", name, (long long)ld, (long long)mult);
@@ -296,11 +417,11 @@ fg_status check_ptr(const void* p, uintptr_t align, const char* name) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
-// Buffer offsets inside a tile are 32-bit: rows of up to 16 MiB.
-constexpr int64_t kMaxLd = (int64_t)1 << 24;
+// Buffer offsets inside a tile are 32-bit: 256 rows of up to 4 MiB.
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
 
 fg_status check_row_bytes(int64_t lda, int64_t ldb) {
-  if (lda > kMaxLd || ldb > kMaxLd) return fail(FG_EUNSUPPORTED, "operand rows above 16 MiB");
+  if (lda > kMaxLd || ldb > kMaxLd) return fail(FG_EUNSUPPORTED, "operand rows above 4 MiB");
   return FG_OK;
 }
 
@@ -331,6 +452,17 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
   p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
   p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
   if (K > 0) {
+    // few activation rows: the weight-streaming kernel
+    const char* force = getenv("FG_FORCE_CONFIG");
+    if (!(force && (strcmp(force, "big") == 0 || strcmp(force, "small") == 0))) {
+      int all_cus = 0;
+      FG_TRY(device_cus(&all_cus));  // the plan (and so the summation order) does not depend on the CU cap
+      SkinnyPlan pl;
+      const bool may_split = !stream_capturing(stream) ||
+                             workspace(kWsSkinny, stream, kSkinnyPartialBytes, kSkinnyMaxTiles) != nullptr;
+      if (plan_skinny(M, N, K, lda, ld_sa, all_cus, may_split, &pl))
+        return launch_skinny(p, pl, (hipStream_t)stream, "gemm_fp8_nt");
+    }
     using C = CfgBig;
     const int64_t tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
     if (prefer_big(tm * tn) && tm * tn < ((int64_t)1 << 30)) {
@@ -343,7 +475,7 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
       if (want_stream_k(tm * tn, p.Kb, cus)) {
         int all_cus = 0;
         FG_TRY(device_cus(&all_cus));
-        SkWorkspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
+        Workspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
         if (ws) return launch_stream_k<C>(p, (hipStream_t)stream, cus, ws, "gemm_fp8_nt[stream-k]");
       }
       return launch_big_width<fg::kDense>(p, 1, (hipStream_t)stream, "gemm_fp8_nt");

@@ -62,6 +62,13 @@ struct GemmParams {
   int* sk_flags;
 };
 
+// A value that no kernel writes while this one runs (the masked counts),
+// read through the scalar cache: a vector load would make the wave wait for
+// its whole queue of outstanding operand loads before using it.
+__device__ __forceinline__ int load_invariant(const int* p) {
+  return *(const __attribute__((address_space(4))) int*)p;
+}
+
 // Position of a workgroup in the persistent walk such that the workgroups of
 // one XCD take consecutive work ids.
 __device__ __forceinline__ int xcd_local_id(int b, int grid) {
@@ -137,7 +144,7 @@ __device__ __forceinline__ bool resolve_tile(const GemmParams& p, int w, int BM,
     const int per_group = p.tiles_m * p.tiles_n;
     const int g = w / per_group;
     raster(w - g * per_group, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int valid = min(max(p.masked_m[g], 0), p.rows);
+    const int valid = min(max(load_invariant(p.masked_m + g), 0), p.rows);
     if (tm * BM >= valid) return false;
     const int64_t Kb = p.Kb;
     t.A = p.A + (int64_t)g * p.rows * p.K;
@@ -175,7 +182,8 @@ __device__ __forceinline__ bool resolve_tile(const GemmParams& p, int w, int BM,
   }
   t.m0 = tm * BM;
   t.n0 = tn * BN;
-  t.rows_alloc = p.rows;
+  // masked: rows past the group's count are never read (they load as zeros)
+  t.rows_alloc = L == kMasked ? t.rows_valid : p.rows;
   return true;
 }
 
@@ -437,7 +445,7 @@ __device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t)
     const int per_group = p.tiles_m * p.tiles_n;
     const int g = w / per_group;
     raster(w - g * per_group, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int valid = min(max(p.masked_m[g], 0), p.rows);
+    const int valid = min(max(load_invariant(p.masked_m + g), 0), p.rows);
     if (tm * BM >= valid) return false;
     const int64_t Kb = p.Kb;
     t.A = p.A + (int64_t)g * p.rows * p.K;
@@ -475,7 +483,8 @@ __device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t)
   }
   t.m0 = tm * BM;
   t.n0 = tn * BN;
-  t.rows_alloc = p.rows;
+  // masked: rows past the group's count are never read (they load as zeros)
+  t.rows_alloc = L == kMasked ? t.rows_valid : p.rows;
   return true;
 }
 

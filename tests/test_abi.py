@@ -75,7 +75,7 @@ def dense(lib, A=P16, lda=512, sa=P16, ld_sa=64, B=P16, ldb=512, sb=P16, D=P16, 
         (dict(ldb=520), FG_EALIGN, "ldb=520"),
         (dict(ldd=200), FG_EINVAL, "ldd=200"),
         (dict(ld_sa=32), FG_EINVAL, "ld_sa=32"),
-        (dict(lda=(1 << 24) + 16, ldb=(1 << 24) + 16), FG_EUNSUPPORTED, "16 MiB"),
+        (dict(lda=(1 << 22) + 16, ldb=(1 << 22) + 16), FG_EUNSUPPORTED, "4 MiB"),
         (dict(M=(1 << 30) + 1, ld_sa=1 << 31), FG_EUNSUPPORTED, "2^30"),
     ],
 )

@@ -73,7 +73,10 @@ def test_contiguous_exact_regime_bitwise(gpu_lib):
     assert (bits[~valid] == SENTINEL_BF16).all()
 
 
-def test_contiguous_equals_dense_per_group(gpu_lib):
+def test_contiguous_equals_dense_per_group(gpu_lib, monkeypatch):
+    """Bit for bit against the large-tile dense kernel, which adds the slices
+    in the same order (the few-row dense kernel adds per-wave K partials)."""
+    monkeypatch.setenv("FG_FORCE_CONFIG", "big")
     announce("contiguous vs dense per group")
     A32, B32, idx = synth.contiguous_problem([256, 128, 384], 384, 768, seed=8)
     qa, sa = quant.quantize_per_token(A32.numpy())
@@ -158,7 +161,8 @@ def test_masked_exact_regime_bitwise(gpu_lib):
     assert (bits[~valid] == SENTINEL_BF16).all()
 
 
-def test_masked_full_equals_dense(gpu_lib):
+def test_masked_full_equals_dense(gpu_lib, monkeypatch):
+    monkeypatch.setenv("FG_FORCE_CONFIG", "big")  # the large-tile dense kernel: same summation order
     announce("masked mask==M_cap vs dense")
     rng = np.random.default_rng(6)
     G, Mc, N, K = 3, 130, 264, 512
