@@ -17,6 +17,8 @@ published 5.0 PFLOP/s dense FP8 peak; ``traffic`` is the HBM bytes per launch
 measured with rocprofv3 counters when the committed counter summary matches
 the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
 oracle timed on a bounded sample of output blocks of the same workload.
+``other_configs`` adds per-shape figures for the small-M dense, contiguous
+and masked workloads (skip with --no-other-configs).
 """
 
 from __future__ import annotations
@@ -123,6 +125,101 @@ def time_casts(problems, reps=10):
     return out
 
 
+def graph_time(launch, launches: int = 20, reps: int = 5) -> float:
+    """GPU milliseconds per launch of `launch(i)` without host overhead: the
+    launches are captured into one HIP graph (after warm-up calls on the same
+    stream, which also create any workspace) and the graph is replayed."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in range(3):
+            launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(launches):
+            launch(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / launches)
+    return float(np.median(ts))
+
+
+def shape_entry(config, shape, ms, flops, nbytes, bound):
+    tf = flops / ms / 1e9
+    gbs = nbytes / ms / 1e6
+    return {"config": config, "shape": list(shape), "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+            "pct_mfma": round(tf / PEAK_FP8_TFLOPS * 100, 1), "gbs": round(gbs, 1),
+            "pct_hbm": round(gbs / PEAK_HBM_GBS * 100, 1), "bound": bound}
+
+
+def other_configs():
+    """Per-shape throughput of the small-M dense, contiguous and masked
+    workloads.  Weight operands are rotated over copies totalling more than
+    the 256 MB last-level cache, so every launch reads them from HBM; the
+    memory-bound launches are timed by graph replay (their GPU time is a few
+    microseconds, below the host's per-call cost)."""
+    out = []
+    for (M, N, K) in synth.DENSE_SMALL_M.shapes:
+        A32, B32 = synth.dense_problem(M, N, K, seed=0)
+        qa, sa = fg.fp8_cast_per_token(A32.cuda())
+        qb, sb = fg.fp8_cast_per_block(B32.cuda())
+        copies = [qb] + [qb.clone() for _ in range(max(1, int(600e6 // (N * K))))]
+        D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ms = graph_time(lambda i: fg.gemm_fp8_nt(qa, sa, copies[i % len(copies)], sb, D))
+        Kb = K // 128
+        nbytes = M * K + N * K + 4 * (M * Kb + -(-N // 128) * Kb) + 2 * M * N
+        out.append(shape_entry("dense_small_m", (M, N, K), ms, 2 * M * N * K, nbytes, "hbm"))
+        del copies
+    G, rows, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
+    A32, B32, idx = synth.contiguous_problem([rows] * G, N, K, seed=0)
+    qa, sa = fg.fp8_cast_per_token(A32.cuda())
+    qb, sb = fg.fp8_cast_per_block(B32.reshape(G * N, K).cuda())
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
+    mi = torch.from_numpy(idx.astype(np.int32)).cuda()
+    D = torch.empty(idx.shape[0], N, dtype=torch.bfloat16, device="cuda")
+    fg.gemm_fp8_grouped_contiguous(qa, sa, qb, sb, mi, D)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fg.gemm_fp8_grouped_contiguous(qa, sa, qb, sb, mi, D)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    Mt = idx.shape[0]
+    out.append(shape_entry("contiguous_8x4096", (G, rows, N, K), float(np.median(ts)), 2 * Mt * N * K,
+                           Mt * K + G * N * K + 2 * Mt * N, "mfma"))
+    del A32, B32, qa, qb, D
+    for (G, Mc, N, K) in synth.MASKED_16x256.shapes:
+        A32, B32, mask = synth.masked_problem(G, Mc, N, K, seed=0)
+        qa = torch.empty(G, Mc, K, dtype=torch.uint8, device="cuda")
+        sa = fg.empty_activation_scales(Mc, K, groups=G)
+        for g in range(G):
+            fg.fp8_cast_per_token(A32[g].cuda(), qa[g], sa[g])
+        qb, sb = fg.fp8_cast_per_block(B32.reshape(G * N, K).cuda())
+        qb, sb = qb.view(G, N, K), sb.view(G, -(-N // 128), K // 128)
+        copies = [qb] + [qb.clone() for _ in range(max(1, int(700e6 // (G * N * K))))]
+        mt = torch.from_numpy(np.asarray(mask, np.int32)).cuda()
+        D = torch.empty(G, Mc, N, dtype=torch.bfloat16, device="cuda")
+        em = int(np.mean(mask))
+        ms = graph_time(lambda i: fg.gemm_fp8_grouped_masked(qa, sa, copies[i % len(copies)], sb, mt, D, expected_m=em),
+                        launches=10)
+        rv = int(np.sum(mask))
+        out.append(shape_entry("masked_16x256", (G, Mc, N, K), ms, 2 * rv * N * K, rv * K + G * N * K + 2 * rv * N,
+                               "hbm"))
+        del copies, qa, qb, D
+    return out
+
+
 def cpu_baseline(problems, budget_s: float = 15.0):
     """The CPU oracle (fp64 blockwise GEMM) on a bounded sample of output
     blocks of every shape: rows [0, ms) x columns [0, ns) at full K, with the
@@ -185,6 +282,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_m4096", choices=["dense_m4096", "dense_small_m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the small-M dense, contiguous and masked per-shape measurements")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 3 times (counter calibration)")
     args = ap.parse_args()
@@ -210,6 +309,7 @@ def main():
 
     wall, per = time_steps(problems, args.steps, args.warmup)
     casts = time_casts(problems)
+    others = None if args.no_other_configs else other_configs()
     gemm_ms = per.sum(axis=1)  # GEMM time per step (sum of launch durations)
     total_flops = sum(pb.flops for pb in problems)
     total_bytes = sum(pb.bytes for pb in problems)
@@ -242,6 +342,7 @@ def main():
                    "gbs": round(total_bytes / (step_ms * 1e-3) / 1e9, 1)},
         "shapes": shapes,
         "cast": casts,
+        "other_configs": others,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

@@ -24,11 +24,15 @@
  * are per 128x128 block, row-major: sb[nb * Kb + kb].
  *
  * Ownership.  Every pointer named "device" is device memory owned by the
- * caller; the library never allocates, frees or retains pointers, and never
- * synchronises the host.  Each GEMM or cast call only enqueues kernels on
- * `stream` (a hipStream_t; NULL is the default stream) and returns.  The calls
- * are therefore safe to capture in a HIP graph, which is what the masked form
- * is for (the host never learns the per-expert counts).
+ * caller; the library never frees or retains caller pointers.  Each GEMM or
+ * cast call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns.  The one exception to "allocates nothing" is
+ * the split-K workspace of gemm_fp8_nt (see there): 16 MiB of fp32 partials
+ * and 64 KiB of counters, allocated by the first call that needs it on a
+ * (device, stream) pair and kept until the process ends.  A call whose stream
+ * is being captured into a HIP graph never allocates (it takes a path without
+ * a workspace), so every call is safe to capture; the masked form, whose
+ * counts the host never learns, is made for that.
  *
  * Errors.  Preconditions that the host can check are checked before anything
  * is launched; on failure the call returns the status, launches nothing, and
@@ -65,7 +69,12 @@ typedef enum {
  *   D   device [M, N] bf16, row stride ldd elems   (ldd >= N, 2-byte aligned; rows that are 8- or
  *       16-byte aligned get vector stores); written
  * M, N >= 0 arbitrary; K % 128 == 0.  K == 0 writes D = 0 (sa, sb may then be NULL).
- * Only D[0:M, 0:N] is written.
+ * Only D[0:M, 0:N] is written.  lda, ldb <= 4 MiB (FG_EUNSUPPORTED beyond).
+ * Few rows (M <= 128): a weight-streaming kernel that may split K over
+ * several workgroups; their fp32 partials meet in the library's workspace for
+ * (device, stream) and are added in a fixed order (results do not depend on
+ * the CU cap).  Calls on one stream are ordered; calls on different streams
+ * use different workspaces.
  * Optional stream-K (environment FG_STREAM_K=1; off by default): the K
  * slices of all tiles are split evenly over the workgroups and fp32 partial
  * tiles are exchanged through a workspace that the library allocates on the

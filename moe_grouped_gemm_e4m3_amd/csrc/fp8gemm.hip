@@ -304,13 +304,13 @@ bool prefer_big(int64_t big_tiles) {
 
 // ---------------------------------------------------------------------------
 // Skinny kernel (dense, M <= 128).  The plan picks the column-tile width
-// (16 CF weight rows per workgroup) and the K split from a two-term model:
-// every active CU must pull its operands through its own L1 (about 130 GB/s
-// each: (M + 16 CF) x K / splits bytes per workgroup), and the weights plus
-// any partials must come through HBM (about 6 TB/s).  Narrow tiles spread the
-// weights over more CUs but make every CU read the activations again; a K
-// split spreads both over more workgroups at the cost of fp32 partials.
-// FG_SKINNY="CF,SPLITS" overrides the choice (tuning and tests).
+// (16 CF weight rows per workgroup) and the K split.  Measured on MI355X on
+// the decode shapes (M = 64, 128; N = 2112 .. 7168), 32-column tiles are best
+// throughout: narrower tiles make every CU read the activations again for
+// fewer weights, wider ones leave CUs idle.  The K split only has to bring
+// the workgroup count near the CU count; each further split adds fp32
+// partial traffic and a reduction.  FG_SKINNY="CF,SPLITS" overrides the
+// choice (tuning and tests).
 
 constexpr size_t kSkinnyPartialBytes = (size_t)16 << 20;
 constexpr int kSkinnyMaxTiles = 1 << 14;
@@ -319,7 +319,6 @@ struct SkinnyPlan {
   int mf = 0, cf = 0, splits = 1;
 };
 
-int skinny_occ(int mf, int cf) { return mf * cf <= 8 ? 2 : 1; }
 
 bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool may_split, SkinnyPlan* out) {
   if (M > 128 || K < 128) return false;
@@ -344,30 +343,14 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
       return true;
     }
   }
-  double best = -1;
-  for (int cf : {1, 2, 4}) {
-    if (pl.mf * cf > 16) continue;  // registers: at most 16 output blocks per wave
-    const int occ = skinny_occ(pl.mf, cf);
-    const int64_t tiles = (N + 16 * cf - 1) / (16 * cf);
-    for (int sp : {1, 2, 4, 8, 16}) {
-      if (sp > 1 && (!may_split || Kb < 4 * sp || tiles > kSkinnyMaxTiles ||
-                     (size_t)sp * tiles * pl.mf * cf * 1024 > kSkinnyPartialBytes))
-        continue;
-      const int64_t wgs = tiles * sp;
-      const int64_t slots = (int64_t)cus * occ;
-      const int64_t rounds = (wgs + slots - 1) / slots;
-      const int64_t per_cu = std::min<int64_t>(wgs, slots) / std::max<int64_t>(1, std::min<int64_t>(wgs, cus));
-      const double wg_bytes = (double)(M + 16 * cf) * 128.0 * ((Kb + sp - 1) / sp);
-      const double t_cu = rounds * wg_bytes * std::max<int64_t>(1, per_cu) / 130e9;
-      const double hbm = (double)N * K + (sp > 1 ? 2.0 * sp * tiles * pl.mf * cf * 1024 : 0.0);
-      const double t = std::max(t_cu, hbm / 6e12) + (sp > 1 ? 1e-6 : 0.0);
-      if (best < 0 || t < best) {
-        best = t;
-        pl.cf = cf;
-        pl.splits = sp;
-      }
-    }
-  }
+  pl.cf = 2;
+  const int64_t tiles = (N + 31) / 32;
+  int sp = 1;
+  if (may_split && tiles * 4 < (int64_t)cus * 3) sp = tiles * 4 >= cus ? 2 : 4;
+  while (sp > 1 && (Kb < 4 * sp || tiles > kSkinnyMaxTiles ||
+                    (size_t)sp * tiles * pl.mf * pl.cf * 1024 > kSkinnyPartialBytes))
+    sp /= 2;
+  pl.splits = sp;
   *out = pl;
   return pl.cf > 0;
 }

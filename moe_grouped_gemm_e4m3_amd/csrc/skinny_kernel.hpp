@@ -32,6 +32,18 @@
 
 namespace fg {
 
+#ifndef FG_SKINNY_DEPTH
+#define FG_SKINNY_DEPTH 2
+#endif
+constexpr int kSkinnyDepth = FG_SKINNY_DEPTH;
+
+// Workgroups per CU the registers allow: a wave holds DEPTH slices of
+// fragments and scales, the slice partials and the accumulators; two
+// workgroups per CU (two waves per SIMD) leave it 256 registers.
+constexpr __host__ __device__ int skinny_occupancy(int mf, int cf) {
+  return kSkinnyDepth * (8 * mf + 8 * cf + mf) + 8 * mf * cf <= 240 ? 2 : 1;
+}
+
 template <int MF_, int CF_>
 struct SkinnyCfg {
   static constexpr int MF = MF_;  // 16-row activation fragments (rows = 16 MF)
@@ -40,8 +52,8 @@ struct SkinnyCfg {
   static constexpr int ROWS = 16 * MF, COLS = 16 * CF;
   static constexpr int GROUPS = MF * CF;  // 16x16 output blocks of the tile
   static constexpr int GPW = GROUPS / WAVES;
-  // two slices of fragments, the partials and the accumulators in registers
-  static constexpr int OCC = MF * CF <= 8 ? 2 : 1;
+  static constexpr int DEPTH = kSkinnyDepth;  // slices of fragments per wave in the ring
+  static constexpr int OCC = skinny_occupancy(MF, CF);
   static constexpr int LDS = WAVES * GROUPS * 64 * 16 + 16;  // wave partials + flag
   static_assert(GROUPS % WAVES == 0, "output blocks split over the waves");
   static_assert(128 % COLS == 0, "a column tile lies in one weight-scale block");
@@ -163,31 +175,42 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
     for (int r = 0; r < 4; ++r) acc[x][r] = 0.f;
 
   {
-    // Two register slices: the next slice's loads are in flight while this
-    // one's MFMAs run.  An odd slice goes first on its own, so the pipelined
-    // loop has no conditional work (the compiler would otherwise sink a
-    // conditionally used load down to its use); its last iteration fetches
-    // the final slice once more, unused.  The scheduling barriers keep each
-    // batch of loads ahead of the MFMAs that do not need it.
-    SkinnySlice<C> f0, f1;
-    int kb = kw0;
-    if ((kw1 - kw0) & 1) {
-      skinny_load<C>(f0, g, kb);
-      skinny_compute<C>(f0, acc);
-      ++kb;
+    // The wave visits its slices in a rotated order that depends on the
+    // workgroup: workgroups running side by side then read different K slices
+    // of the (shared, few-row) activations instead of all requesting the
+    // same L2 lines at once.  The order is a fixed function of the workgroup
+    // and wave, so the fp32 sum is reproducible.
+    const int n = kw1 - kw0;
+    const int rot = n > 0 ? (int)((blockIdx.x * 5u + (unsigned)wave * 3u) % (unsigned)n) : 0;
+    auto kat = [&](int i) {
+      const int j = i + rot;
+      return kw0 + (j >= n ? j - n : j);
+    };
+    // A ring of DEPTH register slices: the loads of the next DEPTH - 1
+    // slices are in flight while one slice's MFMAs run.  The n % DEPTH
+    // leading slices go first on their own, so the pipelined loop has no
+    // conditional work (the compiler would otherwise sink a conditionally
+    // used load down to its use); its last iterations fetch the final slice
+    // again, unused.  The scheduling barriers keep each batch of loads ahead
+    // of the MFMAs that do not need it.
+    constexpr int DEPTH = C::DEPTH;
+    SkinnySlice<C> f[DEPTH];
+    int i = 0;
+    for (const int lead = n % DEPTH; i < lead; ++i) {
+      skinny_load<C>(f[0], g, kat(i));
+      skinny_compute<C>(f[0], acc);
     }
-    if (kb < kw1) {
-      const int klast = kw1 - 1;
-      skinny_load<C>(f0, g, kb);
-      for (; kb < kw1; kb += 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        skinny_load<C>(f1, g, kb + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        skinny_compute<C>(f0, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        skinny_load<C>(f0, g, min(kb + 2, klast));
-        __builtin_amdgcn_sched_barrier(0);
-        skinny_compute<C>(f1, acc);
+    if (i < n) {
+#pragma unroll
+      for (int d = 0; d + 1 < DEPTH; ++d) skinny_load<C>(f[d], g, kat(min(i + d, n - 1)));
+      for (; i < n; i += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          __builtin_amdgcn_sched_barrier(0);
+          skinny_load<C>(f[(d + DEPTH - 1) % DEPTH], g, kat(min(i + d + DEPTH - 1, n - 1)));
+          __builtin_amdgcn_sched_barrier(0);
+          skinny_compute<C>(f[d], acc);
+        }
       }
     }
   }
