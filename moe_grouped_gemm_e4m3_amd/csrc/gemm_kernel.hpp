@@ -390,6 +390,10 @@ struct BigCfg {
   // 1 KiB (8-row) loads per slice: half of the waves load the A rows, the
   // other half the B rows, consecutive loads per wave
   static constexpr int LOADS_A = BM / 8 / (NWAVES / 2), LOADS_B = BN / 8 / (NWAVES / 2);
+  // LDS: two operand stages, then the activation scales of each stage (one
+  // fp32 per tile row, 1 KiB per stage)
+  static constexpr int SA_OFF = 2 * STAGE;
+  static constexpr int LDS_BYTES = 2 * STAGE + 2 * 1024;
   // A wave's columns lie in one 128-wide weight-scale block when the tile
   // width is a multiple of 128 and the wave width divides 128; otherwise a
   // wave may straddle one block boundary and picks the scale per subtile.
@@ -397,6 +401,7 @@ struct BigCfg {
   static_assert(NWAVES % 2 == 0 && BM % (4 * NWAVES) == 0 && BN % (4 * NWAVES) == 0, "loads");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && WN <= 128, "wave tile");
   static_assert(BN <= 256, "epilogue staging rows are 512 bytes");
+  static_assert(BM <= 64 * (NWAVES / 2), "one 64-row activation-scale load per A wave");
   static_assert(BM % 128 == 0 || BM <= 128, "row halves");
 };
 
@@ -511,7 +516,7 @@ __device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& i
 
 template <class C>
 __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Work& t, int kb, uint8_t* stage,
-                                                  int wave, int lane) {
+                                                  uint8_t* sa_area, int wave, int lane) {
   constexpr int BM = C::BM;
   constexpr int HALF = C::NWAVES / 2, LA = C::LOADS_A, LB = C::LOADS_B;
   const bool is_a = wave < HALF;  // wave-uniform: the first half of the waves loads A, the second B
@@ -536,29 +541,44 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
                                                16, voff, kb * 128, 0, 0);
     }
   }
+  if (is_a) {
+    // sa[kb][m0 + 64 wave + lane] into the stage's scale area; rows past
+    // rows_alloc read as 0 (their outputs are never stored)
+    const float* sbase = t.sa + (int64_t)kb * p.ld_sa + t.m0;
+    const int sbytes = max(t.rows_alloc - t.m0, 0) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(sbase, sbytes),
+                                             (__attribute__((address_space(3))) void*)(sa_area + wave * 256), 4,
+                                             (wave * 64 + lane) * 4, 0, 0, 0);
+  }
 }
 
-// Scales of one K slice for this lane's SM rows: sa[kb][m] per row and the
-// weight-block scales sb[nb][kb] of the (at most two) 128-column blocks the
-// wave's columns touch.  Issued one slice ahead, before that slice's operand
-// loads, so the compute never waits on them.
+// Weight-block scales sb[nb][kb] of the (at most two) 128-column blocks the
+// wave's columns touch, for one K slice.  They are wave-uniform and never
+// written while a GEMM runs, so they are read through the scalar cache; the
+// activation scales of the slice arrive in LDS with its operands.
 template <class C>
-__device__ __forceinline__ void load_scales(const GemmParams& p, const Work& t, int kb, int wm, int wn, int l16,
-                                            float (&sa_r)[C::SM], float (&sb_r)[2]) {
+__device__ __forceinline__ void load_sb(const GemmParams& p, const Work& t, int kb, int wn, float (&sb_r)[2]) {
   const int nw = t.n0 + wn * C::WN;
   const int nb0 = min(nw >> 7, p.Nb - 1);
-  sb_r[0] = t.sb[(int64_t)nb0 * p.Kb + kb];
+  const __attribute__((address_space(4))) float* sbk = (const __attribute__((address_space(4))) float*)(t.sb + kb);
+  sb_r[0] = sbk[(int64_t)nb0 * p.Kb];
   if (!C::SCALE_PER_WAVE) {
     const int nb1 = min(nb0 + 1, p.Nb - 1);
-    sb_r[1] = t.sb[(int64_t)nb1 * p.Kb + kb];
+    sb_r[1] = sbk[(int64_t)nb1 * p.Kb];
   } else {
     sb_r[1] = sb_r[0];
   }
-  const float* sa_k = t.sa + (int64_t)kb * p.ld_sa;
+}
+
+// s = sa * sb for this lane's SM rows, sa read from the stage's scale area.
+template <class C>
+__device__ __forceinline__ void slice_scales(const uint8_t* sa_area, int wm, int l16, const float (&sb)[2],
+                                             float (&s)[C::SM][2]) {
 #pragma unroll
   for (int ms = 0; ms < C::SM; ++ms) {
-    const int m = min(t.m0 + wm * C::WM + ms * 16 + l16, t.rows_alloc - 1);
-    sa_r[ms] = sa_k[m];
+    const float a = *(const float*)(sa_area + (wm * C::WM + ms * 16 + l16) * 4);
+    s[ms][0] = a * sb[0];
+    s[ms][1] = a * sb[1];
   }
 }
 
@@ -721,8 +741,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   constexpr int SM = C::SM, SN = C::SN;
 
   // two operand stages
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 #define FG_STAGE(i) (lds + (i) * C::STAGE)
+#define FG_SA(i) (lds + C::SA_OFF + (i) * 1024)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -753,9 +774,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   if (!(local < p.num_tiles && resolve_big<L, BM, BN>(p, local, cur))) advance_big<L, BM, BN>(p, cur, it, local, grid);
   if (cur.w < 0) return;
 
-  float sa_c[SM], sb_c[2];
-  load_scales<C>(p, cur, 0, wm, wn, l16, sa_c, sb_c);
-  issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), wave, lane);
+  float sb_c[2];
+  load_sb<C>(p, cur, 0, wn, sb_c);
+  issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -780,24 +801,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
     for (int kb = 0; kb < Kb; ++kb) {
       // prefetch the following slice: this tile's next one, or the first of the next work item
       const bool last = kb + 1 == Kb;
-      float sa_n[SM], sb_n[2] = {0.f, 0.f};
-#pragma unroll
-      for (int ms = 0; ms < SM; ++ms) sa_n[ms] = 0.f;
+      float sb_n[2] = {0.f, 0.f};
       if (!last) {
-        load_scales<C>(p, cur, kb + 1, wm, wn, l16, sa_n, sb_n);
-        issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), wave, lane);
+        load_sb<C>(p, cur, kb + 1, wn, sb_n);
+        issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       } else if (nxt.w >= 0) {
-        load_scales<C>(p, nxt, 0, wm, wn, l16, sa_n, sb_n);
-        issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), wave, lane);
+        load_sb<C>(p, nxt, 0, wn, sb_n);
+        issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       }
 
       if (active) {
         float s[SM][2];
-#pragma unroll
-        for (int ms = 0; ms < SM; ++ms) {
-          s[ms][0] = sa_c[ms] * sb_c[0];
-          s[ms][1] = sa_c[ms] * sb_c[1];
-        }
+        slice_scales<C>(FG_SA(stage), wm, l16, sb_c, s);
         slice_mma<C>(FG_STAGE(stage), a_off, b_off, s, tb, acc);
       }
 
@@ -808,8 +823,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       stage ^= 1;
-#pragma unroll
-      for (int ms = 0; ms < SM; ++ms) sa_c[ms] = sa_n[ms];
       sb_c[0] = sb_n[0];
       sb_c[1] = sb_n[1];
     }
@@ -830,6 +843,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   // no LDS-direct load may still be in flight when the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(0);
 #undef FG_STAGE
+#undef FG_SA
 }
 
 
@@ -923,8 +937,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
   constexpr int SM = C::SM, SN = C::SN;
   constexpr int NACC = SM * SN * 4;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 #define FG_STAGE(i) (lds + (i) * C::STAGE)
+#define FG_SA(i) (lds + C::SA_OFF + (i) * 1024)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -961,9 +976,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
   Work cw;
   sk_tile_work<C>(p, cur.t, cw);
 
-  float sa_c[SM], sb_c[2];
-  load_scales<C>(p, cw, cur.k0, wm, wn, l16, sa_c, sb_c);
-  issue_slice_loads<C>(p, cw, cur.k0, FG_STAGE(0), wave, lane);
+  float sb_c[2];
+  load_sb<C>(p, cw, cur.k0, wn, sb_c);
+  issue_slice_loads<C>(p, cw, cur.k0, FG_STAGE(0), FG_SA(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -985,23 +1000,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
 
     for (int kb = cur.k0; kb < cur.k1; ++kb) {
       const bool last = kb + 1 == cur.k1;
-      float sa_n[SM], sb_n[2] = {0.f, 0.f};
-#pragma unroll
-      for (int ms = 0; ms < SM; ++ms) sa_n[ms] = 0.f;
+      float sb_n[2] = {0.f, 0.f};
       if (!last) {
-        load_scales<C>(p, cw, kb + 1, wm, wn, l16, sa_n, sb_n);
-        issue_slice_loads<C>(p, cw, kb + 1, FG_STAGE(stage ^ 1), wave, lane);
+        load_sb<C>(p, cw, kb + 1, wn, sb_n);
+        issue_slice_loads<C>(p, cw, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       } else if (nxt.t >= 0) {
-        load_scales<C>(p, nw, nxt.k0, wm, wn, l16, sa_n, sb_n);
-        issue_slice_loads<C>(p, nw, nxt.k0, FG_STAGE(stage ^ 1), wave, lane);
+        load_sb<C>(p, nw, nxt.k0, wn, sb_n);
+        issue_slice_loads<C>(p, nw, nxt.k0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       }
       if (cw.m0 + wm * WM < cw.rows_valid) {
         float sc[SM][2];
-#pragma unroll
-        for (int ms = 0; ms < SM; ++ms) {
-          sc[ms][0] = sa_c[ms] * sb_c[0];
-          sc[ms][1] = sa_c[ms] * sb_c[1];
-        }
+        slice_scales<C>(FG_SA(stage), wm, l16, sb_c, sc);
         slice_mma<C>(FG_STAGE(stage), a_off, b_off, sc, second_block_subtile<C>(cw, wn), acc);
       }
       __builtin_amdgcn_s_waitcnt(0);
@@ -1009,8 +1018,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       stage ^= 1;
-#pragma unroll
-      for (int ms = 0; ms < SM; ++ms) sa_c[ms] = sa_n[ms];
       sb_c[0] = sb_n[0];
       sb_c[1] = sb_n[1];
     }
@@ -1093,6 +1100,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p
   }
   __builtin_amdgcn_s_waitcnt(0);
 #undef FG_STAGE
+#undef FG_SA
 }
 
 }  // namespace fg
