@@ -20,6 +20,10 @@ section; the texts are machine-extracted and partly machine-translated):
   topic 19444, opening bullets; the same digest, "GEMM arayuzu ve yerlesim
   kisitlari", says SM90 scale factors are FP32 and that casting is the user's
   job, done by simple helpers).
+* power-of-two (UE8M0) factors (``oracle.quant``, ``*_ue8m0``): the same
+  digest section says the newer architecture takes UE8M0 factors packed four
+  to an int32; the fp32 factor is rounded up to a power of two and packed
+  along K (readings stated in ``oracle.quant``).
 * the GEMM D = bf16(A . B^T) with per-128-K-slice promotion (``oracle.gemm``):
   "GEMM arayuzu ve yerlesim kisitlari" (NT layout, D = C + A @ B.T, no C here)
   and the two-level promotion described in the release summary's opening

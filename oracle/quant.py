@@ -80,3 +80,97 @@ def quantize_per_block(w) -> tuple[np.ndarray, np.ndarray]:
         sb[nb] = s
         q[rows] = _encode_scaled(blk, s[None, :, None]).reshape(-1, K)
     return q, sb
+
+
+# ---------------------------------------------------------------------------
+# Power-of-two (UE8M0) scale factors.
+#
+# The digest's layout section ("GEMM arayuzu ve yerlesim kisitlari", DeepGEMM
+# digest, GeekNews topic 19459) says the newer architecture takes its scale
+# factors as UE8M0 -- an unsigned 8-bit exponent, value 2**(e - 127) -- with
+# four of them packed into one 32-bit integer.  It gives no rounding rule and
+# no packing axis.  Readings taken:
+#
+# * same granularity as the fp32 factors (1 x 128 activations, 128 x 128
+#   weights);
+# * the factor is the fp32 one, max(amax, 1e-4) / 448, rounded UP to a power
+#   of two, so that |x / s| <= 448 still holds and no code saturates;
+# * q = e4m3fn_RNE(x / s), an exact scaling by a power of two before the
+#   rounding;
+# * four consecutive K groups of one row (activations) or one weight block
+#   row (weights) share an int32, K group 4i + j in byte j (least significant
+#   byte first); bytes past the last K group are unspecified.
+# ---------------------------------------------------------------------------
+
+UE8M0_BIAS = 127
+
+
+def ue8m0_round_up(s) -> np.ndarray:
+    """UE8M0 byte of the smallest power of two >= s, for positive normal fp32 s."""
+    m, e = np.frexp(np.asarray(s, dtype=np.float64))  # s = m * 2**e, 0.5 <= m < 1 (exact)
+    e = np.where(m == 0.5, e - 1, e)  # s is itself 2**(e - 1)
+    return (e + UE8M0_BIAS).astype(np.uint8)
+
+
+def ue8m0_decode(b) -> np.ndarray:
+    """UE8M0 bytes -> float32 powers of two (exact)."""
+    return np.ldexp(np.float32(1.0), np.asarray(b, dtype=np.int32) - UE8M0_BIAS).astype(np.float32)
+
+
+def quantize_per_token_ue8m0(x) -> tuple[np.ndarray, np.ndarray]:
+    """1x128 quantisation with power-of-two factors.
+
+    Returns (q uint8 [M, K], UE8M0 bytes uint8 [K/128, M]) -- K-group-major,
+    unpacked (see pack_ue8m0)."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    Kb = K // GROUP
+    xg = x.reshape(M, Kb, GROUP)
+    amax = np.abs(xg).max(axis=2) if M else np.zeros((0, Kb), np.float32)
+    e = ue8m0_round_up(_scale_from_amax(amax))  # [M, Kb]
+    q = _encode_scaled(xg, ue8m0_decode(e)[:, :, None]).reshape(M, K)
+    return q, np.ascontiguousarray(e.T)
+
+
+def quantize_per_block_ue8m0(w) -> tuple[np.ndarray, np.ndarray]:
+    """128x128 quantisation with power-of-two factors.
+
+    Returns (q uint8 [N, K], UE8M0 bytes uint8 [ceil(N/128), K/128])."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    Kb = K // GROUP
+    Nb = -(-N // GROUP)
+    q = np.empty((N, K), dtype=np.uint8)
+    eb = np.empty((Nb, Kb), dtype=np.uint8)
+    for nb in range(Nb):
+        rows = slice(nb * GROUP, min(N, (nb + 1) * GROUP))
+        blk = w[rows].reshape(-1, Kb, GROUP)
+        e = ue8m0_round_up(_scale_from_amax(np.abs(blk).max(axis=(0, 2))))
+        eb[nb] = e
+        q[rows] = _encode_scaled(blk, ue8m0_decode(e)[None, :, None]).reshape(-1, K)
+    return q, eb
+
+
+def pack_ue8m0(b, axis: int) -> np.ndarray:
+    """Pack UE8M0 bytes four to an int32 along `axis` (the K-group axis):
+    element i holds groups 4i .. 4i+3, group 4i + j in byte j.  Missing bytes
+    of the last element are 0."""
+    b = np.moveaxis(np.asarray(b, dtype=np.uint8), axis, -1)
+    n = b.shape[-1]
+    padded = np.zeros(b.shape[:-1] + (-(-n // 4) * 4,), np.uint8)
+    padded[..., :n] = b
+    words = padded.reshape(b.shape[:-1] + (-1, 4)).astype(np.uint32)
+    packed = words[..., 0] | (words[..., 1] << 8) | (words[..., 2] << 16) | (words[..., 3] << 24)
+    return np.ascontiguousarray(np.moveaxis(packed.view(np.int32), -1, axis))
+
+
+def unpack_ue8m0(p, n: int, axis: int) -> np.ndarray:
+    """Inverse of pack_ue8m0 for n K groups."""
+    p = np.moveaxis(np.asarray(p, dtype=np.int32), axis, -1).view(np.uint32)
+    parts = [((p >> (8 * j)) & 0xFF).astype(np.uint8) for j in range(4)]
+    b = np.stack(parts, axis=-1).reshape(p.shape[:-1] + (-1,))[..., :n]
+    return np.ascontiguousarray(np.moveaxis(b, -1, axis))

@@ -7,7 +7,10 @@
   representable regime, and through linearity in each block scale;
 * the grouped forms against per-row brute force and their reduction to dense;
 * the quantiser against torch's conversion of the same fp32 quotients and
-  against its defining invariants.
+  against its defining invariants;
+* the power-of-two (UE8M0) factors against torch's log2/ceil, a hand-written
+  packing layout, and their reduction to the fp32 mode when a factor is
+  already a power of two.
 """
 
 from __future__ import annotations
@@ -392,3 +395,87 @@ def test_similarity_defect_definition():
     assert metrics.similarity_defect(x, x) == 0.0
     assert abs(metrics.similarity_defect(-x, x) - 2.0) < 1e-15
     assert metrics.similarity_defect(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# --------------------------------------------------------------------------
+# power-of-two (UE8M0) scale factors
+
+
+def test_ue8m0_round_up_closed_forms():
+    """The byte is the exponent of the smallest power of two >= s, plus 127;
+    checked against math.frexp-free closed forms and torch's log2/ceil."""
+    s = np.float32([1.0, 1.5, 0.75, 2.0 ** -20, 3 * 2.0 ** -20, 448.0, 0.5000001, 2.0 ** 100])
+    assert quant.ue8m0_round_up(s).tolist() == [127, 128, 127, 107, 109, 136, 127, 227]
+    rng = np.random.default_rng(8)
+    r = (rng.random(2000).astype(np.float32) + np.float32(1e-3)) * np.float32(2.0) ** rng.integers(-30, 30, 2000)
+    r = r.astype(np.float32)
+    want = torch.ceil(torch.log2(torch.from_numpy(r).double())).to(torch.int64).numpy() + 127
+    assert np.array_equal(quant.ue8m0_round_up(r).astype(np.int64), want)
+    assert quant.ue8m0_decode([127, 128, 100]).tolist() == [1.0, 2.0, 2.0 ** -27]
+
+
+def test_ue8m0_pack_layout_and_roundtrip():
+    """Group 4i + j lands in byte j of element i, along the K-group axis."""
+    b = np.array([[1], [2], [3], [4], [5]], np.uint8)  # [Kb=5, M=1], K-group-major
+    p = quant.pack_ue8m0(b, axis=0)
+    assert p.shape == (2, 1) and p.view(np.uint32).ravel().tolist() == [0x04030201, 0x05]
+    w = np.arange(12, dtype=np.uint8).reshape(2, 6)  # [Nb, Kb]
+    pw = quant.pack_ue8m0(w, axis=1)
+    assert pw.view(np.uint32).tolist() == [[0x03020100, 0x0504], [0x09080706, 0x0B0A]]
+    rng = np.random.default_rng(1)
+    for shape, axis in [((7, 33), 0), ((9, 13), 1), ((4, 4), 0)]:
+        x = rng.integers(0, 256, shape).astype(np.uint8)
+        assert np.array_equal(quant.unpack_ue8m0(quant.pack_ue8m0(x, axis), shape[axis], axis), x)
+
+
+def test_ue8m0_quantize_invariants():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 384)).astype(np.float32) * np.float32(3.0)
+    x[1, 0:128] = 0.0
+    q, e = quant.quantize_per_token_ue8m0(x)
+    assert e.shape == (3, 6) and e.dtype == np.uint8
+    s = quant.ue8m0_decode(e).T  # [M, Kb]
+    amax = np.maximum(np.abs(x.reshape(6, 3, 128)).max(axis=2), np.float32(1e-4))
+    s32 = (amax / np.float32(448)).astype(np.float32)
+    # the smallest power of two at or above the fp32 factor
+    assert (s >= s32).all() and (s / 2 < s32).all()
+    dq = e4m3.decode(q).reshape(6, 3, 128)
+    assert (np.abs(dq) <= 448).all()
+    # dividing by a power of two is exact, so the codes are torch's RNE of x * 2^-e
+    ref = (torch.from_numpy(x.reshape(6, 3, 128)) / torch.from_numpy(s)[:, :, None]).to(torch.float8_e4m3fn)
+    assert np.array_equal(q.reshape(6, 3, 128), ref.view(torch.uint8).numpy())
+    rec = dq * s[:, :, None]
+    tol = np.maximum(np.abs(x.reshape(6, 3, 128)) * 2.0 ** -4, 2.0 ** -10 * s[:, :, None])
+    assert (np.abs(rec - x.reshape(6, 3, 128)) <= tol).all()
+
+
+def test_ue8m0_equals_fp32_factors_when_already_a_power_of_two():
+    """A group whose amax / 448 is a power of two gets the same factor and
+    codes in both modes."""
+    rng = np.random.default_rng(6)
+    x = rng.uniform(-1, 1, (3, 256)).astype(np.float32)
+    for m, kb, k in [(0, 0, -3), (1, 1, 0), (2, 0, 4)]:
+        g = x[m, kb * 128:(kb + 1) * 128]
+        g[:] = g / np.abs(g).max() * np.float32(448 * 2.0 ** k)
+        g[5] = np.float32(448 * 2.0 ** k)
+    qf, sf = quant.quantize_per_token(x)
+    qe, e = quant.quantize_per_token_ue8m0(x)
+    for m, kb in [(0, 0), (1, 1), (2, 0)]:
+        assert quant.ue8m0_decode(e[kb, m]) == sf[kb, m]
+        assert np.array_equal(qf[m, kb * 128:(kb + 1) * 128], qe[m, kb * 128:(kb + 1) * 128])
+
+
+def test_ue8m0_per_block_tail_and_gemm_definition():
+    """Per-block factors of a short tail block use its own amax; a GEMM on
+    decoded UE8M0 factors is the same definition as with fp32 factors."""
+    A, B = synth.dense_problem(16, 200, 256, seed=7)
+    qb, eb = quant.quantize_per_block_ue8m0(B.numpy())
+    assert eb.shape == (2, 2)
+    qt, et = quant.quantize_per_block_ue8m0(B.numpy()[128:])
+    assert np.array_equal(eb[1], et[0]) and np.array_equal(qb[128:], qt)
+    qa, ea = quant.quantize_per_token_ue8m0(A.numpy())
+    X = gemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb))
+    # brute force in fp64 from the decoded operands
+    a = e4m3.decode(qa) * np.repeat(quant.ue8m0_decode(ea).T, 128, axis=1)
+    b = e4m3.decode(qb) * np.repeat(np.repeat(quant.ue8m0_decode(eb), 128, axis=0)[:200], 128, axis=1)
+    assert np.allclose(X, a @ b.T, rtol=1e-12, atol=1e-12)
