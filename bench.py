@@ -18,7 +18,8 @@ measured with rocprofv3 counters when the committed counter summary matches
 the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
 oracle timed on a bounded sample of output blocks of the same workload.
 ``other_configs`` adds per-shape figures for the small-M dense, contiguous
-and masked workloads (skip with --no-other-configs).
+and masked workloads, and for the dense M=4096 shapes with power-of-two
+(UE8M0) factors on the scaled MFMA (skip with --no-other-configs).
 """
 
 from __future__ import annotations
@@ -178,6 +179,28 @@ def other_configs():
         nbytes = M * K + N * K + 4 * (M * Kb + -(-N // 128) * Kb) + 2 * M * N
         out.append(shape_entry("dense_small_m", (M, N, K), ms, 2 * M * N * K, nbytes, "hbm"))
         del copies
+    # the dense M=4096 shapes with power-of-two (UE8M0) factors (GPU casts)
+    for (M, N, K) in synth.DENSE_M4096.shapes:
+        A32, B32 = synth.dense_problem(M, N, K, seed=0)
+        qa, sa = fg.fp8_cast_per_token_ue8m0(A32.cuda())
+        qb, sb = fg.fp8_cast_per_block_ue8m0(B32.cuda())
+        del A32, B32
+        D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            fg.gemm_fp8_nt_ue8m0(qa, sa, qb, sb, D)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fg.gemm_fp8_nt_ue8m0(qa, sa, qb, sb, D)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        Kb, Kb4 = K // 128, (K // 128 + 3) // 4
+        nbytes = M * K + N * K + 4 * (M * Kb4 + -(-N // 128) * Kb4) + 2 * M * N
+        out.append(shape_entry("dense_m4096_ue8m0", (M, N, K), float(np.median(ts)), 2 * M * N * K, nbytes, "mfma"))
+        del qa, qb, D
     G, rows, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
     A32, B32, idx = synth.contiguous_problem([rows] * G, N, K, seed=0)
     qa, sa = fg.fp8_cast_per_token(A32.cuda())

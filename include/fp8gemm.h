@@ -155,6 +155,48 @@ fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa,
 fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
                              int N, int K, void* stream);
 
+/*
+ * Power-of-two (UE8M0) scale factors.  The digest's layout section
+ * ("GEMM arayuzu ve yerlesim kisitlari") gives the newer architecture's
+ * factors as UE8M0 -- an unsigned exponent byte e, value 2^(e - 127) -- packed
+ * four to a 32-bit integer.  Same granularity as the fp32 factors; four
+ * consecutive K groups share an int32, K group 4i + j in byte j (least
+ * significant first).  Kb4 = ceil(Kb / 4).
+ *
+ * Dense GEMM  D = bf16( sum_kb 2^(sa - 127) 2^(sb - 127) (A_kb . B_kb^T) )
+ *   A   device [M, K] e4m3, row stride lda bytes (lda >= K, lda % 16 == 0), 16-byte aligned
+ *   sa  device int32 [Kb4][ld_sa], ld_sa >= M: byte kb % 4 of sa[kb / 4][m] is row m's factor
+ *       of K group kb
+ *   B   device [N, K] e4m3, row stride ldb bytes (ldb >= K, ldb % 16 == 0), 16-byte aligned
+ *   sb  device int32 [Nb][Kb4]: byte kb % 4 of sb[nb][kb / 4] is block (nb, kb)'s factor
+ *   D   device [M, N] bf16, row stride ldd elements
+ * The matrix cores apply the factors (gfx950's scaled FP8 MFMA) and add each
+ * 128-deep slice into fp32 accumulators; the output is the same definition
+ * as gemm_fp8_nt with factors 2^(e - 127).  Factor bytes 0 and 255 are not
+ * meaningful inputs (the casts below never write them).  K % 128 == 0,
+ * lda, ldb <= 4 MiB.  Allocates nothing; errors as for gemm_fp8_nt.
+ */
+fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
+                            const uint8_t* B, int64_t ldb, const int32_t* sb,
+                            uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
+
+/*
+ * Per-token (1 x 128) cast with power-of-two factors: as fp8_cast_per_token,
+ * but the fp32 factor max(amax, 1e-4f) / 448 is rounded up to the next power
+ * of two 2^(e - 127) (so no code saturates) and e is written as a byte:
+ *   sa  device int32 [Kb4][ld_sa], ld_sa >= M; byte kb % 4 of sa[kb / 4][m] is
+ *       written for every kb < Kb (bytes for K groups >= Kb are not written)
+ */
+fg_status fp8_cast_per_token_ue8m0(const float* x, int64_t ldx, uint8_t* q, int32_t* sa, int64_t ld_sa,
+                                   int M, int K, void* stream);
+
+/*
+ * Per-block (128 x 128) cast with power-of-two factors (rounding as above):
+ *   sb  device int32 [Nb][Kb4]; byte kb % 4 of sb[nb][kb / 4] is written for every kb < Kb
+ */
+fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int32_t* sb,
+                                   int N, int K, void* stream);
+
 /* Row alignment of each expert segment in the contiguous layout: 128. */
 int fg_get_mk_alignment_for_contiguous_layout(void);
 

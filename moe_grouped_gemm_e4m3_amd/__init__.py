@@ -32,6 +32,10 @@ __all__ = [
     "gemm_fp8_grouped_masked",
     "fp8_cast_per_token",
     "fp8_cast_per_block",
+    "gemm_fp8_nt_ue8m0",
+    "fp8_cast_per_token_ue8m0",
+    "fp8_cast_per_block_ue8m0",
+    "empty_activation_scales_ue8m0",
     "get_mk_alignment_for_contiguous_layout",
     "set_num_cus",
     "get_num_cus",
@@ -52,6 +56,9 @@ _SIGNATURES = {
     "gemm_fp8_grouped_masked": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
+    "gemm_fp8_nt_ue8m0": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
+    "fp8_cast_per_token_ue8m0": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
+    "fp8_cast_per_block_ue8m0": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "fg_get_mk_alignment_for_contiguous_layout": (_I, []),
     "fg_set_num_cus": (None, [_I]),
     "fg_get_num_cus": (_I, []),
@@ -247,6 +254,79 @@ def fp8_cast_per_block(w, q=None, sb=None, stream=None):
     if not (q.is_contiguous() and sb.is_contiguous()):
         raise ValueError("q and sb must be contiguous")
     _call("fp8_cast_per_block", _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
+    return q, sb
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_cuda:
+        raise TypeError(f"{name} must be an int32 CUDA tensor of packed UE8M0 factors")
+    return t
+
+
+def empty_activation_scales_ue8m0(rows: int, K: int, device="cuda") -> torch.Tensor:
+    """A [ceil(Kb/4), rows] view of a padded int32 buffer for packed UE8M0 activation factors."""
+    kb4 = (K // 128 + 3) // 4
+    return torch.empty(kb4, aligned_scale_ld(rows), dtype=torch.int32, device=device)[:, :rows]
+
+
+def gemm_fp8_nt_ue8m0(A, sa, B, sb, D, stream=None):
+    """D[M,N] = bf16(A . B^T) with packed power-of-two (UE8M0) factors:
+    sa int32 [ceil(Kb/4), M] view (row stride ld_sa), sb int32 [Nb, ceil(Kb/4)]."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _i32(sa, "sa"), _i32(sb, "sb")
+    if D.dtype != torch.bfloat16 or not D.is_cuda:
+        raise TypeError("D must be a bfloat16 CUDA tensor")
+    for t, n in ((A, "A"), (B, "B"), (sa, "sa"), (D, "D")):
+        _unit_inner(t, n)
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous [Nb, ceil(Kb/4)]")
+    M, K = A.shape
+    N = B.shape[0]
+    kb4 = (K // 128 + 3) // 4
+    if B.shape[1] != K or tuple(D.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)}")
+    if K and (tuple(sa.shape) != (kb4, M) or tuple(sb.shape) != ((N + 127) // 128, kb4)):
+        raise ValueError("factor shapes must be sa [ceil(Kb/4), M] and sb [Nb, ceil(Kb/4)]")
+    _call(
+        "gemm_fp8_nt_ue8m0",
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        _ptr(D), D.stride(0), M, N, K, _stream(stream),
+    )
+    return D
+
+
+def fp8_cast_per_token_ue8m0(x, q=None, sa=None, stream=None):
+    """1x128 cast with power-of-two factors -> (q uint8 [M, K], sa int32 [ceil(Kb/4), M] view)."""
+    x = _f32(x, "x")
+    _unit_inner(x, "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = empty_activation_scales_ue8m0(M, K, device=x.device)
+    q = _fp8(q, "q")
+    sa = _i32(sa, "sa")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _unit_inner(sa, "sa")
+    _call("fp8_cast_per_token_ue8m0", _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
+    return q, sa
+
+
+def fp8_cast_per_block_ue8m0(w, q=None, sb=None, stream=None):
+    """128x128 cast with power-of-two factors -> (q uint8 [N, K], sb int32 [Nb, ceil(Kb/4)])."""
+    w = _f32(w, "w")
+    _unit_inner(w, "w")
+    N, K = w.shape
+    if q is None:
+        q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
+    if sb is None:
+        sb = torch.empty((N + 127) // 128, (K // 128 + 3) // 4, dtype=torch.int32, device=w.device)
+    q = _fp8(q, "q")
+    sb = _i32(sb, "sb")
+    if not (q.is_contiguous() and sb.is_contiguous()):
+        raise ValueError("q and sb must be contiguous")
+    _call("fp8_cast_per_block_ue8m0", _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
     return q, sb
 
 

@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -17,7 +18,6 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp8gemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["fp8gemm.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code: the scalar fp32
@@ -27,11 +27,17 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA results in VGPRs: the promotion FMAs read them directly
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
+]
+
+# Sources and their own options.  The fp32-factor kernels keep MFMA results in
+# VGPRs (the promotion FMAs read them directly); the power-of-two-factor
+# kernel accumulates in the matrix core and is built without that option, so
+# its accumulators go to the accumulation registers.
+SOURCES = [
+    ("fp8gemm.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("ue8m0.hip", []),
 ]
 
 
@@ -42,19 +48,29 @@ def hipcc_path() -> str:
     return p
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
-    """Compile the library; returns the path of the built .so."""
-    out = out or LIB_PATH
-    tmp = out + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source to an object with its options, link the library;
+    returns the path of the built .so."""
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    hipcc = hipcc_path()
+    with tempfile.TemporaryDirectory(prefix="fp8gemm_build_") as objdir:
+        objs = []
+        for src, opts in SOURCES:
+            obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+            _run([hipcc, *HIPCC_FLAGS, *opts, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

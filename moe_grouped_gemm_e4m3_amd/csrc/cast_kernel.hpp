@@ -39,6 +39,17 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
 
 __device__ __forceinline__ float scale_of(float amax) { return fmaxf(amax, 1e-4f) / 448.0f; }
 
+// Power-of-two (UE8M0) factors, the digest's packed format for the newer
+// architecture (same section): the fp32 factor rounded up to a power of two
+// so that no code saturates, stored as its biased exponent (value
+// 2^(e - 127)).  s is a positive normal fp32 here, so the exponent field is
+// the floor of log2(s) and any set significand bit rounds it up.
+__device__ __forceinline__ uint32_t ue8m0_of(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return ((u >> 23) & 0xffu) + ((u & 0x7fffffu) != 0u ? 1u : 0u);
+}
+__device__ __forceinline__ float ue8m0_value(uint32_t e) { return __uint_as_float(e << 23); }
+
 __device__ __forceinline__ float absmax4(float4 v, float m) {
   return fmaxf(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))), m);
 }
@@ -48,8 +59,11 @@ __device__ __forceinline__ uint32_t encode4(float4 v, float s) {
 }
 
 // One 16-lane group per (row, 128-column group); each lane handles 8 floats.
+// UE8M0: sa is int32 [ceil(Kb/4)][ld_sa], the factor of K group kb of row m in
+// byte kb % 4 of element [kb / 4][m] (one byte store per group).
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void cast_per_token_kernel(const float* __restrict__ x, int64_t ldx,
-                                                             uint8_t* __restrict__ q, float* __restrict__ sa,
+                                                             uint8_t* __restrict__ q, void* __restrict__ sa,
                                                              int64_t ld_sa, int M, int K, int64_t total_lanes) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= total_lanes) return;  // total_lanes % 16 == 0: a group is all in or all out
@@ -64,19 +78,28 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const float* __rest
   float amax = absmax4(v1, absmax4(v0, 0.f));
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-  const float s = scale_of(amax);
+  const float s32 = scale_of(amax);
+  const uint32_t e = UE8M0 ? ue8m0_of(s32) : 0u;
+  const float s = UE8M0 ? ue8m0_value(e) : s32;
   uint2 out;
   out.x = encode4(v0, s);
   out.y = encode4(v1, s);
   *(uint2*)(q + (int64_t)m * K + kb * 128 + sub * 8) = out;
-  if (sub == 0) sa[(int64_t)kb * ld_sa + m] = s;
+  if (sub == 0) {
+    if (UE8M0)
+      ((uint8_t*)sa)[((int64_t)(kb >> 2) * ld_sa + m) * 4 + (kb & 3)] = (uint8_t)e;
+    else
+      ((float*)sa)[(int64_t)kb * ld_sa + m] = s;
+  }
 }
 
 // One workgroup per 128x128 block: 32 lanes cover a 128-float row, 8 rows per
 // pass, 16 passes; the block is kept in registers between the amax reduction
-// and the encode.
+// and the encode.  UE8M0: sb is int32 [Nb][ceil(Kb/4)], the factor of block
+// (nb, kb) in byte kb % 4 of element [nb][kb / 4].
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void cast_per_block_kernel(const float* __restrict__ w, int64_t ldw,
-                                                             uint8_t* __restrict__ q, float* __restrict__ sb,
+                                                             uint8_t* __restrict__ q, void* __restrict__ sb,
                                                              int N, int K) {
   __shared__ float red[4];
   const int Kb = K >> 7;
@@ -102,14 +125,21 @@ __global__ __launch_bounds__(256) void cast_per_block_kernel(const float* __rest
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = scale_of(amax);
+  const float s32 = scale_of(amax);
+  const uint32_t e = UE8M0 ? ue8m0_of(s32) : 0u;
+  const float s = UE8M0 ? ue8m0_value(e) : s32;
   uint8_t* qb = q + (int64_t)nb * 128 * K + kb * 128 + c * 4;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = r0 + 8 * i;
     if (r < rows) *(uint32_t*)(qb + (int64_t)r * K) = encode4(v[i], s);
   }
-  if (tid == 0) sb[(int64_t)nb * Kb + kb] = s;
+  if (tid == 0) {
+    if (UE8M0)
+      ((uint8_t*)sb)[((int64_t)nb * ((Kb + 3) >> 2) + (kb >> 2)) * 4 + (kb & 3)] = (uint8_t)e;
+    else
+      ((float*)sb)[(int64_t)nb * Kb + kb] = s;
+  }
 }
 
 }  // namespace fg

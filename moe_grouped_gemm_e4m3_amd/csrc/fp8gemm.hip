@@ -24,6 +24,7 @@
 #include "fp8gemm.h"
 #include "cast_kernel.hpp"
 #include "gemm_kernel.hpp"
+#include "ue8m0_launch.hpp"
 #include "skinny_kernel.hpp"
 
 #define FG_TRY(x)                    \
@@ -250,19 +251,21 @@ fg_status launch_stream_k(fg::GemmParams& p, hipStream_t stream, int grid, Works
 // overrides the choice (tuning and tests).
 constexpr int kTileCostCols = 16;
 
-int pick_bn(int64_t row_tiles, int N) {
+int pick_bn(int64_t row_tiles, int N, bool allow_256 = true) {
   const char* f = getenv("FG_FORCE_BN");
   if (f && *f) {
     const int v = atoi(f);
-    if (v == 256 || v == 224 || v == 160) return v;
+    if (v == 224 || v == 160 || (v == 256 && allow_256)) return v;
   }
   int cus = 0;
-  if (device_cus(&cus) != FG_OK) return 256;
+  if (device_cus(&cus) != FG_OK) return allow_256 ? 256 : 224;
   if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
   static const int widths[] = {256, 224, 160};
   int best = 256;
   int64_t best_cost = -1;
+  if (!allow_256) best = 224;
   for (int bn : widths) {
+    if (bn == 256 && !allow_256) continue;
     const int64_t tiles = row_tiles * ((N + bn - 1) / bn);
     const int64_t rounds = (tiles + cus - 1) / cus;
     const int64_t cost = rounds * (bn + kTileCostCols);
@@ -284,6 +287,26 @@ fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream
   if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
   p.num_tiles = (int)slots;
   return launch_big<C, L>(p, stream, what);
+}
+
+// Dense GEMM with power-of-two factors: the large kernel's tiles (widths as
+// pick_bn chooses them) on the scaled MFMA; the kernel is in ue8m0.hip.
+fg_status launch_ue8m0(fg::GemmParams& p, int bn, hipStream_t stream, const char* what) {
+  static int occ_cache[2] = {0, 0};
+  int& occ = occ_cache[bn == 160 ? 1 : 0];
+  if (occ == 0) occ = fg::ue8m0_occupancy(bn);
+  p.tiles_m = (p.rows + CfgBig::BM - 1) / CfgBig::BM;
+  p.tiles_n = (p.N + bn - 1) / bn;
+  const int64_t slots = (int64_t)p.tiles_m * p.tiles_n;
+  if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
+  p.num_tiles = (int)slots;
+  p.group_m = raster_band(p.K);
+  int64_t grid = 0;
+  FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
+  print_config(what, p, CfgBig::BM, bn, CfgBig::THREADS, grid, occ);
+  const hipError_t e = fg::ue8m0_launch(p, bn, grid, stream);
+  if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return FG_OK;
 }
 
 template <int L>
@@ -549,6 +572,39 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
   return launch_gemm<C, fg::kMasked>(p, (hipStream_t)stream, "gemm_fp8_grouped_masked");
 }
 
+fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, int64_t ld_sa, const uint8_t* B,
+                            int64_t ldb, const int32_t* sb, uint16_t* D, int64_t ldd, int M, int N, int K,
+                            void* stream) {
+  g_err.clear();
+  if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M == 0 || N == 0) return FG_OK;
+  if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
+  FG_TRY(check_ptr(D, 2, "D"));
+  FG_TRY(check_ld(ldd, N, 1, "ldd"));
+  fg::GemmParams p{};
+  p.A = A; p.lda = lda; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb;
+  p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = ldd;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  if (K == 0) {  // no factors are read: the plain kernel writes the zeros
+    using C = CfgDefault;
+    p.tiles_m = (M + C::BM - 1) / C::BM;
+    p.tiles_n = (N + C::BN - 1) / C::BN;
+    p.num_tiles = p.tiles_m * p.tiles_n;
+    return launch_gemm<C, fg::kDense>(p, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+  }
+  FG_TRY(check_ptr(A, 16, "A"));
+  FG_TRY(check_ptr(B, 16, "B"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(lda, K, 16, "lda"));
+  FG_TRY(check_ld(ldb, K, 16, "ldb"));
+  FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+  FG_TRY(check_row_bytes(lda, ldb));
+  const int64_t row_tiles = (M + CfgBig::BM - 1) / CfgBig::BM;
+  return launch_ue8m0(p, pick_bn(row_tiles, N, false), (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+}
+
 fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa, int M, int K,
                              void* stream) {
   g_err.clear();
@@ -563,10 +619,50 @@ fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa,
   const int64_t lanes = (int64_t)M * (K / 128) * 16;
   const int64_t blocks = (lanes + 255) / 256;
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
-  hipLaunchKernelGGL(fg::cast_per_token_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, ldx, q,
+  hipLaunchKernelGGL(fg::cast_per_token_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, ldx, q,
                      sa, ld_sa, M, K, lanes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_token launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+fg_status fp8_cast_per_token_ue8m0(const float* x, int64_t ldx, uint8_t* q, int32_t* sa, int64_t ld_sa, int M, int K,
+                                   void* stream) {
+  g_err.clear();
+  if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(x, 16, "x"));
+  FG_TRY(check_ptr(q, 8, "q"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ld(ldx, K, 4, "ldx"));
+  FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+  const int64_t lanes = (int64_t)M * (K / 128) * 16;
+  const int64_t blocks = (lanes + 255) / 256;
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL(fg::cast_per_token_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x,
+                     ldx, q, (void*)sa, ld_sa, M, K, lanes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_token_ue8m0 launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int32_t* sb, int N, int K,
+                                   void* stream) {
+  g_err.clear();
+  if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (N == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(w, 16, "w"));
+  FG_TRY(check_ptr(q, 4, "q"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(ldw, K, 4, "ldw"));
+  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL(fg::cast_per_block_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
+                     ldw, q, (void*)sb, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block_ue8m0 launch: %s", hipGetErrorString(e));
   return FG_OK;
 }
 
@@ -581,7 +677,7 @@ fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
   const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
-  hipLaunchKernelGGL(fg::cast_per_block_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
+  hipLaunchKernelGGL(fg::cast_per_block_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
                      sb, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block launch: %s", hipGetErrorString(e));

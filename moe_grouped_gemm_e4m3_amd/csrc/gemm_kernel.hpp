@@ -514,9 +514,11 @@ __device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& i
   }
 }
 
+// sa_k: the row of the activation-factor array that holds slice kb's factors
+// (kb itself for fp32 factors; kb / 4 for packed power-of-two factors).
 template <class C>
 __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Work& t, int kb, uint8_t* stage,
-                                                  uint8_t* sa_area, int wave, int lane) {
+                                                  uint8_t* sa_area, int wave, int lane, int sa_k = -1) {
   constexpr int BM = C::BM;
   constexpr int HALF = C::NWAVES / 2, LA = C::LOADS_A, LB = C::LOADS_B;
   const bool is_a = wave < HALF;  // wave-uniform: the first half of the waves loads A, the second B
@@ -544,7 +546,7 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
   if (is_a) {
     // sa[kb][m0 + 64 wave + lane] into the stage's scale area; rows past
     // rows_alloc read as 0 (their outputs are never stored)
-    const float* sbase = t.sa + (int64_t)kb * p.ld_sa + t.m0;
+    const float* sbase = t.sa + (int64_t)(sa_k < 0 ? kb : sa_k) * p.ld_sa + t.m0;
     const int sbytes = max(t.rows_alloc - t.m0, 0) * 4;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(sbase, sbytes),
                                              (__attribute__((address_space(3))) void*)(sa_area + wave * 256), 4,
@@ -846,6 +848,177 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 #undef FG_SA
 }
 
+
+// ===========================================================================
+// Power-of-two (UE8M0) factors on the scaled MFMA (dense).  The digest's
+// layout section gives the newer architecture's factors as UE8M0 bytes packed
+// four to an int32.  gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes such a
+// byte per lane for each operand (lane l: operand row l % 16, 32-wide K block
+// l / 16) and applies 2^(e - 127) inside the matrix core, so with one factor
+// per 128-deep slice every lane passes its row's byte and the MFMA can add
+// each slice straight into the fp32 accumulator: the per-slice promotion
+// (four VALU FMAs per MFMA with fp32 factors) disappears.  Tiles, loads and
+// epilogue are the large kernel's; the activation factors of a slice arrive
+// in the stage's scale area (the packed word of K groups 4i..4i+3 of each
+// row), the weight factors through the scalar cache.
+//
+// Built for the 256x224 and 256x160 tiles only.  The accumulators are
+// updated in place in VGPRs; with a 256x256 tile's 128 of them plus the
+// operand fragments the register allocator falls back to copying every
+// MFMA result and spills (two waves per SIMD leave 256 registers a wave).
+// ===========================================================================
+
+// Factor bytes of the (at most two) 128-column weight blocks the wave's
+// columns touch, for slice kb: byte kb % 4 of element [nb][kb / 4].
+template <class C>
+__device__ __forceinline__ void load_sb_ue8m0(const GemmParams& p, const Work& t, int kb, int wn, int (&sb_r)[2]) {
+  const int Kb4 = (p.Kb + 3) >> 2;
+  const int nw = t.n0 + wn * C::WN;
+  const int nb0 = min(nw >> 7, p.Nb - 1);
+  const __attribute__((address_space(4))) int* sbk =
+      (const __attribute__((address_space(4))) int*)((const int*)(const void*)t.sb + (kb >> 2));
+  const int sh = 8 * (kb & 3);
+  sb_r[0] = (sbk[(int64_t)nb0 * Kb4] >> sh) & 0xff;
+  if (!C::SCALE_PER_WAVE) {
+    const int nb1 = min(nb0 + 1, p.Nb - 1);
+    sb_r[1] = (sbk[(int64_t)nb1 * Kb4] >> sh) & 0xff;
+  } else {
+    sb_r[1] = sb_r[0];
+  }
+}
+
+// One slice: acc += 2^(sa - 127) * 2^(sb - 127) * (A_slice . B_slice^T) per
+// 16x16 block, in the matrix core.  The weight fragment is the first operand
+// (its rows are the block's weight rows, one factor for all of them), the
+// activation fragment the second (lane l carries the factor of activation
+// row l % 16).
+template <class C>
+__device__ __forceinline__ void slice_mma_ue8m0(const uint8_t* st, const int (&a_off)[2], const int (&b_off)[2],
+                                                const uint8_t* sa_area, int wm, int l16, int kb, const int (&sb)[2],
+                                                int tb, f32x4 (&acc)[C::SM][C::SN]) {
+  constexpr int SM = C::SM, SN = C::SN;
+  const int sh = 8 * (kb & 3);
+  int sa[SM];
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms) sa[ms] = (*(const int*)(sa_area + (wm * C::WM + ms * 16 + l16) * 4) >> sh) & 0xff;
+  // fragments: all of A, B one subtile ahead; the fences keep the compiler
+  // from reading further ahead (registers: the 128 accumulators are updated
+  // in place only while the live fragments stay this few)
+  i32x8 af[SM];
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms) af[ms] = lds_frag(st, a_off[0] + ms * 2048, a_off[1] + ms * 2048);
+  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
+#pragma unroll
+  for (int tt = 0; tt < SN; ++tt) {
+    i32x8 bn = bf;
+    if (tt + 1 < SN) bn = lds_frag(st, b_off[0] + (tt + 1) * 2048, b_off[1] + (tt + 1) * 2048);
+    const int sbt = C::SCALE_PER_WAVE ? sb[0] : (tt < tb ? sb[0] : sb[1]);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms)
+      acc[ms][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], acc[ms][tt], 0, 0, 0, sbt, 0, sa[ms]);
+    __builtin_amdgcn_sched_barrier(0);
+    bf = bn;
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  constexpr int SM = C::SM, SN = C::SN;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
+#define FG_STAGE(i) (lds + (i) * C::STAGE)
+#define FG_SA(i) (lds + C::SA_OFF + (i) * 1024)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
+  const int l16 = lane & 15;
+  const int kq = lane >> 4;
+
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ra = wm * WM + l16;
+    const int rb = BM + wn * WN + l16;
+    a_off[h] = ra * 128 + (((2 * kq + h) ^ swz16(ra)) << 4);
+    b_off[h] = rb * 128 + (((2 * kq + h) ^ swz16(rb)) << 4);
+  }
+
+  const int grid = gridDim.x;
+  const int local = xcd_local_id(blockIdx.x, grid);
+  const int Kb = p.Kb;
+
+  Work cur;
+  int it = 0;
+  cur.w = -1;
+  if (!(local < p.num_tiles && resolve_big<kDense, BM, BN>(p, local, cur)))
+    advance_big<kDense, BM, BN>(p, cur, it, local, grid);
+  if (cur.w < 0) return;
+
+  int sb_c[2];
+  load_sb_ue8m0<C>(p, cur, 0, wn, sb_c);
+  issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[SM][SN];
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms)
+#pragma unroll
+    for (int tt = 0; tt < SN; ++tt) acc[ms][tt] = zero;
+
+  int stage = 0;
+  while (cur.w >= 0) {
+    Work nxt = cur;
+    int it_n = it;
+    advance_big<kDense, BM, BN>(p, nxt, it_n, local, grid);
+    const bool active = cur.m0 + wm * WM < cur.rows_valid;
+    const int tb = second_block_subtile<C>(cur, wn);
+
+    for (int kb = 0; kb < Kb; ++kb) {
+      const bool last = kb + 1 == Kb;
+      int sb_n[2] = {127, 127};
+      if (!last) {
+        load_sb_ue8m0<C>(p, cur, kb + 1, wn, sb_n);
+        issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, (kb + 1) >> 2);
+      } else if (nxt.w >= 0) {
+        load_sb_ue8m0<C>(p, nxt, 0, wn, sb_n);
+        issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, 0);
+      }
+      if (active) slice_mma_ue8m0<C>(FG_STAGE(stage), a_off, b_off, FG_SA(stage), wm, l16, kb, sb_c, tb, acc);
+
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      stage ^= 1;
+      sb_c[0] = sb_n[0];
+      sb_c[1] = sb_n[1];
+    }
+
+    float accf[SM][SN][4];
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms)
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accf[ms][tt][r] = acc[ms][tt][r];
+    store_tile<C, kDense>(p, cur, accf, FG_STAGE(stage ^ 1), wave, lane);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms)
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt) acc[ms][tt] = zero;
+    cur = nxt;
+    it = it_n;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+#undef FG_STAGE
+#undef FG_SA
+}
 
 // ===========================================================================
 // Stream-K variant of the large-tile kernel (dense).  When the tile count is

@@ -1,0 +1,181 @@
+"""Power-of-two (UE8M0) factors on the GPU against the CPU oracle: the two
+casts and the dense GEMM on the scaled MFMA.
+
+The casts must match the oracle byte for byte (codes and factor bytes).  The
+GEMM is compared bit for bit in the exact regime -- its factors {1/2, 1, 2}
+are powers of two already -- for both of its tile widths (FG_FORCE_BN), and within
+the oracle's per-element bound on random inputs.  Doubling one factor (its
+byte + 1) must double exactly the outputs it touches."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gemm as ogemm, quant
+from tests.helpers import (
+    SENTINEL_BF16, announce, assert_close, bf16_bits, bf16_to_f64, dev_u8, exact_regime, sentinel_like,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def dev_sa_packed(e: np.ndarray, pad: int = 4) -> torch.Tensor:
+    """UE8M0 bytes [Kb, M] -> a [ceil(Kb/4), M] view of a padded int32 buffer."""
+    p = quant.pack_ue8m0(e, axis=0)
+    kb4, M = p.shape
+    ld = max(4, (M + pad - 1) // pad * pad)
+    buf = np.full((kb4, ld), -1, np.int32)  # padding never read
+    buf[:, :M] = p
+    return dev_i32(buf)[:, :M]
+
+
+def to_bytes(s: np.ndarray) -> np.ndarray:
+    """Power-of-two fp32 factors -> UE8M0 bytes (exact)."""
+    e = quant.ue8m0_round_up(s)
+    assert np.array_equal(quant.ue8m0_decode(e), s)
+    return e
+
+
+def run(fg, qa, ea, qb, eb, out=None):
+    M, N = qa.shape[0], qb.shape[0]
+    D = out if out is not None else sentinel_like((M, N))
+    fg.gemm_fp8_nt_ue8m0(dev_u8(qa), dev_sa_packed(ea), dev_u8(qb), dev_i32(quant.pack_ue8m0(eb, axis=1)), D)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (37, 640), (256, 1536), (130, 512)])
+def test_cast_per_token_bytes(gpu_lib, M, K):
+    announce(f"ue8m0 cast per token {M}x{K}")
+    A32, _ = synth.dense_problem(M, 8, K, seed=M + K)
+    x = A32.numpy().copy()
+    x[0, :128] = 0.0  # an all-zero group
+    q_ref, e_ref = quant.quantize_per_token_ue8m0(x)
+    q, sa = gpu_lib.fp8_cast_per_token_ue8m0(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    got = quant.unpack_ue8m0(sa.cpu().numpy(), K // 128, axis=0)
+    assert np.array_equal(got, e_ref)
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (2112, 640), (300, 1024)])
+def test_cast_per_block_bytes(gpu_lib, N, K):
+    announce(f"ue8m0 cast per block {N}x{K}")
+    _, B32 = synth.dense_problem(1, N, K, seed=N + K)
+    q_ref, e_ref = quant.quantize_per_block_ue8m0(B32.numpy())
+    q, sb = gpu_lib.fp8_cast_per_block_ue8m0(B32.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(quant.unpack_ue8m0(sb.cpu().numpy(), K // 128, axis=1), e_ref)
+
+
+@pytest.fixture(params=[224, 160])
+def width(request, monkeypatch):
+    monkeypatch.setenv("FG_FORCE_BN", str(request.param))
+    return request.param
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (70, 300, 256), (256, 896, 512), (300, 1000, 640), (513, 2112, 256)])
+def test_gemm_exact_regime_bitwise(gpu_lib, width, M, N, K):
+    announce(f"ue8m0 gemm width {width} exact regime {M}x{N}x{K}")
+    rng = np.random.default_rng(M + N + K + width)
+    qa, sa, qb, sb = exact_regime(rng, M, N, K)
+    D = run(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb))
+    X = ogemm.gemm_nt(qa, sa, qb, sb)
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(X))
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 232, 256), (257, 1030, 1536), (512, 7168, 1024)])
+def test_gemm_random(gpu_lib, width, M, N, K):
+    announce(f"ue8m0 gemm width {width} random {M}x{N}x{K}")
+    A32, B32 = synth.dense_problem(M, N, K, seed=N + K)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quant.quantize_per_block_ue8m0(B32.numpy())
+    D = run(gpu_lib, qa, ea, qb, eb)
+    X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
+    assert_close(bf16_to_f64(D), X, S, K // 128, f"ue8m0 width {width} {M}x{N}x{K}")
+
+
+def test_gemm_factor_equivariance(gpu_lib, width):
+    """Raising one activation factor byte by one doubles that row exactly; one
+    weight block's bytes by one double its 128 columns exactly."""
+    M, N, K = 64, 640, 384
+    A32, B32 = synth.dense_problem(M, N, K, seed=41)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quant.quantize_per_block_ue8m0(B32.numpy())
+    announce(f"ue8m0 gemm width {width} equivariance")
+    base = bf16_to_f64(run(gpu_lib, qa, ea, qb, eb))
+    ea2 = ea.copy()
+    ea2[:, 5] += 1
+    y = bf16_to_f64(run(gpu_lib, qa, ea2, qb, eb))
+    assert np.array_equal(y[5], 2 * base[5])
+    assert np.array_equal(np.delete(y, 5, 0), np.delete(base, 5, 0))
+    for nb in range(N // 128):
+        eb2 = eb.copy()
+        eb2[nb, :] += 1
+        y = bf16_to_f64(run(gpu_lib, qa, ea, qb, eb2))
+        cols = slice(128 * nb, 128 * nb + 128)
+        assert np.array_equal(y[:, cols], 2 * base[:, cols]), nb
+        rest = np.ones(N, bool)
+        rest[cols] = False
+        assert np.array_equal(y[:, rest], base[:, rest]), nb
+
+
+def test_gemm_width_256_request_falls_back(gpu_lib, monkeypatch):
+    """This mode has no 256-wide tile; asking for one gives the 224-wide result."""
+    M, N, K = 300, 700, 384
+    rng = np.random.default_rng(7)
+    qa, sa, qb, sb = exact_regime(rng, M, N, K)
+    announce("ue8m0 gemm width 256 request")
+    monkeypatch.setenv("FG_FORCE_BN", "256")
+    D = run(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb))
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_nt(qa, sa, qb, sb)))
+
+
+def test_gemm_strided_output_and_tails(gpu_lib):
+    announce("ue8m0 gemm strided output")
+    M, N, K = 300, 200, 256
+    A32, B32 = synth.dense_problem(M, N, K, seed=43)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quant.quantize_per_block_ue8m0(B32.numpy())
+    Dbuf = sentinel_like((M + 3, N + 8))
+    run(gpu_lib, qa, ea, qb, eb, out=Dbuf[:M, :N])
+    X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
+    assert_close(bf16_to_f64(Dbuf[:M, :N]), X, S, K // 128, "ue8m0 strided")
+    bits = bf16_bits(Dbuf)
+    assert (bits[M:, :] == SENTINEL_BF16).all() and (bits[:, N:] == SENTINEL_BF16).all()
+
+
+@pytest.mark.parametrize("shape", synth.DENSE_M4096.shapes, ids=lambda s: "x".join(map(str, s)))
+def test_full_size_gpu_cast_sampled(gpu_lib, monkeypatch, shape):
+    """GPU casts + GEMM at the dense M=4096 sizes; sampled rows x column blocks
+    against the oracle on the same codes."""
+    monkeypatch.delenv("FG_FORCE_BN", raising=False)
+    M, N, K = shape
+    announce(f"ue8m0 full size {M}x{N}x{K}")
+    A32, B32 = synth.dense_problem(M, N, K, seed=0)
+    qa_d, sa_d = gpu_lib.fp8_cast_per_token_ue8m0(A32.cuda())
+    qb_d, sb_d = gpu_lib.fp8_cast_per_block_ue8m0(B32.cuda())
+    D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.gemm_fp8_nt_ue8m0(qa_d, sa_d, qb_d, sb_d, D)
+    torch.cuda.synchronize()
+    Kb = K // 128
+    ea = quant.unpack_ue8m0(sa_d.cpu().numpy(), Kb, axis=0)
+    eb = quant.unpack_ue8m0(sb_d.cpu().numpy(), Kb, axis=1)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False)]))
+    qa = qa_d[torch.from_numpy(rows).cuda()].cpu().numpy()
+    for nb in np.unique(np.concatenate([[0, -(-N // 128) - 1], rng.choice(N // 128, 2, replace=False)])):
+        cols = slice(nb * 128, min(N, nb * 128 + 128))
+        qb = qb_d[cols].cpu().numpy()
+        X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea[:, rows]), qb, quant.ue8m0_decode(eb[nb:nb + 1]),
+                             with_magnitude=True)
+        y = bf16_to_f64(D[torch.from_numpy(rows).cuda(), cols])
+        assert_close(y, X, S, Kb, f"ue8m0 full size block {nb}")
