@@ -156,6 +156,19 @@ fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
                              int N, int K, void* stream);
 
 /*
+ * The same two casts from BF16 inputs (raw bf16 bit patterns).  Each input
+ * is widened to fp32 exactly and then quantised as fp8_cast_per_token /
+ * fp8_cast_per_block quantise that fp32 value (same formula, same outputs).
+ *   x   device bf16 [M, K], row stride ldx elements (ldx >= K, ldx % 8 == 0), 16-byte aligned
+ *   w   device bf16 [N, K], row stride ldw elements (ldw >= K, ldw % 4 == 0), 16-byte aligned
+ * Other arguments, outputs and errors as for the fp32-input casts.
+ */
+fg_status fp8_cast_per_token_bf16(const uint16_t* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa,
+                                  int M, int K, void* stream);
+fg_status fp8_cast_per_block_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, float* sb,
+                                  int N, int K, void* stream);
+
+/*
  * Power-of-two (UE8M0) scale factors.  The digest's layout section
  * ("GEMM arayuzu ve yerlesim kisitlari") gives the newer architecture's
  * factors as UE8M0 -- an unsigned exponent byte e, value 2^(e - 127) -- packed

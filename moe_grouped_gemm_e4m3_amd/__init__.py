@@ -59,6 +59,8 @@ _SIGNATURES = {
     "gemm_fp8_nt_ue8m0": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
     "fp8_cast_per_token_ue8m0": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block_ue8m0": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
+    "fp8_cast_per_token_bf16": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
+    "fp8_cast_per_block_bf16": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "fg_get_mk_alignment_for_contiguous_layout": (_I, []),
     "fg_set_num_cus": (None, [_I]),
     "fg_get_num_cus": (_I, []),
@@ -224,9 +226,16 @@ def gemm_fp8_grouped_masked(A, sa, B, sb, masked_m, D, expected_m: int = 0, stre
     return D
 
 
+def _f32_or_bf16(t: torch.Tensor, name: str) -> tuple[torch.Tensor, str]:
+    """Cast input and the entry-point suffix for its dtype."""
+    if t.dtype == torch.bfloat16 and t.is_cuda:
+        return t, "_bf16"
+    return _f32(t, name), ""
+
+
 def fp8_cast_per_token(x, q=None, sa=None, stream=None):
-    """1x128 cast of fp32 activations [M, K] -> (q uint8 [M, K], sa fp32 [Kb, M] view)."""
-    x = _f32(x, "x")
+    """1x128 cast of fp32 or bf16 activations [M, K] -> (q uint8 [M, K], sa fp32 [Kb, M] view)."""
+    x, sfx = _f32_or_bf16(x, "x")
     _unit_inner(x, "x")
     M, K = x.shape
     if q is None:
@@ -237,13 +246,13 @@ def fp8_cast_per_token(x, q=None, sa=None, stream=None):
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     _unit_inner(sa, "sa")
-    _call("fp8_cast_per_token", _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
+    _call("fp8_cast_per_token" + sfx, _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
     return q, sa
 
 
 def fp8_cast_per_block(w, q=None, sb=None, stream=None):
-    """128x128 cast of fp32 weights [N, K] -> (q uint8 [N, K], sb fp32 [Nb, Kb])."""
-    w = _f32(w, "w")
+    """128x128 cast of fp32 or bf16 weights [N, K] -> (q uint8 [N, K], sb fp32 [Nb, Kb])."""
+    w, sfx = _f32_or_bf16(w, "w")
     _unit_inner(w, "w")
     N, K = w.shape
     if q is None:
@@ -253,7 +262,7 @@ def fp8_cast_per_block(w, q=None, sb=None, stream=None):
     q = _fp8(q, "q")
     if not (q.is_contiguous() and sb.is_contiguous()):
         raise ValueError("q and sb must be contiguous")
-    _call("fp8_cast_per_block", _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
+    _call("fp8_cast_per_block" + sfx, _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
     return q, sb
 
 

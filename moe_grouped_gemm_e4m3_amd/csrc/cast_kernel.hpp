@@ -58,11 +58,36 @@ __device__ __forceinline__ uint32_t encode4(float4 v, float s) {
   return e4m3_rne(v.x / s) | (e4m3_rne(v.y / s) << 8) | (e4m3_rne(v.z / s) << 16) | (e4m3_rne(v.w / s) << 24);
 }
 
-// One 16-lane group per (row, 128-column group); each lane handles 8 floats.
+// Inputs: fp32, or bf16 (raw bits, uint16_t) widened exactly to fp32 first
+// (the digest names BF16-input helpers beside the fp32 ones, "GEMM arayuzu
+// ve yerlesim kisitlari"), so a bf16 input quantises as its fp32 value does.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// 8 consecutive inputs (16-byte aligned) as two float4.
+__device__ __forceinline__ void load8(const float* src, float4& v0, float4& v1) {
+  v0 = *(const float4*)src;
+  v1 = *(const float4*)(src + 4);
+}
+__device__ __forceinline__ void load8(const uint16_t* src, float4& v0, float4& v1) {
+  const uint4 u = *(const uint4*)src;
+  v0 = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                   bf16_to_f32(u.y >> 16));
+  v1 = make_float4(bf16_to_f32(u.z & 0xffffu), bf16_to_f32(u.z >> 16), bf16_to_f32(u.w & 0xffffu),
+                   bf16_to_f32(u.w >> 16));
+}
+// 4 consecutive inputs (16-byte aligned for fp32, 8-byte for bf16).
+__device__ __forceinline__ float4 load4(const float* src) { return *(const float4*)src; }
+__device__ __forceinline__ float4 load4(const uint16_t* src) {
+  const uint2 u = *(const uint2*)src;
+  return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                     bf16_to_f32(u.y >> 16));
+}
+
+// One 16-lane group per (row, 128-column group); each lane handles 8 inputs.
 // UE8M0: sa is int32 [ceil(Kb/4)][ld_sa], the factor of K group kb of row m in
 // byte kb % 4 of element [kb / 4][m] (one byte store per group).
-template <bool UE8M0>
-__global__ __launch_bounds__(256) void cast_per_token_kernel(const float* __restrict__ x, int64_t ldx,
+template <bool UE8M0, typename T>
+__global__ __launch_bounds__(256) void cast_per_token_kernel(const T* __restrict__ x, int64_t ldx,
                                                              uint8_t* __restrict__ q, void* __restrict__ sa,
                                                              int64_t ld_sa, int M, int K, int64_t total_lanes) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -72,9 +97,8 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const float* __rest
   const int sub = (int)(gid & 15);
   const int m = (int)(grp / Kb);
   const int kb = (int)(grp - (int64_t)m * Kb);
-  const float* src = x + (int64_t)m * ldx + kb * 128 + sub * 8;
-  const float4 v0 = *(const float4*)src;
-  const float4 v1 = *(const float4*)(src + 4);
+  float4 v0, v1;
+  load8(x + (int64_t)m * ldx + kb * 128 + sub * 8, v0, v1);
   float amax = absmax4(v1, absmax4(v0, 0.f));
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
@@ -97,8 +121,8 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const float* __rest
 // pass, 16 passes; the block is kept in registers between the amax reduction
 // and the encode.  UE8M0: sb is int32 [Nb][ceil(Kb/4)], the factor of block
 // (nb, kb) in byte kb % 4 of element [nb][kb / 4].
-template <bool UE8M0>
-__global__ __launch_bounds__(256) void cast_per_block_kernel(const float* __restrict__ w, int64_t ldw,
+template <bool UE8M0, typename T>
+__global__ __launch_bounds__(256) void cast_per_block_kernel(const T* __restrict__ w, int64_t ldw,
                                                              uint8_t* __restrict__ q, void* __restrict__ sb,
                                                              int N, int K) {
   __shared__ float red[4];
@@ -109,14 +133,14 @@ __global__ __launch_bounds__(256) void cast_per_block_kernel(const float* __rest
   const int c = tid & 31;
   const int r0 = tid >> 5;
   const int rows = min(128, N - nb * 128);
-  const float* base = w + (int64_t)nb * 128 * ldw + kb * 128 + c * 4;
+  const T* base = w + (int64_t)nb * 128 * ldw + kb * 128 + c * 4;
   float4 v[16];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = r0 + 8 * i;
     if (r < rows) {
-      v[i] = *(const float4*)(base + (int64_t)r * ldw);
+      v[i] = load4(base + (int64_t)r * ldw);
       amax = absmax4(v[i], amax);
     }
   }

@@ -619,7 +619,7 @@ fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa,
   const int64_t lanes = (int64_t)M * (K / 128) * 16;
   const int64_t blocks = (lanes + 255) / 256;
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
-  hipLaunchKernelGGL(fg::cast_per_token_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, ldx, q,
+  hipLaunchKernelGGL((fg::cast_per_token_kernel<false, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, ldx, q,
                      sa, ld_sa, M, K, lanes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_token launch: %s", hipGetErrorString(e));
@@ -640,7 +640,7 @@ fg_status fp8_cast_per_token_ue8m0(const float* x, int64_t ldx, uint8_t* q, int3
   const int64_t lanes = (int64_t)M * (K / 128) * 16;
   const int64_t blocks = (lanes + 255) / 256;
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
-  hipLaunchKernelGGL(fg::cast_per_token_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x,
+  hipLaunchKernelGGL((fg::cast_per_token_kernel<true, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x,
                      ldx, q, (void*)sa, ld_sa, M, K, lanes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_token_ue8m0 launch: %s", hipGetErrorString(e));
@@ -659,10 +659,50 @@ fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int3
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
   const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
-  hipLaunchKernelGGL(fg::cast_per_block_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
+  hipLaunchKernelGGL((fg::cast_per_block_kernel<true, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
                      ldw, q, (void*)sb, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block_ue8m0 launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+fg_status fp8_cast_per_token_bf16(const uint16_t* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa, int M, int K,
+                                  void* stream) {
+  g_err.clear();
+  if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(x, 16, "x"));
+  FG_TRY(check_ptr(q, 8, "q"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ld(ldx, K, 8, "ldx"));
+  FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+  const int64_t lanes = (int64_t)M * (K / 128) * 16;
+  const int64_t blocks = (lanes + 255) / 256;
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL((fg::cast_per_token_kernel<false, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, x, ldx, q, (void*)sa, ld_sa, M, K, lanes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_token_bf16 launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+fg_status fp8_cast_per_block_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, float* sb, int N, int K,
+                                  void* stream) {
+  g_err.clear();
+  if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (N == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(w, 16, "w"));
+  FG_TRY(check_ptr(q, 4, "q"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(ldw, K, 4, "ldw"));
+  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL((fg::cast_per_block_kernel<false, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, w, ldw, q, (void*)sb, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block_bf16 launch: %s", hipGetErrorString(e));
   return FG_OK;
 }
 
@@ -677,7 +717,7 @@ fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
   const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
-  hipLaunchKernelGGL(fg::cast_per_block_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
+  hipLaunchKernelGGL((fg::cast_per_block_kernel<false, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
                      sb, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block launch: %s", hipGetErrorString(e));

@@ -110,3 +110,10 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     """Value of bf16 bit patterns as float64."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> float32, exactly (the 16 bits are the upper half
+    of the fp32 pattern).  The casts take bf16 inputs through this widening."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)

@@ -479,3 +479,13 @@ def test_ue8m0_per_block_tail_and_gemm_definition():
     a = e4m3.decode(qa) * np.repeat(quant.ue8m0_decode(ea).T, 128, axis=1)
     b = e4m3.decode(qb) * np.repeat(np.repeat(quant.ue8m0_decode(eb), 128, axis=0)[:200], 128, axis=1)
     assert np.allclose(X, a @ b.T, rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_widening_matches_torch():
+    """bf16 -> fp32 is exact: every pattern against torch's conversion."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = e4m3.bf16_bits_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    assert np.isnan(got[~np.isfinite(ref) & np.isnan(ref)]).all()

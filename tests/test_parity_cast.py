@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from oracle import gemm as ogemm, quant
+from oracle import e4m3, gemm as ogemm, quant
 from tests.helpers import announce, assert_close, bf16_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -83,3 +83,53 @@ def test_cast_then_gemm_end_to_end(gpu_lib):
     qb, sb = quant.quantize_per_block(B32.numpy())
     X, S = ogemm.gemm_nt(qa, sa, qb, sb, with_magnitude=True)
     assert_close(bf16_to_f64(D), X, S, K // 128, "end to end")
+
+
+# ------------------------------------------------------------- bf16 inputs
+
+
+def bf16_values(rng, shape) -> np.ndarray:
+    """bf16 bit patterns of special_values (rounded to bf16 by torch)."""
+    x = special_values(rng, shape)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (129, 7168), (257, 1024)])
+def test_per_token_bf16_input_bytes(gpu_lib, M, K):
+    """bf16 input quantises exactly as its fp32 widening does in the oracle."""
+    announce(f"cast per-token bf16 {M}x{K}")
+    bits = bf16_values(np.random.default_rng(M * 3 + K), (M, K))
+    q_ref, s_ref = quant.quantize_per_token(e4m3.bf16_bits_to_f32(bits))
+    q, sa = gpu_lib.fp8_cast_per_token(dev_bf16(bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (2112, 512), (300, 1024)])
+def test_per_block_bf16_input_bytes(gpu_lib, N, K):
+    announce(f"cast per-block bf16 {N}x{K}")
+    bits = bf16_values(np.random.default_rng(N + K), (N, K))
+    q_ref, s_ref = quant.quantize_per_block(e4m3.bf16_bits_to_f32(bits))
+    q, sb = gpu_lib.fp8_cast_per_block(dev_bf16(bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sb.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_bf16_input_strided_rows(gpu_lib):
+    """A bf16 view with a padded row stride (ldx > K)."""
+    M, K = 40, 256
+    bits = bf16_values(np.random.default_rng(5), (M, K))
+    buf = torch.zeros(M, K + 64, dtype=torch.bfloat16, device="cuda")
+    buf[:, :K] = dev_bf16(bits)
+    announce("cast per-token bf16 strided")
+    q, sa = gpu_lib.fp8_cast_per_token(buf[:, :K])
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.quantize_per_token(e4m3.bf16_bits_to_f32(bits))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
