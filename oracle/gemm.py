@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Operation (DeepGEMM digest, GeekNews topic 19459, "GEMM arayuzu ve yerlesim
 kisitlari"): the NT GEMM D = A @ B.T with A [M, K] row-major and B [N, K]
-(K-contiguous rows); the C addend of the pages is not part of this path.  The
+(K-contiguous rows), and D = C + A @ B.T with an fp32 addend C (the digest's
+naming convention for every GEMM kernel; ``gemm_nt_addend``).  The
 fp32 accumulation is "promoted" once per 128-wide K slice (GeekNews topic
 19444, opening bullets; 7minutos.es, "Detalles y beneficios tecnicos"):
 
@@ -100,6 +101,19 @@ def gemm_dequant(A, sa, B, sb):
 def gemm_nt(A, sa, B, sb, with_magnitude: bool = False):
     """Dense NT GEMM: float64 X (and S).  Use ``to_bf16`` for the D bits."""
     return gemm_blockwise(A, sa, B, sb, with_magnitude=with_magnitude)
+
+
+def gemm_nt_addend(A, sa, B, sb, C, with_magnitude: bool = False):
+    """D = C + A @ B.T (GeekNews topic 19459, "GEMM arayuzu ve yerlesim
+    kisitlari": the kernels are named after D = C + A @ B).  Reading where the
+    pages are silent: C is float32 [M, N], added once to the exact product
+    before the single BF16 rounding of D; |C| joins the magnitude S."""
+    C = np.asarray(C, np.float32).astype(np.float64)
+    X, S = gemm_blockwise(A, sa, B, sb, with_magnitude=True)
+    if C.shape != X.shape:
+        raise ValueError(f"C has shape {C.shape}, expected {X.shape}")
+    X = X + C
+    return (X, S + np.abs(C)) if with_magnitude else X
 
 
 def to_bf16(X) -> np.ndarray:

@@ -223,6 +223,37 @@ def test_gemm_matches_exact_rational_bruteforce(M, N, K):
         assert abs(Fraction(float(S[m, n])) - Se[m, n]) <= Fraction(2) ** -50 * Se[m, n]
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (3, 130, 256), (2, 5, 384)])
+def test_addend_matches_exact_rational_bruteforce(M, N, K):
+    """D = C + A @ B.T against Fraction sums; C holds values of every size,
+    including ones that cancel the product exactly."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    A, sa, B, sb = _random_problem(rng, M, N, K)
+    Xe, Se = _fraction_gemm(A, sa, B, sb)
+    C = (rng.standard_normal((M, N)) * 10.0 ** rng.integers(-3, 4, (M, N))).astype(np.float32)
+    C[0, 0] = np.float32(-float(Xe[0, 0]))  # cancellation: X = product - fp32(product)
+    X, S = gemm.gemm_nt_addend(A, sa, B, sb, C, with_magnitude=True)
+    for m, n in itertools.product(range(M), range(N)):
+        c = Fraction(float(C[m, n]))
+        assert abs(Fraction(float(X[m, n])) - (Xe[m, n] + c)) <= Fraction(2) ** -50 * (Se[m, n] + abs(c))
+        assert Fraction(float(S[m, n])) - (Se[m, n] + abs(c)) <= Fraction(2) ** -50 * (Se[m, n] + abs(c))
+
+
+def test_addend_bf16_rounds_the_sum_once():
+    """bf16(C + P) is not bf16(C) + bf16(P): with P = 1 and C = 2^-8 + 2^-16
+    the sum rounds up to 1 + 2^-7 while the separately rounded terms give 1."""
+    A = np.full((1, 128), 0x38, np.uint8)  # 1.0
+    B = np.zeros((1, 128), np.uint8)
+    B[0, 0] = 0x38
+    sa = np.ones((1, 1), np.float32)
+    sb = np.ones((1, 1), np.float32)
+    C = np.array([[2.0 ** -8 + 2.0 ** -16]], np.float32)
+    X = gemm.gemm_nt_addend(A, sa, B, sb, C)
+    assert X[0, 0] == 1 + 2.0 ** -8 + 2.0 ** -16
+    bits = int(gemm.to_bf16(X)[0, 0])
+    assert bits == 0x3F81  # 1 + 2^-7
+
+
 def test_two_oracle_forms_agree():
     rng = np.random.default_rng(7)
     A, sa, B, sb = _random_problem(rng, 48, 300, 640)
