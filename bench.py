@@ -19,7 +19,8 @@ the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
 oracle timed on a bounded sample of output blocks of the same workload.
 ``other_configs`` adds per-shape figures for the small-M dense, contiguous
 and masked workloads, and for the dense M=4096 shapes with power-of-two
-(UE8M0) factors on the scaled MFMA (skip with --no-other-configs).
+(UE8M0) factors on the scaled MFMA and with an fp32 addend (D = C + A B^T,
+timed beside the plain GEMM); skip them with --no-other-configs.
 """
 
 from __future__ import annotations
@@ -153,6 +154,23 @@ def graph_time(launch, launches: int = 20, reps: int = 5) -> float:
     return float(np.median(ts))
 
 
+def event_time(launch, reps: int = 10) -> float:
+    """Median GPU milliseconds of `launch()` over `reps` event-timed calls,
+    after three untimed ones."""
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
 def shape_entry(config, shape, ms, flops, nbytes, bound):
     tf = flops / ms / 1e9
     gbs = nbytes / ms / 1e6
@@ -186,21 +204,28 @@ def other_configs():
         qb, sb = fg.fp8_cast_per_block_ue8m0(B32.cuda())
         del A32, B32
         D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-        for _ in range(3):
-            fg.gemm_fp8_nt_ue8m0(qa, sa, qb, sb, D)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(10):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fg.gemm_fp8_nt_ue8m0(qa, sa, qb, sb, D)
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        Kb, Kb4 = K // 128, (K // 128 + 3) // 4
+        ms = event_time(lambda: fg.gemm_fp8_nt_ue8m0(qa, sa, qb, sb, D))
+        Kb4 = (K // 128 + 3) // 4
         nbytes = M * K + N * K + 4 * (M * Kb4 + -(-N // 128) * Kb4) + 2 * M * N
-        out.append(shape_entry("dense_m4096_ue8m0", (M, N, K), float(np.median(ts)), 2 * M * N * K, nbytes, "mfma"))
+        out.append(shape_entry("dense_m4096_ue8m0", (M, N, K), ms, 2 * M * N * K, nbytes, "mfma"))
         del qa, qb, D
+    # the dense M=4096 shapes with an fp32 addend, D = C + A B^T; the plain
+    # GEMM on the same operands is timed beside it
+    for (M, N, K) in synth.DENSE_M4096.shapes:
+        A32, B32 = synth.dense_problem(M, N, K, seed=0)
+        qa, sa = fg.fp8_cast_per_token(A32.cuda())
+        qb, sb = fg.fp8_cast_per_block(B32.cuda())
+        del A32, B32
+        C = torch.randn(M, N, generator=torch.Generator().manual_seed(1)).cuda()
+        D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ms = event_time(lambda: fg.gemm_fp8_nt_c(qa, sa, qb, sb, C, D))
+        plain = event_time(lambda: fg.gemm_fp8_nt(qa, sa, qb, sb, D))
+        Kb = K // 128
+        nbytes = M * K + N * K + 4 * (M * Kb + -(-N // 128) * Kb) + 4 * M * N + 2 * M * N
+        e = shape_entry("dense_m4096_addend", (M, N, K), ms, 2 * M * N * K, nbytes, "mfma")
+        e["plain_us"] = round(plain * 1e3, 2)
+        out.append(e)
+        del qa, qb, C, D
     G, rows, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
     A32, B32, idx = synth.contiguous_problem([rows] * G, N, K, seed=0)
     qa, sa = fg.fp8_cast_per_token(A32.cuda())

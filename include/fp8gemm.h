@@ -88,6 +88,22 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
                       uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
 
 /*
+ * Dense NT GEMM with an addend, D = C + A . B^T (the digest, "GEMM arayuzu ve
+ * yerlesim kisitlari": every GEMM kernel is named after D = C + A @ B, and
+ * fp8_gemm_nt computes D = C + A @ B.T).
+ *   C   device fp32 [M, N], row stride ldc elems   (ldc >= N, 4-byte aligned; rows that are
+ *       16-byte aligned get vector loads); read only, may not overlap D
+ *   every other argument as in gemm_fp8_nt.
+ * C is added to the fp32 accumulator once, after the last K slice, and the sum
+ * is rounded to BF16 once.  K == 0 writes D = bf16(C).  Same kernels, plans
+ * and workspace rules as gemm_fp8_nt, except that the optional stream-K path
+ * is never taken.  C == NULL is FG_EINVAL when M, N > 0.
+ */
+fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                        const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
+                        uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
+
+/*
  * M-grouped "contiguous" GEMM (digest, section "Dense ve Grouped GEMM": the
  * experts share N and K; every expert's rows are concatenated along M and each
  * expert segment is aligned to the GEMM M block, here 128 rows).

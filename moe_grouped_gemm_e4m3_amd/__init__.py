@@ -28,6 +28,7 @@ __all__ = [
     "load_library",
     "library_path",
     "gemm_fp8_nt",
+    "gemm_fp8_nt_c",
     "gemm_fp8_grouped_contiguous",
     "gemm_fp8_grouped_masked",
     "fp8_cast_per_token",
@@ -52,6 +53,7 @@ _I64 = ctypes.c_int64
 _I = ctypes.c_int
 _SIGNATURES = {
     "gemm_fp8_nt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
+    "gemm_fp8_nt_c": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P]),
     "gemm_fp8_grouped_contiguous": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gemm_fp8_grouped_masked": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
@@ -175,6 +177,28 @@ def gemm_fp8_nt(A, sa, B, sb, D, stream=None):
         "gemm_fp8_nt",
         _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
         _ptr(D), D.stride(0), M, N, K, _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_nt_c(A, sa, B, sb, C, D, stream=None):
+    """D[M,N] = bf16(C + A . B^T): gemm_fp8_nt with an fp32 addend C [M, N]."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb, C = _f32(sa, "sa"), _f32(sb, "sb"), _f32(C, "C")
+    if D.dtype != torch.bfloat16 or not D.is_cuda:
+        raise TypeError("D must be a bfloat16 CUDA tensor")
+    for t, n in ((A, "A"), (B, "B"), (sa, "sa"), (C, "C"), (D, "D")):
+        _unit_inner(t, n)
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous [Nb, Kb]")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(D.shape) != (M, N) or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)} D{tuple(D.shape)}")
+    _call(
+        "gemm_fp8_nt_c",
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, _stream(stream),
     )
     return D
 

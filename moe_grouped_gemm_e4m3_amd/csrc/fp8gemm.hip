@@ -384,7 +384,7 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
   return pl.cf > 0;
 }
 
-template <int MF, int CF>
+template <int MF, int CF, bool ADD_C>
 fg_status launch_skinny_cfg(fg::GemmParams& p, int splits, hipStream_t stream, const char* what) {
   using C = fg::SkinnyCfg<MF, CF>;
   const int64_t tiles = (p.N + C::COLS - 1) / C::COLS;
@@ -394,12 +394,13 @@ fg_status launch_skinny_cfg(fg::GemmParams& p, int splits, hipStream_t stream, c
   if (env_flag("FG_PRINT_CONFIGS"))
     fprintf(stderr, "[fp8gemm] %s M=%d N=%d K=%d skinny rows=%d cols=%d splits=%d grid=%lld\n", what, p.rows, p.N,
             p.K, C::ROWS, C::COLS, splits, (long long)grid);
-  hipLaunchKernelGGL((fg::gemm_fp8_skinny_kernel<C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p, splits);
+  hipLaunchKernelGGL((fg::gemm_fp8_skinny_kernel<C, ADD_C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p, splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
 }
 
+template <bool ADD_C>
 fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, hipStream_t stream, const char* what) {
   if (pl.splits > 1) {
     Workspace* ws = workspace(kWsSkinny, (void*)stream, kSkinnyPartialBytes, kSkinnyMaxTiles);
@@ -408,7 +409,7 @@ fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, hipStream_t str
     p.sk_flags = ws->flags;
   }
 #define FG_SKINNY_CASE(MF, CF) \
-  if (pl.mf == MF && pl.cf == CF) return launch_skinny_cfg<MF, CF>(p, pl.splits, stream, what);
+  if (pl.mf == MF && pl.cf == CF) return launch_skinny_cfg<MF, CF, ADD_C>(p, pl.splits, stream, what);
   FG_SKINNY_CASE(4, 1) FG_SKINNY_CASE(4, 2) FG_SKINNY_CASE(4, 4)
   FG_SKINNY_CASE(8, 1) FG_SKINNY_CASE(8, 2)
 #undef FG_SKINNY_CASE
@@ -437,13 +438,13 @@ fg_status check_row_bytes(int64_t lda, int64_t ldb) {
   return FG_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
-                      const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* stream) {
-  g_err.clear();
+// Validation and dispatch shared by D = A B^T (kDense) and D = C + A B^T
+// (kDenseC, C already checked and set in the parameters).
+template <int L>
+fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                   const uint8_t* B, int64_t ldb, const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K,
+                   void* stream, const char* what) {
   if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
   if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
   if (M == 0 || N == 0) return FG_OK;
@@ -460,7 +461,6 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
     FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
     FG_TRY(check_row_bytes(lda, ldb));
   }
-  fg::GemmParams p{};
   p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
   p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
   if (K > 0) {
@@ -473,7 +473,7 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
       const bool may_split = !stream_capturing(stream) ||
                              workspace(kWsSkinny, stream, kSkinnyPartialBytes, kSkinnyMaxTiles) != nullptr;
       if (plan_skinny(M, N, K, lda, ld_sa, all_cus, may_split, &pl))
-        return launch_skinny(p, pl, (hipStream_t)stream, "gemm_fp8_nt");
+        return launch_skinny<L == fg::kDenseC>(p, pl, (hipStream_t)stream, what);
     }
     using C = CfgBig;
     const int64_t tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
@@ -484,20 +484,44 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
       int cus = 0;
       FG_TRY(device_cus(&cus));
       if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
-      if (want_stream_k(tm * tn, p.Kb, cus)) {
+      if (L == fg::kDense && want_stream_k(tm * tn, p.Kb, cus)) {
         int all_cus = 0;
         FG_TRY(device_cus(&all_cus));
         Workspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
         if (ws) return launch_stream_k<C>(p, (hipStream_t)stream, cus, ws, "gemm_fp8_nt[stream-k]");
       }
-      return launch_big_width<fg::kDense>(p, 1, (hipStream_t)stream, "gemm_fp8_nt");
+      return launch_big_width<L>(p, 1, (hipStream_t)stream, what);
     }
   }
   using C = CfgDefault;
   p.tiles_m = (M + C::BM - 1) / C::BM;
   p.tiles_n = (N + C::BN - 1) / C::BN;
   p.num_tiles = p.tiles_m * p.tiles_n;
-  return launch_gemm<C, fg::kDense>(p, (hipStream_t)stream, "gemm_fp8_nt");
+  return launch_gemm<C, L>(p, (hipStream_t)stream, what);
+}
+}  // namespace
+
+extern "C" {
+
+fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                      const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* stream) {
+  g_err.clear();
+  fg::GemmParams p{};
+  return dense_nt<fg::kDense>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, "gemm_fp8_nt");
+}
+
+fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B,
+                        int64_t ldb, const float* sb, const float* C, int64_t ldc, uint16_t* D, int64_t ldd, int M,
+                        int N, int K, void* stream) {
+  g_err.clear();
+  if (M > 0 && N > 0) {
+    FG_TRY(check_ptr(C, 4, "C"));
+    FG_TRY(check_ld(ldc, N, 1, "ldc"));
+  }
+  fg::GemmParams p{};
+  p.Cin = C;
+  p.ldc = ldc;
+  return dense_nt<fg::kDenseC>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, "gemm_fp8_nt_c");
 }
 
 fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t ld_sa, const uint8_t* B,

@@ -36,7 +36,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum LayoutKind { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kDenseC is the dense GEMM with an fp32 addend, D = C + A B^T: it runs
+// exactly as kDense except that the epilogue adds C before the BF16 rounding.
+enum LayoutKind { kDense = 0, kContiguous = 1, kMasked = 2, kDenseC = 3 };
 
 struct GemmParams {
   const uint8_t* A;  // dense/contiguous: [rows, K] (lda); masked: [G, M_cap, K] packed
@@ -48,6 +50,8 @@ struct GemmParams {
   const float* sb;   // [Nb][Kb] or [G][Nb][Kb]
   uint16_t* D;       // [rows, N] (ldd) or [G, M_cap, N]
   int64_t ldd;       // elements
+  const float* Cin;  // kDenseC: fp32 addend [rows, N] (ldc floats)
+  int64_t ldc;
   const int32_t* m_indices;  // contiguous
   const int32_t* masked_m;   // masked
   int rows;     // dense: M; contiguous: M_total; masked: M_cap
@@ -85,6 +89,31 @@ __device__ __forceinline__ void raster(int w, int tiles_m, int tiles_n, int grou
   const int idx = w - band * band_size;
   tm = first + idx % rows;
   tn = idx / rows;
+}
+
+// D = C + A B^T: the fp32 addend at row m, columns n .. n+3 (zeros where
+// !valid and at columns >= N), added to the accumulator before the single BF16
+// rounding.  Callers issue every load of an epilogue pass before the first
+// use, so the pass waits for memory once.
+__device__ __forceinline__ f32x4 load_addend4(const GemmParams& p, int m, int n, bool valid) {
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const float* c = p.Cin + (int64_t)m * p.ldc + n;
+    if (n + 4 <= p.N && (p.ldc & 3) == 0 && ((uintptr_t)p.Cin & 15) == 0) {
+      x = *(const f32x4*)c;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < p.N) x[r] = c[r];
+    }
+  }
+  return x;
+}
+
+__device__ __forceinline__ void add_addend4(const GemmParams& p, int m, int n, float (&v)[4]) {
+  const f32x4 x = load_addend4(p, m, n, true);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] += x[r];
 }
 
 __device__ __forceinline__ int wave_max(int v) {
@@ -345,11 +374,19 @@ __global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
       }
       if (!ok) continue;
       uint16_t* drow = t.D + (int64_t)m * p.ldd;
+      f32x4 cv[SN];
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt)
+        cv[tt] = L == kDenseC ? load_addend4(p, m, n_base + 4 * tt, n_base + 4 * tt < p.N) : f32x4{0.f, 0.f, 0.f, 0.f};
       uint32_t pk[Q / 2];
 #pragma unroll
       for (int tt = 0; tt < SN; ++tt) {
-        pk[2 * tt] = pack_bf16x2(acc[ms][tt][0], acc[ms][tt][1]);
-        pk[2 * tt + 1] = pack_bf16x2(acc[ms][tt][2], acc[ms][tt][3]);
+        float v[4] = {acc[ms][tt][0], acc[ms][tt][1], acc[ms][tt][2], acc[ms][tt][3]};
+        if (L == kDenseC)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += cv[tt][r];
+        pk[2 * tt] = pack_bf16x2(v[0], v[1]);
+        pk[2 * tt + 1] = pack_bf16x2(v[2], v[3]);
       }
       if (vec && n_base + Q <= p.N) {
 #pragma unroll
@@ -688,6 +725,19 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
   const bool vec = (p.ldd & 7) == 0 && ((uintptr_t)p.D & 15) == 0;
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
+    // the addend of this pass's fragments, all loads in flight together
+    f32x4 cv[L == kDenseC ? G::MS_PER_PASS : 1][SN];
+    if (L == kDenseC) {
+#pragma unroll
+      for (int j = 0; j < G::MS_PER_PASS; ++j) {
+        const int m = t.m0 + wm * WM + (pass * G::MS_PER_PASS + j) * 16 + l16;
+#pragma unroll
+        for (int tt = 0; tt < SN; ++tt) {
+          const int n = t.n0 + wn * WN + tt * 16 + 4 * kq;
+          cv[j][tt] = load_addend4(p, m, n, m < t.rows_valid && n < p.N);
+        }
+      }
+    }
     // write this wave's fragment rows of the pass
 #pragma unroll
     for (int j = 0; j < G::MS_PER_PASS; ++j) {
@@ -698,8 +748,11 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
         const int byte = (wn * WN + tt * 16 + 4 * kq) * 2;
         const int c = byte >> 4;
         const int off = srow * ROWB + ((c ^ (srow & 15)) << 4) + (byte & 15);
-        *(uint2*)(stg + off) = make_uint2(pack_bf16x2(acc[ms][tt][0], acc[ms][tt][1]),
-                                          pack_bf16x2(acc[ms][tt][2], acc[ms][tt][3]));
+        float v[4] = {acc[ms][tt][0], acc[ms][tt][1], acc[ms][tt][2], acc[ms][tt][3]};
+        if (L == kDenseC)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += cv[j][tt][r];
+        *(uint2*)(stg + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
     lds_barrier();

@@ -123,12 +123,15 @@ __device__ __forceinline__ void skinny_compute(const SkinnySlice<C>& f, float (&
 }
 
 // Store 16x16 block g (lane: row 16i + l%16, columns 16j + 4(l/16) .. +3) as bf16.
-template <class C>
-__device__ __forceinline__ void skinny_store(const GemmParams& p, int n_tile0, int g, const float (&v)[4], int lane) {
+// With ADD_C the fp32 addend C is added first (D = C + A B^T).
+template <class C, bool ADD_C>
+__device__ __forceinline__ void skinny_store(const GemmParams& p, int n_tile0, int g, const float (&acc)[4], int lane) {
   const int i = g / C::CF, j = g % C::CF;
   const int m = 16 * i + (lane & 15);
   const int n = n_tile0 + 16 * j + 4 * (lane >> 4);
   if (m >= p.rows || n >= p.N) return;
+  float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+  if (ADD_C) add_addend4(p, m, n, v);
   uint16_t* dst = p.D + (int64_t)m * p.ldd + n;
   if (n + 4 <= p.N && (p.ldd & 3) == 0 && ((uintptr_t)p.D & 7) == 0) {
     *(uint2*)dst = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -141,7 +144,7 @@ __device__ __forceinline__ void skinny_store(const GemmParams& p, int n_tile0, i
 
 // Grid: (column tiles) x splits workgroups; workgroup b works on column tile
 // b / splits and K split b % splits.
-template <class C>
+template <class C, bool ADD_C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(GemmParams p, int splits) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   const int tid = threadIdx.x;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
 
   if (splits == 1) {
 #pragma unroll
-    for (int y = 0; y < C::GPW; ++y) skinny_store<C>(p, n0, wave * C::GPW + y, sum[y], lane);
+    for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, n0, wave * C::GPW + y, sum[y], lane);
     return;
   }
 
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
         t[r] = s == 0 ? u : t[r] + u;
       }
     }
-    skinny_store<C>(p, n0, x, t, lane);
+    skinny_store<C, ADD_C>(p, n0, x, t, lane);
   }
   // every workgroup of the tile has counted in: reset for the next launch
   if (tid == 0) __hip_atomic_store(p.sk_flags + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
