@@ -116,6 +116,26 @@ def gemm_nt_addend(A, sa, B, sb, C, with_magnitude: bool = False):
     return (X, S + np.abs(C)) if with_magnitude else X
 
 
+def gemm_layout(layout: str, A, sa, B, sb, C=None, with_magnitude: bool = False):
+    """The four storage layouts (GeekNews topic 19459, "Dense ve Grouped GEMM":
+    fp8_gemm_{nt, nn, tn, tt}).  Reading: the first letter says whether the
+    stored A is used as is ("n", A [M, K]) or transposed ("t", A stored
+    [K, M]); the second the same for B, where "t" is the NT form's B [N, K]
+    (D = A @ B.T) and "n" stores B as [K, N] (D = A @ B).  The scale factors
+    belong to the logical operands -- A as [M, K] with sa [Kb][M], B as
+    [N, K] with sb [Nb][Kb] -- whatever the storage.  A transpose of the
+    stored codes gives the NT operands; C is the optional fp32 addend."""
+    if layout not in ("nt", "nn", "tn", "tt"):
+        raise ValueError(f"layout {layout!r}")
+    A = np.asarray(A, np.uint8)
+    B = np.asarray(B, np.uint8)
+    a = A.T if layout[0] == "t" else A
+    b = B.T if layout[1] == "n" else B
+    if C is None:
+        return gemm_blockwise(a, sa, b, sb, with_magnitude=with_magnitude)
+    return gemm_nt_addend(a, sa, b, sb, C, with_magnitude=with_magnitude)
+
+
 def to_bf16(X) -> np.ndarray:
     """Expected BF16 output bits, D = bf16_RNE(X)."""
     return bf16_rne_bits(X)

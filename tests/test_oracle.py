@@ -254,6 +254,32 @@ def test_addend_bf16_rounds_the_sum_once():
     assert bits == 0x3F81  # 1 + 2^-7
 
 
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+def test_layouts_match_bruteforce_on_stored_arrays(layout):
+    """Each layout against Fraction sums that index the stored arrays directly
+    (A[k, m] when A is stored transposed, B[k, n] when B is stored [K, N])."""
+    M, N, K = 3, 5, 256
+    rng = np.random.default_rng(len(layout) + ord(layout[0]) * 3 + ord(layout[1]))
+    A, sa, B, sb = _random_problem(rng, M, N, K)
+    As = np.ascontiguousarray(A.T) if layout[0] == "t" else A
+    Bs = np.ascontiguousarray(B.T) if layout[1] == "n" else B
+    C = rng.standard_normal((M, N)).astype(np.float32)
+    X, S = gemm.gemm_layout(layout, As, sa, Bs, sb, C=C, with_magnitude=True)
+    da, db = torch_decode(As), torch_decode(Bs)
+    for m, n in itertools.product(range(M), range(N)):
+        terms = []
+        for k in range(K):
+            a = da[k, m] if layout[0] == "t" else da[m, k]
+            b = db[k, n] if layout[1] == "n" else db[n, k]
+            terms.append(Fraction(float(a)) * Fraction(float(sa[k // 128, m])) * Fraction(float(b))
+                         * Fraction(float(sb[n // 128, k // 128])))
+        c = Fraction(float(C[m, n]))
+        se = sum((abs(t) for t in terms), Fraction(0)) + abs(c)
+        assert abs(Fraction(float(X[m, n])) - (sum(terms, Fraction(0)) + c)) <= Fraction(2) ** -50 * se
+    X0 = gemm.gemm_layout(layout, As, sa, Bs, sb)
+    assert np.array_equal(X0, gemm.gemm_nt(A, sa, B, sb))
+
+
 def test_two_oracle_forms_agree():
     rng = np.random.default_rng(7)
     A, sa, B, sb = _random_problem(rng, 48, 300, 640)
