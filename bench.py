@@ -19,8 +19,9 @@ the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
 oracle timed on a bounded sample of output blocks of the same workload.
 ``other_configs`` adds per-shape figures for the small-M dense, contiguous
 and masked workloads, and for the dense M=4096 shapes with power-of-two
-(UE8M0) factors on the scaled MFMA and with an fp32 addend (D = C + A B^T,
-timed beside the plain GEMM); skip them with --no-other-configs.
+(UE8M0) factors on the scaled MFMA, with an fp32 addend (D = C + A B^T) and
+in the NN and TN storage layouts, each timed beside the plain GEMM; skip them
+with --no-other-configs.
 """
 
 from __future__ import annotations
@@ -225,6 +226,19 @@ def other_configs():
         e = shape_entry("dense_m4096_addend", (M, N, K), ms, 2 * M * N * K, nbytes, "mfma")
         e["plain_us"] = round(plain * 1e3, 2)
         out.append(e)
+        # the NN and TN storage layouts (transposes into the workspace + the
+        # NT GEMM); bytes count the operands once, as stored
+        for layout in ("nn", "tn"):
+            As = qa.t().contiguous() if layout[0] == "t" else qa
+            Bs = qb.t().contiguous() if layout[1] == "n" else qb
+            ws = torch.empty(fg.layout_workspace_bytes(layout, M, N, K), dtype=torch.uint8, device="cuda")
+            gemm = getattr(fg, "gemm_fp8_" + layout)
+            ms = event_time(lambda: gemm(As, sa, Bs, sb, D, workspace=ws))
+            nbytes = M * K + N * K + 4 * (M * Kb + -(-N // 128) * Kb) + 2 * M * N
+            e = shape_entry("dense_m4096_" + layout, (M, N, K), ms, 2 * M * N * K, nbytes, "mfma")
+            e["plain_us"] = round(plain * 1e3, 2)
+            out.append(e)
+            del As, Bs, ws
         del qa, qb, C, D
     G, rows, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
     A32, B32, idx = synth.contiguous_problem([rows] * G, N, K, seed=0)

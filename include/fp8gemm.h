@@ -104,6 +104,45 @@ fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t 
                         uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
 
 /*
+ * The other storage layouts (the digest's fp8_gemm_{nn, tn, tt}, section
+ * "Dense ve Grouped GEMM"; the same D = C + A @ B naming).  The first letter
+ * says whether the stored A is used as is (n: A [M, K]) or transposed (t: A
+ * stored [K, M]); the second the same for B, where t is the NT form's
+ * B [N, K] and n stores B as [K, N]:
+ *   gemm_fp8_nn   D = C + A . B      A [M, K] (lda bytes, as in gemm_fp8_nt), B [K, N] (ldb >= N bytes)
+ *   gemm_fp8_tn   D = C + A^T . B    A [K, M] (lda >= M bytes),                B [K, N] (ldb >= N bytes)
+ *   gemm_fp8_tt   D = C + A^T . B^T  A [K, M] (lda >= M bytes),                B [N, K] (as in gemm_fp8_nt)
+ * The scale factors belong to the logical operands, in the NT layouts: sa
+ * fp32 [Kb][ld_sa] (1x128 along K for each of the M rows), sb fp32 [Nb][Kb]
+ * (128x128 blocks of the [N, K] operand).  C: fp32 [M, N] addend (row stride
+ * ldc >= N) or NULL for none.  D: as in gemm_fp8_nt.  An operand stored MN-major
+ * has no alignment requirement.
+ * Each MN-major operand is first transposed, K-major, into the caller's
+ * device workspace (a byte copy bound by HBM), then the NT kernels run on the
+ * copy.  workspace must be 16-byte aligned and hold at least
+ * fg_layout_workspace_bytes(layout, M, N, K) bytes (FG_EINVAL otherwise); it is
+ * in use until the call's work on `stream` has finished.  Transposed rows must
+ * fit 4 MiB (K <= 2^22) and the stored [K, .] operands at most 65535*128 rows
+ * (FG_EUNSUPPORTED).  K % 128 == 0.  Nothing is allocated.
+ */
+fg_status gemm_fp8_nn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
+                      uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream);
+fg_status gemm_fp8_tn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
+                      uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream);
+fg_status gemm_fp8_tt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                      const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
+                      uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes that gemm_fp8_<layout> needs for (M, N, K); layout is one
+ * of "nt" (0), "nn", "tn", "tt".  -1 for an unknown layout or a negative size. */
+int64_t fg_layout_workspace_bytes(const char* layout, int M, int N, int K);
+
+/*
  * M-grouped "contiguous" GEMM (digest, section "Dense ve Grouped GEMM": the
  * experts share N and K; every expert's rows are concatenated along M and each
  * expert segment is aligned to the GEMM M block, here 128 rows).

@@ -29,6 +29,10 @@ __all__ = [
     "library_path",
     "gemm_fp8_nt",
     "gemm_fp8_nt_c",
+    "gemm_fp8_nn",
+    "gemm_fp8_tn",
+    "gemm_fp8_tt",
+    "layout_workspace_bytes",
     "gemm_fp8_grouped_contiguous",
     "gemm_fp8_grouped_masked",
     "fp8_cast_per_token",
@@ -54,6 +58,10 @@ _I = ctypes.c_int
 _SIGNATURES = {
     "gemm_fp8_nt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
     "gemm_fp8_nt_c": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P]),
+    "gemm_fp8_nn": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
+    "gemm_fp8_tn": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
+    "gemm_fp8_tt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
+    "fg_layout_workspace_bytes": (_I64, [ctypes.c_char_p, _I, _I, _I]),
     "gemm_fp8_grouped_contiguous": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gemm_fp8_grouped_masked": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
@@ -201,6 +209,62 @@ def gemm_fp8_nt_c(A, sa, B, sb, C, D, stream=None):
         _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, _stream(stream),
     )
     return D
+
+
+def layout_workspace_bytes(layout: str, M: int, N: int, K: int) -> int:
+    """Device workspace bytes gemm_fp8_<layout> needs (0 for "nt")."""
+    n = load_library().fg_layout_workspace_bytes(layout.encode(), M, N, K)
+    if n < 0:
+        raise ValueError(f"layout {layout!r} or sizes {(M, N, K)} not accepted")
+    return n
+
+
+def _gemm_layout(layout, A, sa, B, sb, D, C, stream, workspace):
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    if C is not None:
+        C = _f32(C, "C")
+    if D.dtype != torch.bfloat16 or not D.is_cuda:
+        raise TypeError("D must be a bfloat16 CUDA tensor")
+    for t, n in ((A, "A"), (B, "B"), (sa, "sa"), (C, "C"), (D, "D")):
+        if t is not None:
+            _unit_inner(t, n)
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous [Nb, Kb]")
+    K, M = A.shape if layout[0] == "t" else A.shape[::-1]
+    N = B.shape[1] if layout[1] == "n" else B.shape[0]
+    kb = B.shape[0] if layout[1] == "n" else B.shape[1]
+    if kb != K or tuple(D.shape) != (M, N) or (C is not None and tuple(C.shape) != (M, N)):
+        raise ValueError(f"{layout}: shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)}")
+    need = layout_workspace_bytes(layout, M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=D.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 CUDA tensor")
+    _call(
+        "gemm_fp8_" + layout,
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        _ptr(C), C.stride(0) if C is not None else 0, _ptr(D), D.stride(0), M, N, K,
+        _ptr(workspace), workspace.numel(), _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_nn(A, sa, B, sb, D, C=None, stream=None, workspace=None):
+    """D[M,N] = bf16(C + A . B), A [M, K], B stored [K, N].  Scales as for
+    gemm_fp8_nt (sb: 128x128 blocks of the logical [N, K] operand).  The
+    workspace (layout_workspace_bytes) comes from torch's allocator if not given."""
+    return _gemm_layout("nn", A, sa, B, sb, D, C, stream, workspace)
+
+
+def gemm_fp8_tn(A, sa, B, sb, D, C=None, stream=None, workspace=None):
+    """D[M,N] = bf16(C + A^T . B), A stored [K, M], B stored [K, N]."""
+    return _gemm_layout("tn", A, sa, B, sb, D, C, stream, workspace)
+
+
+def gemm_fp8_tt(A, sa, B, sb, D, C=None, stream=None, workspace=None):
+    """D[M,N] = bf16(C + A^T . B^T), A stored [K, M], B [N, K]."""
+    return _gemm_layout("tt", A, sa, B, sb, D, C, stream, workspace)
 
 
 def gemm_fp8_grouped_contiguous(A, sa, B, sb, m_indices, D, stream=None):

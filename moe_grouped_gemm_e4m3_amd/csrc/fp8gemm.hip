@@ -26,6 +26,7 @@
 #include "gemm_kernel.hpp"
 #include "ue8m0_launch.hpp"
 #include "skinny_kernel.hpp"
+#include "transpose_kernel.hpp"
 
 #define FG_TRY(x)                    \
   do {                               \
@@ -499,9 +500,115 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
   p.num_tiles = p.tiles_m * p.tiles_n;
   return launch_gemm<C, L>(p, (hipStream_t)stream, what);
 }
+// ---------------------------------------------------------------------------
+// Storage layouts NN / TN / TT: an operand stored MN-major ([K, M] or [K, N])
+// is transposed into the caller's workspace, K-major, and the NT kernels run
+// on the copy.  Workspace: the copy of A (M*K bytes) then the copy of B
+// (N*K bytes), each rounded up to 256 bytes.
+
+int64_t ws_round(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t layout_ws_bytes(bool ta, bool tb, int M, int N, int K) {
+  return (ta ? ws_round((int64_t)M * K) : 0) + (tb ? ws_round((int64_t)N * K) : 0);
+}
+
+// out [cols, rows] = in [rows, cols]^T, bytes.
+fg_status launch_transpose(const uint8_t* in, int64_t ld_in, uint8_t* out, int64_t ld_out, int rows, int cols,
+                           hipStream_t stream, const char* what) {
+  if (rows == 0 || cols == 0) return FG_OK;
+  const int64_t gx = (cols + fg::kTrTile - 1) / fg::kTrTile, gy = (rows + fg::kTrTile - 1) / fg::kTrTile;
+  if (gy > 65535) return fail(FG_EUNSUPPORTED, "%s: %d rows to transpose is above %d", what, rows, 65535 * 128);
+  if (env_flag("FG_PRINT_CONFIGS"))
+    fprintf(stderr, "[fp8gemm] %s transpose %dx%d grid=%lldx%lld\n", what, rows, cols, (long long)gx, (long long)gy);
+  hipLaunchKernelGGL(fg::transpose_u8_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, in, ld_in, out,
+                     ld_out, rows, cols);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "%s transpose launch: %s", what, hipGetErrorString(e));
+  return FG_OK;
+}
+
+template <bool TA, bool TB>
+fg_status gemm_layout(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                      const float* sb, const float* C, int64_t ldc, uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream, const char* what) {
+  g_err.clear();
+  if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M == 0 || N == 0) return FG_OK;
+  if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
+  if (C) FG_TRY(check_ptr(C, 4, "C"));
+  if (C) FG_TRY(check_ld(ldc, N, 1, "ldc"));
+  const uint8_t* a = A;
+  const uint8_t* b = B;
+  if (K > 0 && (TA || TB)) {
+    if (TA) {
+      FG_TRY(check_ptr(A, 1, "A"));
+      FG_TRY(check_ld(lda, M, 1, "lda"));
+    }
+    if (TB) {
+      FG_TRY(check_ptr(B, 1, "B"));
+      FG_TRY(check_ld(ldb, N, 1, "ldb"));
+    }
+    if (K > kMaxLd) return fail(FG_EUNSUPPORTED, "K=%d: transposed rows above 4 MiB", K);
+    const int64_t need = layout_ws_bytes(TA, TB, M, N, K);
+    if (workspace_bytes < need)
+      return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
+                  (long long)workspace_bytes, (long long)need);
+    FG_TRY(check_ptr(workspace, 16, "workspace"));
+    uint8_t* ws = (uint8_t*)workspace;
+    if (TA) {
+      FG_TRY(launch_transpose(A, lda, ws, K, K, M, (hipStream_t)stream, what));
+      a = ws;
+      lda = K;
+      ws += ws_round((int64_t)M * K);
+    }
+    if (TB) {
+      FG_TRY(launch_transpose(B, ldb, ws, K, K, N, (hipStream_t)stream, what));
+      b = ws;
+      ldb = K;
+    }
+  }
+  fg::GemmParams p{};
+  if (C) {
+    p.Cin = C;
+    p.ldc = ldc;
+    return dense_nt<fg::kDenseC>(p, a, lda, sa, ld_sa, b, ldb, sb, D, ldd, M, N, K, stream, what);
+  }
+  return dense_nt<fg::kDense>(p, a, lda, sa, ld_sa, b, ldb, sb, D, ldd, M, N, K, stream, what);
+}
 }  // namespace
 
 extern "C" {
+
+int64_t fg_layout_workspace_bytes(const char* layout, int M, int N, int K) {
+  if (!layout || M < 0 || N < 0 || K < 0) return -1;
+  if (strcmp(layout, "nt") == 0) return 0;
+  if (strcmp(layout, "nn") == 0) return layout_ws_bytes(false, true, M, N, K);
+  if (strcmp(layout, "tn") == 0) return layout_ws_bytes(true, true, M, N, K);
+  if (strcmp(layout, "tt") == 0) return layout_ws_bytes(true, false, M, N, K);
+  return -1;
+}
+
+fg_status gemm_fp8_nn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                      const float* sb, const float* C, int64_t ldc, uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_layout<false, true>(A, lda, sa, ld_sa, B, ldb, sb, C, ldc, D, ldd, M, N, K, workspace, workspace_bytes,
+                                  stream, "gemm_fp8_nn");
+}
+
+fg_status gemm_fp8_tn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                      const float* sb, const float* C, int64_t ldc, uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_layout<true, true>(A, lda, sa, ld_sa, B, ldb, sb, C, ldc, D, ldd, M, N, K, workspace, workspace_bytes,
+                                 stream, "gemm_fp8_tn");
+}
+
+fg_status gemm_fp8_tt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                      const float* sb, const float* C, int64_t ldc, uint16_t* D, int64_t ldd, int M, int N, int K,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_layout<true, false>(A, lda, sa, ld_sa, B, ldb, sb, C, ldc, D, ldd, M, N, K, workspace, workspace_bytes,
+                                  stream, "gemm_fp8_tt");
+}
 
 fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
                       const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* stream) {

@@ -1,0 +1,154 @@
+"""The NN, TN and TT storage layouts on the GPU against the CPU oracle.
+
+An operand stored MN-major is transposed into the workspace by a byte
+transpose and the NT kernels run on the copy, so a wrong byte anywhere in
+the transpose changes the GEMM result: in the exact regime (integer codes,
+power-of-two scales, an addend on a 1/4 grid) every layout is compared bit
+for bit, for the few-row, 128x128 and large-tile kernels, with ragged shapes
+that leave partial transpose tiles and with row strides that force the
+transpose's byte-wise paths."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gemm as ogemm
+from tests.helpers import (
+    SENTINEL_BF16, announce, assert_close, bf16_bits, bf16_to_f64, dev_f32, dev_sa, dev_u8, exact_regime,
+    quantize_dense, sentinel_like,
+)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["nn", "tn", "tt"]
+ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN", "FG_STREAM_K")
+
+
+@pytest.fixture(autouse=True)
+def default_plan(monkeypatch):
+    for k in ENV_KEYS:
+        monkeypatch.delenv(k, raising=False)
+
+
+def stored(layout, A, B):
+    """NT codes A [M, K], B [N, K] -> the arrays the layout stores."""
+    As = np.ascontiguousarray(A.T) if layout[0] == "t" else A
+    Bs = np.ascontiguousarray(B.T) if layout[1] == "n" else B
+    return As, Bs
+
+
+def dev_padded(a: np.ndarray, pad: int) -> torch.Tensor:
+    """A view of a wider device buffer (row stride = columns + pad); the padding
+    holds 0x7F (NaN) bytes that must never be read into the result."""
+    buf = torch.full((a.shape[0], a.shape[1] + pad), 0x7F, dtype=torch.uint8, device="cuda")
+    buf[:, : a.shape[1]] = dev_u8(a)
+    return buf[:, : a.shape[1]]
+
+
+def call(fg, layout, As, sa, Bs, sb, C=None, out=None, pad=(0, 0)):
+    M = sa.shape[1]
+    N = Bs.shape[1] if layout[1] == "n" else Bs.shape[0]
+    D = out if out is not None else sentinel_like((M, N))
+    Ad = dev_padded(As, pad[0]) if pad[0] else dev_u8(As)
+    Bd = dev_padded(Bs, pad[1]) if pad[1] else dev_u8(Bs)
+    getattr(fg, "gemm_fp8_" + layout)(Ad, dev_sa(sa), Bd, dev_f32(sb), D, C=None if C is None else dev_f32(C))
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (37, 200, 512), (128, 130, 256), (300, 1000, 640),
+                                   (513, 2112, 256), (1100, 1300, 384)])
+@pytest.mark.parametrize("with_c", [False, True], ids=["no-C", "C"])
+def test_exact_regime_bitwise(gpu_lib, layout, M, N, K, with_c):
+    announce(f"layout {layout} exact regime {M}x{N}x{K} C={with_c}")
+    rng = np.random.default_rng(M + 7 * N + K + len(layout))
+    A, sa, B, sb = exact_regime(rng, M, N, K)
+    As, Bs = stored(layout, A, B)
+    C = (rng.integers(-1024, 1025, (M, N)) / 4.0).astype(np.float32) if with_c else None
+    D = call(gpu_lib, layout, As, sa, Bs, sb, C)
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C)))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("pad", [(1, 3), (5, 16), (16, 7)])
+def test_strided_operands(gpu_lib, layout, pad):
+    """Row strides that are not multiples of 16 on the stored operands (byte-wise
+    transpose loads), NaN bytes in the padding, and an output view with a
+    sentinel border."""
+    M, N, K = 150, 290, 384
+    announce(f"layout {layout} strided pad={pad}")
+    rng = np.random.default_rng(sum(pad))
+    A, sa, B, sb = exact_regime(rng, M, N, K)
+    As, Bs = stored(layout, A, B)
+    # the K-major operand of nn / tt keeps the NT rule (stride a multiple of 16)
+    pa = pad[0] if layout[0] == "t" else 16
+    pb = pad[1] if layout[1] == "n" else 16
+    Dbuf = sentinel_like((M + 2, N + 5))
+    call(gpu_lib, layout, As, sa, Bs, sb, out=Dbuf[:M, :N], pad=(pa, pb))
+    assert np.array_equal(bf16_bits(Dbuf[:M, :N]), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb)))
+    bits = bf16_bits(Dbuf)
+    assert (bits[M:, :] == SENTINEL_BF16).all() and (bits[:, N:] == SENTINEL_BF16).all()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_random_inputs(gpu_lib, layout):
+    M, N, K = 257, 1030, 1024
+    announce(f"layout {layout} random {M}x{N}x{K}")
+    A32, B32 = synth.dense_problem(M, N, K, seed=23)
+    qa, sa, qb, sb = quantize_dense(A32, B32)
+    As, Bs = stored(layout, qa, qb)
+    C = np.random.default_rng(2).standard_normal((M, N)).astype(np.float32)
+    D = call(gpu_lib, layout, As, sa, Bs, sb, C)
+    X, S = ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C, with_magnitude=True)
+    assert_close(bf16_to_f64(D), X, S, K // 128 + 1, f"layout {layout} random")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_same_bits_as_nt(gpu_lib, layout):
+    """The layouts run the NT kernels on a transposed copy: same bits as NT."""
+    M, N, K = 64, 2112, 1024
+    announce(f"layout {layout} equals nt")
+    A32, B32 = synth.dense_problem(M, N, K, seed=29)
+    qa, sa, qb, sb = quantize_dense(A32, B32)
+    D0 = sentinel_like((M, N))
+    gpu_lib.gemm_fp8_nt(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), D0)
+    As, Bs = stored(layout, qa, qb)
+    D1 = call(gpu_lib, layout, As, sa, Bs, sb)
+    assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
+
+
+def test_workspace_too_small_is_rejected(gpu_lib):
+    M, N, K = 64, 256, 256
+    rng = np.random.default_rng(3)
+    A, sa, B, sb = exact_regime(rng, M, N, K)
+    As, Bs = stored("tn", A, B)
+    need = gpu_lib.layout_workspace_bytes("tn", M, N, K)
+    assert need == M * K + N * K
+    ws = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    D = sentinel_like((M, N))
+    with pytest.raises(gpu_lib.FP8GemmError, match="workspace"):
+        gpu_lib.gemm_fp8_tn(dev_u8(As), dev_sa(sa), dev_u8(Bs), dev_f32(sb), D, workspace=ws)
+    torch.cuda.synchronize()
+    assert (bf16_bits(D) == SENTINEL_BF16).all()
+
+
+def test_full_size_tn_sampled(gpu_lib):
+    """TN (both operands stored [K, .], the weight-gradient form) at the dense
+    4096 x 7168 x 2048 size; sampled rows x column blocks."""
+    M, N, K = synth.DENSE_M4096.shapes[4]
+    announce(f"layout tn full size {M}x{N}x{K}")
+    A32, B32 = synth.dense_problem(M, N, K, seed=0)
+    qa, sa, qb, sb = quantize_dense(A32, B32)
+    As, Bs = stored("tn", qa, qb)
+    D = call(gpu_lib, "tn", As, sa, Bs, sb)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False)]))
+    for nb in np.unique(np.concatenate([[0, N // 128 - 1], rng.choice(N // 128, 2, replace=False)])):
+        cols = slice(nb * 128, nb * 128 + 128)
+        X, S = ogemm.gemm_nt(qa[rows], sa[:, rows], qb[cols], sb[nb:nb + 1], with_magnitude=True)
+        y = bf16_to_f64(D[torch.from_numpy(rows).cuda(), cols])
+        assert_close(y, X, S, K // 128, f"tn full size block {nb}")
