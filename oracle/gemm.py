@@ -136,6 +136,44 @@ def gemm_layout(layout: str, A, sa, B, sb, C=None, with_magnitude: bool = False)
     return gemm_nt_addend(a, sa, b, sb, C, with_magnitude=with_magnitude)
 
 
+def gemm_k_grouped_tn(A, sa, B, sb, ks, C=None, with_magnitude: bool = False):
+    """K-grouped TN GEMM for MoE weight gradients (GeekNews topic 19459,
+    "Dense ve Grouped GEMM": grouped along K, M and N fixed,
+    k_grouped_fp8_gemm_tn_contiguous).  A is stored [K_total, M] and B
+    [K_total, N]; group g owns the ks[g] consecutive K rows starting at
+    sum(ks[:g]) and gives D[g] = C[g] + A_g^T @ B_g, [M, N].
+
+    Readings where the pages are silent: every ks[g] is a multiple of 128
+    (zero allowed: D[g] = C[g], or 0); the scale factors are those of the
+    dense form over the whole K range -- sa [Kb_total][M] (1x128 along K) and
+    sb [Nb][Kb_total] (128x128 blocks of the logical [N, K] operand) -- and
+    group g uses their K groups sum(ks[:g])/128 ..; C is an optional fp32
+    [G, M, N] addend."""
+    A = np.asarray(A, np.uint8)
+    B = np.asarray(B, np.uint8)
+    sa = np.asarray(sa, np.float32)
+    sb = np.asarray(sb, np.float32)
+    ks = [int(k) for k in ks]
+    if any(k < 0 or k % GROUP for k in ks) or sum(ks) != A.shape[0] or B.shape[0] != A.shape[0]:
+        raise ValueError(f"group sizes {ks} do not tile K_total = {A.shape[0]} in multiples of {GROUP}")
+    M, N = A.shape[1], B.shape[1]
+    G = len(ks)
+    X = np.zeros((G, M, N))
+    S = np.zeros((G, M, N))
+    k0 = 0
+    for g, k in enumerate(ks):
+        kb0, kb1 = k0 // GROUP, (k0 + k) // GROUP
+        if k:
+            X[g], S[g] = gemm_blockwise(A[k0:k0 + k].T, sa[kb0:kb1], B[k0:k0 + k].T, sb[:, kb0:kb1],
+                                        with_magnitude=True)
+        if C is not None:
+            c = np.asarray(C[g], np.float32).astype(np.float64)
+            X[g] += c
+            S[g] += np.abs(c)
+        k0 += k
+    return (X, S) if with_magnitude else X
+
+
 def to_bf16(X) -> np.ndarray:
     """Expected BF16 output bits, D = bf16_RNE(X)."""
     return bf16_rne_bits(X)

@@ -280,6 +280,35 @@ def test_layouts_match_bruteforce_on_stored_arrays(layout):
     assert np.array_equal(X0, gemm.gemm_nt(A, sa, B, sb))
 
 
+def test_k_grouped_tn_matches_bruteforce():
+    """Three groups along K, one of them empty, against Fraction sums over the
+    stored [K_total, .] arrays; the group's scale columns start at its first
+    K group."""
+    M, N, ks = 3, 130, [256, 0, 128]
+    Kt = sum(ks)
+    rng = np.random.default_rng(31)
+    A, sa, B, sb = _random_problem(rng, M, N, Kt)  # NT codes, scales over K_total
+    As, Bs = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    C = rng.standard_normal((len(ks), M, N)).astype(np.float32)
+    X, S = gemm.gemm_k_grouped_tn(As, sa, Bs, sb, ks, C=C, with_magnitude=True)
+    da, db = torch_decode(As), torch_decode(Bs)
+    k0 = 0
+    for g, kg in enumerate(ks):
+        for m, n in itertools.product(range(M), (0, 1, 127, 128, 129)):
+            terms = [Fraction(float(da[k, m])) * Fraction(float(sa[k // 128, m])) * Fraction(float(db[k, n]))
+                     * Fraction(float(sb[n // 128, k // 128])) for k in range(k0, k0 + kg)]
+            c = Fraction(float(C[g, m, n]))
+            se = sum((abs(t) for t in terms), Fraction(0)) + abs(c)
+            assert abs(Fraction(float(X[g, m, n])) - (sum(terms, Fraction(0)) + c)) <= Fraction(2) ** -50 * se
+            assert abs(Fraction(float(S[g, m, n])) - se) <= Fraction(2) ** -50 * se
+        k0 += kg
+    # one group is the dense TN layout
+    X1 = gemm.gemm_k_grouped_tn(As, sa, Bs, sb, [Kt])
+    assert np.array_equal(X1[0], gemm.gemm_layout("tn", As, sa, Bs, sb))
+    with pytest.raises(ValueError):
+        gemm.gemm_k_grouped_tn(As, sa, Bs, sb, [200, 184])
+
+
 def test_two_oracle_forms_agree():
     rng = np.random.default_rng(7)
     A, sa, B, sb = _random_problem(rng, 48, 300, 640)
