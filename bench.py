@@ -20,8 +20,8 @@ oracle timed on a bounded sample of output blocks of the same workload.
 ``other_configs`` adds per-shape figures for the small-M dense, contiguous
 and masked workloads, and for the dense M=4096 shapes with power-of-two
 (UE8M0) factors on the scaled MFMA, with an fp32 addend (D = C + A B^T) and
-in the NN and TN storage layouts, each timed beside the plain GEMM; skip them
-with --no-other-configs.
+in the NN and TN storage layouts, each timed beside the plain GEMM, and for
+the K-grouped TN GEMM of weight gradients; skip them with --no-other-configs.
 """
 
 from __future__ import annotations
@@ -240,6 +240,24 @@ def other_configs():
             out.append(e)
             del As, Bs, ws
         del qa, qb, C, D
+    # K-grouped TN (weight gradients of the contiguous workload: 8 experts x
+    # 4096 tokens, M = 4096, N = 7168); operands drawn on the GPU from a
+    # seeded generator and cast there
+    M, N, ks = 4096, 7168, [4096] * 8
+    Kt = sum(ks)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    qa, sa = fg.fp8_cast_per_token(torch.randn(M, Kt, device="cuda", generator=gen))
+    qb, sb = fg.fp8_cast_per_block(torch.randn(N, Kt, device="cuda", generator=gen))
+    As, Bs = qa.t().contiguous(), qb.t().contiguous()
+    del qa, qb
+    D = torch.empty(len(ks), M, N, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(fg.k_grouped_workspace_bytes(M, N, Kt), dtype=torch.uint8, device="cuda")
+    ms = event_time(lambda: fg.gemm_fp8_k_grouped_tn_contiguous(As, sa, Bs, sb, ks, D, workspace=ws), reps=5)
+    Kb = Kt // 128
+    nbytes = (M + N) * Kt + 4 * (M * Kb + -(-N // 128) * Kb) + 2 * len(ks) * M * N
+    e = shape_entry("k_grouped_tn_8x4096", (len(ks), M, N, ks[0]), ms, 2 * M * N * Kt, nbytes, "mfma")
+    out.append(e)
+    del As, Bs, D, ws
     G, rows, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
     A32, B32, idx = synth.contiguous_problem([rows] * G, N, K, seed=0)
     qa, sa = fg.fp8_cast_per_token(A32.cuda())

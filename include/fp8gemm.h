@@ -143,6 +143,34 @@ fg_status gemm_fp8_tt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
 int64_t fg_layout_workspace_bytes(const char* layout, int M, int N, int K);
 
 /*
+ * K-grouped TN GEMM for MoE weight gradients (the digest's
+ * k_grouped_fp8_gemm_tn_contiguous, section "Dense ve Grouped GEMM": grouped
+ * along K, M and N fixed).  Group g owns the ks[g] consecutive K rows that
+ * start at k_g = ks[0] + .. + ks[g-1] and computes
+ *     D[g] = C[g] + A_g^T . B_g          (A_g = A[k_g : k_g + ks[g], :], B_g likewise)
+ *   A   device [K_total, M] e4m3, row stride lda >= M bytes (K_total = sum of ks)
+ *   sa  device fp32 [K_total/128][ld_sa], ld_sa >= M: 1x128 factors along K per column m of A
+ *   B   device [K_total, N] e4m3, row stride ldb >= N bytes
+ *   sb  device fp32 [Nb][K_total/128]: 128x128 blocks of the logical [N, K] operand
+ *   ks  HOST int [G]; each a multiple of 128 (FG_EALIGN otherwise); 0 allowed (D[g] = C[g], or 0)
+ *   C   device fp32 [G, M, N] addend, contiguous, or NULL
+ *   D   device bf16 [G, M, N], contiguous; written
+ * Group g uses the factors of its own K groups (columns k_g/128 .. of sa
+ * and sb).  Both operands are transposed K-major into the caller's device
+ * workspace (16-byte aligned, at least fg_k_grouped_workspace_bytes(M, N,
+ * K_total) bytes; FG_EINVAL otherwise), then one NT GEMM per group runs on
+ * its K columns of the copies, all on `stream`.  K_total <= 2^22 and at most
+ * 65535*128 (FG_EUNSUPPORTED).  Nothing is allocated.
+ */
+fg_status gemm_fp8_k_grouped_tn_contiguous(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                           const uint8_t* B, int64_t ldb, const float* sb,
+                                           const int* ks, int G, const float* C, uint16_t* D, int M, int N,
+                                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of gemm_fp8_k_grouped_tn_contiguous; -1 for a negative size. */
+int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total);
+
+/*
  * M-grouped "contiguous" GEMM (digest, section "Dense ve Grouped GEMM": the
  * experts share N and K; every expert's rows are concatenated along M and each
  * expert segment is aligned to the GEMM M block, here 128 rows).

@@ -33,6 +33,8 @@ __all__ = [
     "gemm_fp8_tn",
     "gemm_fp8_tt",
     "layout_workspace_bytes",
+    "gemm_fp8_k_grouped_tn_contiguous",
+    "k_grouped_workspace_bytes",
     "gemm_fp8_grouped_contiguous",
     "gemm_fp8_grouped_masked",
     "fp8_cast_per_token",
@@ -62,6 +64,9 @@ _SIGNATURES = {
     "gemm_fp8_tn": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
     "gemm_fp8_tt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
     "fg_layout_workspace_bytes": (_I64, [ctypes.c_char_p, _I, _I, _I]),
+    "gemm_fp8_k_grouped_tn_contiguous": (
+        _I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I, _P, _P, _I, _I, _P, _I64, _P]),
+    "fg_k_grouped_workspace_bytes": (_I64, [_I, _I, _I64]),
     "gemm_fp8_grouped_contiguous": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gemm_fp8_grouped_masked": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
@@ -265,6 +270,55 @@ def gemm_fp8_tn(A, sa, B, sb, D, C=None, stream=None, workspace=None):
 def gemm_fp8_tt(A, sa, B, sb, D, C=None, stream=None, workspace=None):
     """D[M,N] = bf16(C + A^T . B^T), A stored [K, M], B [N, K]."""
     return _gemm_layout("tt", A, sa, B, sb, D, C, stream, workspace)
+
+
+def k_grouped_workspace_bytes(M: int, N: int, K_total: int) -> int:
+    """Device workspace bytes gemm_fp8_k_grouped_tn_contiguous needs."""
+    n = load_library().fg_k_grouped_workspace_bytes(M, N, K_total)
+    if n < 0:
+        raise ValueError(f"sizes {(M, N, K_total)} not accepted")
+    return n
+
+
+def gemm_fp8_k_grouped_tn_contiguous(A, sa, B, sb, ks, D, C=None, stream=None, workspace=None):
+    """D[g] = bf16(C[g] + A_g^T . B_g) for groups of ks[g] consecutive K rows.
+
+    A [K_total, M] and B [K_total, N] (uint8 / e4m3, row-contiguous); sa fp32
+    [K_total/128, M] view; sb fp32 [Nb, K_total/128]; ks: host sequence of
+    group sizes (multiples of 128); D bf16 [G, M, N] and C fp32 [G, M, N]
+    contiguous.  The workspace comes from torch's allocator if not given."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    if C is not None:
+        C = _f32(C, "C")
+        if not C.is_contiguous():
+            raise ValueError("C must be contiguous [G, M, N]")
+    if D.dtype != torch.bfloat16 or not D.is_cuda or not D.is_contiguous():
+        raise TypeError("D must be a contiguous bfloat16 CUDA tensor [G, M, N]")
+    for t, n in ((A, "A"), (B, "B"), (sa, "sa")):
+        _unit_inner(t, n)
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous [Nb, Kb_total]")
+    ks = [int(k) for k in ks]
+    G = len(ks)
+    K_total, M = A.shape
+    N = B.shape[1]
+    if B.shape[0] != K_total or sum(ks) != K_total or tuple(D.shape) != (G, M, N) or (
+            C is not None and tuple(C.shape) != (G, M, N)):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)} ks={ks}")
+    need = k_grouped_workspace_bytes(M, N, K_total)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=D.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 CUDA tensor")
+    ks_host = (ctypes.c_int * G)(*ks)
+    _call(
+        "gemm_fp8_k_grouped_tn_contiguous",
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        ctypes.cast(ks_host, ctypes.c_void_p), G, _ptr(C), _ptr(D), M, N,
+        _ptr(workspace), workspace.numel(), _stream(stream),
+    )
+    return D
 
 
 def gemm_fp8_grouped_contiguous(A, sa, B, sb, m_indices, D, stream=None):

@@ -464,6 +464,7 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
   }
   p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
   p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  if (p.ld_sb == 0) p.ld_sb = p.Kb;
   if (K > 0) {
     // few activation rows: the weight-streaming kernel
     const char* force = getenv("FG_FORCE_CONFIG");
@@ -610,6 +611,83 @@ fg_status gemm_fp8_tt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
                                   stream, "gemm_fp8_tt");
 }
 
+int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total) {
+  if (M < 0 || N < 0 || K_total < 0) return -1;
+  return ws_round((int64_t)M * K_total) + ws_round((int64_t)N * K_total);
+}
+
+fg_status gemm_fp8_k_grouped_tn_contiguous(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                                           const uint8_t* B, int64_t ldb, const float* sb, const int* ks, int G,
+                                           const float* C, uint16_t* D, int M, int N, void* workspace,
+                                           int64_t workspace_bytes, void* stream) {
+  const char* what = "gemm_fp8_k_grouped_tn_contiguous";
+  g_err.clear();
+  if (G <= 0) return fail(FG_EINVAL, "G=%d", G);
+  if (M < 0 || N < 0) return fail(FG_EINVAL, "negative size M=%d N=%d", M, N);
+  if (!ks) return fail(FG_EINVAL, "ks is NULL");
+  int64_t K_total = 0;
+  for (int g = 0; g < G; ++g) {
+    if (ks[g] < 0) return fail(FG_EINVAL, "ks[%d]=%d is negative", g, ks[g]);
+    if (ks[g] % 128) return fail(FG_EALIGN, "ks[%d]=%d is not a multiple of 128", g, ks[g]);
+    K_total += ks[g];
+  }
+  if (M == 0 || N == 0) return FG_OK;
+  if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
+  if (K_total > kMaxLd) return fail(FG_EUNSUPPORTED, "K_total=%lld: transposed rows above 4 MiB", (long long)K_total);
+  if ((int64_t)G * M * N >= ((int64_t)1 << 62) / 4) return fail(FG_EUNSUPPORTED, "output too large");
+  FG_TRY(check_ptr(D, 2, "D"));
+  if (C) FG_TRY(check_ptr(C, 4, "C"));
+  const int Kbt = (int)(K_total / 128);
+  const uint8_t* at = nullptr;
+  const uint8_t* bt = nullptr;
+  if (K_total > 0) {
+    FG_TRY(check_ptr(A, 1, "A"));
+    FG_TRY(check_ptr(B, 1, "B"));
+    FG_TRY(check_ptr(sa, 4, "sa"));
+    FG_TRY(check_ptr(sb, 4, "sb"));
+    FG_TRY(check_ld(lda, M, 1, "lda"));
+    FG_TRY(check_ld(ldb, N, 1, "ldb"));
+    FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+    const int64_t need = fg_k_grouped_workspace_bytes(M, N, K_total);
+    if (workspace_bytes < need)
+      return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
+                  (long long)workspace_bytes, (long long)need);
+    FG_TRY(check_ptr(workspace, 16, "workspace"));
+    uint8_t* ws = (uint8_t*)workspace;
+    FG_TRY(launch_transpose(A, lda, ws, K_total, (int)K_total, M, (hipStream_t)stream, what));
+    FG_TRY(launch_transpose(B, ldb, ws + ws_round((int64_t)M * K_total), K_total, (int)K_total, N,
+                            (hipStream_t)stream, what));
+    at = ws;
+    bt = ws + ws_round((int64_t)M * K_total);
+  }
+  // one dense NT GEMM per group on its K columns of the transposed copies;
+  // sb keeps its full row stride (Kb_total)
+  int64_t k0 = 0;
+  for (int g = 0; g < G; ++g) {
+    const int kg = ks[g];
+    const int64_t kb0 = k0 / 128;
+    fg::GemmParams p{};
+    p.ld_sb = Kbt > 0 ? Kbt : 1;
+    uint16_t* Dg = D + (int64_t)g * M * N;
+    const uint8_t* ag = at ? at + k0 : nullptr;
+    const uint8_t* bg = bt ? bt + k0 : nullptr;
+    const float* sag = kg ? sa + kb0 * ld_sa : sa;
+    const float* sbg = kg ? sb + kb0 : sb;
+    const int64_t ldt = K_total > 0 ? K_total : 16;
+    fg_status st;
+    if (C) {
+      p.Cin = C + (int64_t)g * M * N;
+      p.ldc = N;
+      st = dense_nt<fg::kDenseC>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, stream, what);
+    } else {
+      st = dense_nt<fg::kDense>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, stream, what);
+    }
+    if (st != FG_OK) return st;
+    k0 += kg;
+  }
+  return FG_OK;
+}
+
 fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
                       const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* stream) {
   g_err.clear();
@@ -654,7 +732,7 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
   p.m_indices = m_indices;
-  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K > 0) {
     // 256-row tiles: a tile whose halves hold different experts runs as two segments
     return launch_big_width<fg::kContiguous>(p, 1, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
@@ -690,7 +768,7 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
   p.masked_m = masked_m;
-  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K > 0) {
     return launch_big_width<fg::kMasked>(p, G, (hipStream_t)stream, "gemm_fp8_grouped_masked");
   }
@@ -716,7 +794,7 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   fg::GemmParams p{};
   p.A = A; p.lda = lda; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = ldd;
-  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros
     using C = CfgDefault;
     p.tiles_m = (M + C::BM - 1) / C::BM;

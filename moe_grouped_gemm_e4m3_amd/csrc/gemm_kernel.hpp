@@ -57,6 +57,7 @@ struct GemmParams {
   int rows;     // dense: M; contiguous: M_total; masked: M_cap
   int N, K, G;
   int Kb, Nb;
+  int ld_sb;             // row stride of sb in floats: Kb, or more when the K range is part of a wider sb
   int tiles_m, tiles_n;  // per group
   int num_tiles;         // tile slots walked by the persistent grid
   int group_m;           // raster band height in tiles
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) sa_row[ms] = min(t.m0 + a_row0 + ms * 16, t.rows_alloc - 1);
     const int nb_wave = min((t.n0 + wn * WN) >> 7, p.Nb - 1);
-    const float* sb_wave = t.sb + (int64_t)nb_wave * p.Kb;
+    const float* sb_wave = t.sb + (int64_t)nb_wave * p.ld_sb;
 
     float acc[SM][SN][4];
 #pragma unroll
@@ -600,10 +601,10 @@ __device__ __forceinline__ void load_sb(const GemmParams& p, const Work& t, int 
   const int nw = t.n0 + wn * C::WN;
   const int nb0 = min(nw >> 7, p.Nb - 1);
   const __attribute__((address_space(4))) float* sbk = (const __attribute__((address_space(4))) float*)(t.sb + kb);
-  sb_r[0] = sbk[(int64_t)nb0 * p.Kb];
+  sb_r[0] = sbk[(int64_t)nb0 * p.ld_sb];
   if (!C::SCALE_PER_WAVE) {
     const int nb1 = min(nb0 + 1, p.Nb - 1);
-    sb_r[1] = sbk[(int64_t)nb1 * p.Kb];
+    sb_r[1] = sbk[(int64_t)nb1 * p.ld_sb];
   } else {
     sb_r[1] = sb_r[0];
   }

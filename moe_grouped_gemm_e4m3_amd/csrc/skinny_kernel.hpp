@@ -169,7 +169,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   g.rsa = make_rsrc(p.sa, ((int64_t)(p.Kb - 1) * p.ld_sa + p.rows) * 4);
   g.sa_voff = l16 * 4;
   g.sa_kstep = (int)p.ld_sa * 4;
-  g.sb = p.sb + (int64_t)(n0 >> 7) * p.Kb;
+  g.sb = p.sb + (int64_t)(n0 >> 7) * p.ld_sb;
 
   float acc[C::GROUPS][4];
 #pragma unroll
