@@ -48,14 +48,14 @@ GROUP = 128
 def _check_dense(A, sa, B, sb):
     M, K = A.shape
     N, K2 = B.shape
-    if K != K2 or K % GROUP:
-        raise ValueError("A and B need the same K, a multiple of 128")
-    Kb = K // GROUP
+    if K != K2:
+        raise ValueError("A and B need the same K")
+    Kb = -(-K // GROUP)  # a last, partial K group when K % 128 != 0
     Nb = -(-N // GROUP)
     if sa.shape[0] != Kb or sa.shape[1] < M:
-        raise ValueError(f"sa must be [K/128, >=M], got {sa.shape}")
+        raise ValueError(f"sa must be [ceil(K/128), >=M], got {sa.shape}")
     if sb.shape != (Nb, Kb):
-        raise ValueError(f"sb must be [ceil(N/128), K/128], got {sb.shape}")
+        raise ValueError(f"sb must be [ceil(N/128), ceil(K/128)], got {sb.shape}")
     return M, N, K, Kb
 
 
@@ -75,7 +75,7 @@ def gemm_blockwise(A, sa, B, sb, with_magnitude: bool = False):
     X = np.zeros((M, N), dtype=np.float64)
     S = np.zeros((M, N), dtype=np.float64) if with_magnitude else None
     for kb in range(Kb):
-        ks = slice(kb * GROUP, (kb + 1) * GROUP)
+        ks = slice(kb * GROUP, min(K, (kb + 1) * GROUP))
         P = a[:, ks] @ b[:, ks].T  # exact slice partial
         scale = sa[kb, :M].astype(np.float64)[:, None] * sb[nblk, kb].astype(np.float64)[None, :]
         X += P * scale

@@ -38,48 +38,61 @@ def _encode_scaled(x: np.ndarray, s: np.ndarray) -> np.ndarray:
     return encode_rne(y)
 
 
+def _pad_k(x: np.ndarray) -> np.ndarray:
+    """Zero columns up to the next multiple of 128.  A partial last K group
+    (K % 128 != 0) is quantised on its own elements: zeros never raise an
+    amax, and the codes of the added columns are dropped again."""
+    K = x.shape[-1]
+    Kp = -(-K // GROUP) * GROUP
+    if Kp == K:
+        return x
+    out = np.zeros(x.shape[:-1] + (Kp,), np.float32)
+    out[..., :K] = x
+    return out
+
+
 def quantize_per_token(x) -> tuple[np.ndarray, np.ndarray]:
     """1x128 quantisation of activations.
 
-    x: float32 [M, K] with K % 128 == 0.
-    Returns (q uint8 [M, K], sa float32 [K/128, M]) -- the scales are returned
-    K-group-major ("transposed"), the layout the GEMM consumes.
+    x: float32 [M, K].  When K % 128 != 0 the last group holds the K % 128
+    remaining columns and its factor comes from their amax alone.
+    Returns (q uint8 [M, K], sa float32 [ceil(K/128), M]) -- the scales are
+    returned K-group-major ("transposed"), the layout the GEMM consumes.
     """
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
-    Kb = K // GROUP
-    xg = x.reshape(M, Kb, GROUP)
+    xp = _pad_k(x)
+    Kb = xp.shape[1] // GROUP
+    xg = xp.reshape(M, Kb, GROUP)
     amax = np.abs(xg).max(axis=2) if M else np.zeros((0, Kb), np.float32)
     s = _scale_from_amax(amax)  # [M, Kb]
-    q = _encode_scaled(xg, s[:, :, None]).reshape(M, K)
-    return q, np.ascontiguousarray(s.T)
+    q = _encode_scaled(xg, s[:, :, None]).reshape(M, Kb * GROUP)[:, :K]
+    return np.ascontiguousarray(q), np.ascontiguousarray(s.T)
 
 
 def quantize_per_block(w) -> tuple[np.ndarray, np.ndarray]:
     """128x128 quantisation of weights.
 
-    w: float32 [N, K] with K % 128 == 0; N is arbitrary (the last row block
-    covers N % 128 rows when N is not a multiple of 128).
-    Returns (q uint8 [N, K], sb float32 [ceil(N/128), K/128]).
+    w: float32 [N, K]; N is arbitrary (the last row block covers N % 128
+    rows when N is not a multiple of 128), and so is K (the last column block
+    covers K % 128 columns).
+    Returns (q uint8 [N, K], sb float32 [ceil(N/128), ceil(K/128)]).
     """
     w = np.asarray(w, dtype=np.float32)
     N, K = w.shape
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
-    Kb = K // GROUP
+    wp = _pad_k(w)
+    Kb = wp.shape[1] // GROUP
     Nb = -(-N // GROUP)
-    q = np.empty((N, K), dtype=np.uint8)
+    q = np.empty((N, Kb * GROUP), dtype=np.uint8)
     sb = np.empty((Nb, Kb), dtype=np.float32)
     for nb in range(Nb):
         rows = slice(nb * GROUP, min(N, (nb + 1) * GROUP))
-        blk = w[rows].reshape(-1, Kb, GROUP)  # [r, Kb, 128]
+        blk = wp[rows].reshape(-1, Kb, GROUP)  # [r, Kb, 128]
         amax = np.abs(blk).max(axis=(0, 2))  # [Kb]
         s = _scale_from_amax(amax)
         sb[nb] = s
-        q[rows] = _encode_scaled(blk, s[None, :, None]).reshape(-1, K)
-    return q, sb
+        q[rows] = _encode_scaled(blk, s[None, :, None]).reshape(-1, Kb * GROUP)
+    return np.ascontiguousarray(q[:, :K]), sb
 
 
 # ---------------------------------------------------------------------------

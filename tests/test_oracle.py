@@ -309,6 +309,48 @@ def test_k_grouped_tn_matches_bruteforce():
         gemm.gemm_k_grouped_tn(As, sa, Bs, sb, [200, 184])
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 3, 16), (3, 130, 176), (2, 5, 304)])
+def test_k_tail_gemm_matches_bruteforce(M, N, K):
+    """K % 128 != 0: the last K group is partial; Fraction sums over all K."""
+    rng = np.random.default_rng(K + M)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    Kb, Nb = -(-K // 128), -(-N // 128)
+    A = rng.choice(finite, (M, K))
+    B = rng.choice(finite, (N, K))
+    sa = np.exp(rng.uniform(-8, 8, (Kb, M))).astype(np.float32)
+    sb = np.exp(rng.uniform(-8, 8, (Nb, Kb))).astype(np.float32)
+    X, S = gemm.gemm_nt(A, sa, B, sb, with_magnitude=True)
+    Xe, Se = _fraction_gemm(A, sa, B, sb)
+    for m, n in itertools.product(range(M), range(N)):
+        assert abs(Fraction(float(X[m, n])) - Xe[m, n]) <= Fraction(2) ** -50 * Se[m, n]
+        assert abs(Fraction(float(S[m, n])) - Se[m, n]) <= Fraction(2) ** -50 * Se[m, n]
+    assert np.allclose(X, gemm.gemm_dequant(A, sa, B, sb), rtol=0, atol=1e-12 * S.max())
+
+
+def test_k_tail_quantisers_match_torch_on_their_own_columns():
+    """The partial last group's factor is max(amax, 1e-4)/448 over its own
+    columns, its codes torch's RNE of x / s; full groups are unaffected."""
+    A, B = synth.dense_problem(5, 130, 208, seed=4)
+    x, w = A.numpy(), B.numpy()
+    q, sa = quant.quantize_per_token(x)
+    assert q.shape == (5, 208) and sa.shape == (2, 5)
+    tail = torch.from_numpy(x[:, 128:])
+    s = torch.clamp(tail.abs().amax(dim=1), min=torch.tensor(1e-4, dtype=torch.float32)) / 448.0
+    assert np.array_equal(sa[1], s.numpy())
+    ref = (tail / s[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q[:, 128:], ref)
+    q0, sa0 = quant.quantize_per_token(x[:, :128])
+    assert np.array_equal(q[:, :128], q0) and np.array_equal(sa[:1], sa0)
+    qb, sb = quant.quantize_per_block(w)
+    assert qb.shape == (130, 208) and sb.shape == (2, 2)
+    for nb, rows in ((0, slice(0, 128)), (1, slice(128, 130))):
+        blk = torch.from_numpy(w[rows, 128:])
+        s = torch.clamp(blk.abs().amax(), min=torch.tensor(1e-4, dtype=torch.float32)) / 448.0
+        assert sb[nb, 1] == s.item()
+        ref = (blk / s).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(qb[rows, 128:], ref)
+
+
 def test_two_oracle_forms_agree():
     rng = np.random.default_rng(7)
     A, sa, B, sb = _random_problem(rng, 48, 300, 640)
