@@ -16,7 +16,13 @@
  *
  * Types.  FP8 operands are e4m3fn bytes (OCP: bias 7, max 448, NaN 0x7F/0xFF)
  * passed as uint8_t.  Scales are IEEE fp32.  BF16 results are uint16_t bit
- * patterns.  Kb = K/128, Nb = ceil(N/128).
+ * patterns.  Kb = ceil(K/128), Nb = ceil(N/128).
+ *
+ * K tails.  The digest leaves K % 128 != 0 open.  Reading taken here: K must
+ * be a multiple of 16 (the 16-byte row granularity of the operand loads); the
+ * last K group is then partial and holds the K % 128 remaining columns, with
+ * its own factors (the casts take its amax over those columns alone).  The
+ * power-of-two (UE8M0) calls and the K-grouped GEMM keep K % 128 == 0.
  *
  * Scale layouts.  Activation scales are per (row, 128-wide K group) and are
  * stored K-group-major ("transposed", as the digest requires for the LHS
@@ -55,7 +61,7 @@ extern "C" {
 typedef enum {
   FG_OK = 0,
   FG_EINVAL = 1,      /* null pointer, negative size, G <= 0, leading dimension too small */
-  FG_EALIGN = 2,      /* K % 128 != 0, M_total % 128 != 0, misaligned operand pointer or row stride */
+  FG_EALIGN = 2,      /* K % 16 != 0 (K % 128 != 0 where stated), M_total % 128 != 0, misaligned pointer or row stride */
   FG_EUNSUPPORTED = 3,/* sizes beyond what the kernels index (see per call) */
   FG_EHIP = 4         /* a HIP launch failed; see fg_last_error() */
 } fg_status;
@@ -68,7 +74,8 @@ typedef enum {
  *   sb  device fp32 [Nb][Kb]                       (4-byte aligned)
  *   D   device [M, N] bf16, row stride ldd elems   (ldd >= N, 2-byte aligned; rows that are 8- or
  *       16-byte aligned get vector stores); written
- * M, N >= 0 arbitrary; K % 128 == 0.  K == 0 writes D = 0 (sa, sb may then be NULL).
+ * M, N >= 0 arbitrary; K % 16 == 0 (a partial last K group when K % 128 != 0).
+ * K == 0 writes D = 0 (sa, sb may then be NULL).
  * Only D[0:M, 0:N] is written.  lda, ldb <= 4 MiB (FG_EUNSUPPORTED beyond).
  * Few rows (M <= 128): a weight-streaming kernel that may split K over
  * several workgroups; their fp32 partials meet in the library's workspace for
@@ -123,7 +130,7 @@ fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t 
  * fg_layout_workspace_bytes(layout, M, N, K) bytes (FG_EINVAL otherwise); it is
  * in use until the call's work on `stream` has finished.  Transposed rows must
  * fit 4 MiB (K <= 2^22) and the stored [K, .] operands at most 65535*128 rows
- * (FG_EUNSUPPORTED).  K % 128 == 0.  Nothing is allocated.
+ * (FG_EUNSUPPORTED).  K % 16 == 0.  Nothing is allocated.
  */
 fg_status gemm_fp8_nn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
@@ -180,7 +187,7 @@ int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total);
  *   sb        device fp32 [G][Nb][Kb]
  *   m_indices device int32 [M_total]: expert of each row, or -1 for a padding row
  *   D         device [M_total, N] bf16, packed (row stride N)
- * M_total % 128 == 0, K % 128 == 0, G >= 1.
+ * M_total % 128 == 0, K % 16 == 0, G >= 1.
  * Device-side precondition (not checked): within each aligned 128-row block
  * every non-negative index is the same value e < G.  The block is computed
  * against B[e], where e is the largest index in the block; rows whose index
@@ -203,7 +210,7 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
  *   D        device [G, M_cap, N] bf16, packed
  *   expected_m  host hint of the typical count (0 = unknown); only picks a tile shape
  * Group g computes rows [0, clamp(masked_m[g], 0, M_cap)); every other row of
- * D[g] is left untouched (bit for bit).  K % 128 == 0, G >= 1.
+ * D[g] is left untouched (bit for bit).  K % 16 == 0, G >= 1.
  */
 fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_sa,
                                   const uint8_t* B, const float* sb,
@@ -215,24 +222,26 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
  * Per-token (1 x 128) FP8 cast of activations (the digest leaves casting to
  * the user, "GEMM arayuzu ve yerlesim kisitlari"; this is the library's own
  * helper).  For each row m and group kb:
- *     amax = max |x[m, 128kb : 128kb+128]|
+ *     amax = max |x[m, 128kb : min(128kb+128, K)]|
  *     s    = max(amax, 1e-4f) / 448          (fp32, correctly rounded)
  *     q    = e4m3_RNE(x / s)                 (fp32 division, nearest-even)
  *   x   device fp32 [M, K], row stride ldx elements (ldx >= K, ldx % 4 == 0, 16-byte aligned)
  *   q   device [M, K] e4m3, packed (row stride K), 8-byte aligned
  *   sa  device fp32 [Kb][ld_sa], ld_sa >= M (written; the GEMM's activation-scale layout)
- * K % 128 == 0.  Input values must be finite.
+ * K % 16 == 0 (the last group holds K % 128 columns when K % 128 != 0).
+ * Input values must be finite.
  */
 fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa,
                              int M, int K, void* stream);
 
 /*
  * Per-block (128 x 128) FP8 cast of a weight matrix, same formula with amax
- * taken over each 128x128 block (the last row block covers N % 128 rows).
+ * taken over each 128x128 block (the last row block covers N % 128 rows, the
+ * last column block K % 128 columns).
  *   w   device fp32 [N, K], row stride ldw elements (ldw >= K, ldw % 4 == 0, 16-byte aligned)
  *   q   device [N, K] e4m3, packed, 4-byte aligned
  *   sb  device fp32 [Nb][Kb] (written; the GEMM's weight-scale layout)
- * K % 128 == 0.  For expert weights [G, N, K] with N % 128 == 0 one call on
+ * K % 16 == 0.  For expert weights [G, N, K] with N % 128 == 0 one call on
  * [G*N, K] yields the [G][Nb][Kb] layout; otherwise call once per expert.
  */
 fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,

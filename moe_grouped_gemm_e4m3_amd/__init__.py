@@ -7,7 +7,7 @@ same name.  Every step of the computation runs in the library's HIP kernels;
 there is no host or PyTorch fallback: if the library cannot be loaded, every
 call raises.
 
-Layouts (Kb = K/128, Nb = ceil(N/128)):
+Layouts (Kb = ceil(K/128), Nb = ceil(N/128)):
   A   e4m3 [M, K] (uint8 or torch.float8_e4m3fn), rows K-contiguous
   sa  fp32 [Kb, M] view of a [Kb, ld_sa] buffer (activation scales, K-group-major)
   B   e4m3 [N, K]                      sb  fp32 [Nb, Kb]
@@ -166,7 +166,7 @@ def aligned_scale_ld(rows: int) -> int:
 def empty_activation_scales(rows: int, K: int, device="cuda", groups: int | None = None) -> torch.Tensor:
     """A [Kb, rows] (or [G, Kb, rows]) view of a padded [.., Kb, ld_sa] fp32 buffer."""
     ld = aligned_scale_ld(rows)
-    Kb = K // 128
+    Kb = -(-K // 128)  # a partial last K group when K % 128 != 0
     if groups is None:
         return torch.empty(Kb, ld, dtype=torch.float32, device=device)[:, :rows]
     return torch.empty(groups, Kb, ld, dtype=torch.float32, device=device)[:, :, :rows]
@@ -400,7 +400,7 @@ def fp8_cast_per_block(w, q=None, sb=None, stream=None):
     if q is None:
         q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if sb is None:
-        sb = torch.empty((N + 127) // 128, K // 128, dtype=torch.float32, device=w.device)
+        sb = torch.empty((N + 127) // 128, -(-K // 128), dtype=torch.float32, device=w.device)
     q = _fp8(q, "q")
     if not (q.is_contiguous() and sb.is_contiguous()):
         raise ValueError("q and sb must be contiguous")

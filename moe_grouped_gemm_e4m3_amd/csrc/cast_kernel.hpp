@@ -86,29 +86,34 @@ __device__ __forceinline__ float4 load4(const uint16_t* src) {
 // One 16-lane group per (row, 128-column group); each lane handles 8 inputs.
 // UE8M0: sa is int32 [ceil(Kb/4)][ld_sa], the factor of K group kb of row m in
 // byte kb % 4 of element [kb / 4][m] (one byte store per group).
+// K tails (K % 128 != 0, K % 16 == 0): the last group holds K % 128 columns;
+// lanes past K load nothing, add nothing to the amax and store nothing.
 template <bool UE8M0, typename T>
 __global__ __launch_bounds__(256) void cast_per_token_kernel(const T* __restrict__ x, int64_t ldx,
                                                              uint8_t* __restrict__ q, void* __restrict__ sa,
                                                              int64_t ld_sa, int M, int K, int64_t total_lanes) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= total_lanes) return;  // total_lanes % 16 == 0: a group is all in or all out
-  const int Kb = K >> 7;
+  const int Kb = (K + 127) >> 7;
   const int64_t grp = gid >> 4;
   const int sub = (int)(gid & 15);
   const int m = (int)(grp / Kb);
   const int kb = (int)(grp - (int64_t)m * Kb);
-  float4 v0, v1;
-  load8(x + (int64_t)m * ldx + kb * 128 + sub * 8, v0, v1);
+  const bool in_k = kb * 128 + sub * 8 < K;  // K % 16 == 0: all 8 columns or none
+  float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+  if (in_k) load8(x + (int64_t)m * ldx + kb * 128 + sub * 8, v0, v1);
   float amax = absmax4(v1, absmax4(v0, 0.f));
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
   const float s32 = scale_of(amax);
   const uint32_t e = UE8M0 ? ue8m0_of(s32) : 0u;
   const float s = UE8M0 ? ue8m0_value(e) : s32;
-  uint2 out;
-  out.x = encode4(v0, s);
-  out.y = encode4(v1, s);
-  *(uint2*)(q + (int64_t)m * K + kb * 128 + sub * 8) = out;
+  if (in_k) {
+    uint2 out;
+    out.x = encode4(v0, s);
+    out.y = encode4(v1, s);
+    *(uint2*)(q + (int64_t)m * K + kb * 128 + sub * 8) = out;
+  }
   if (sub == 0) {
     if (UE8M0)
       ((uint8_t*)sa)[((int64_t)(kb >> 2) * ld_sa + m) * 4 + (kb & 3)] = (uint8_t)e;
@@ -120,19 +125,22 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const T* __restrict
 // One workgroup per 128x128 block: 32 lanes cover a 128-float row, 8 rows per
 // pass, 16 passes; the block is kept in registers between the amax reduction
 // and the encode.  UE8M0: sb is int32 [Nb][ceil(Kb/4)], the factor of block
-// (nb, kb) in byte kb % 4 of element [nb][kb / 4].
+// (nb, kb) in byte kb % 4 of element [nb][kb / 4].  The last row block may
+// hold fewer than 128 rows (N % 128) and the last column block fewer than
+// 128 columns (K % 128, a multiple of 16); lanes outside take no part.
 template <bool UE8M0, typename T>
 __global__ __launch_bounds__(256) void cast_per_block_kernel(const T* __restrict__ w, int64_t ldw,
                                                              uint8_t* __restrict__ q, void* __restrict__ sb,
                                                              int N, int K) {
   __shared__ float red[4];
-  const int Kb = K >> 7;
+  const int Kb = (K + 127) >> 7;
   const int nb = blockIdx.x / Kb;
   const int kb = blockIdx.x - nb * Kb;
   const int tid = threadIdx.x;
   const int c = tid & 31;
   const int r0 = tid >> 5;
-  const int rows = min(128, N - nb * 128);
+  // rows of the block this lane reads: none when its 4 columns lie past K
+  const int rows = kb * 128 + c * 4 < K ? min(128, N - nb * 128) : 0;
   const T* base = w + (int64_t)nb * 128 * ldw + kb * 128 + c * 4;
   float4 v[16];
   float amax = 0.f;

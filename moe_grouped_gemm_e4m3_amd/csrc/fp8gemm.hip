@@ -140,18 +140,25 @@ fg_status launch_gemm(fg::GemmParams& p, hipStream_t stream, const char* what) {
 // M=4096 shapes, 16 rows is 3 % faster at K=16384 and 4-5 % slower at K=1536.
 int raster_band(int K) { return K >= 8192 ? 16 : 8; }
 
-template <class C, int L>
-fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
+// K % 128 != 0 runs a build of the kernel whose last slice clips its loads
+// at column K; whole-slice problems keep the build without that code.
+template <class C, int L, bool KTAIL>
+fg_status launch_big_k(fg::GemmParams& p, hipStream_t stream, const char* what) {
   static int occ_cache = 0;
-  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L>, C::THREADS, &occ_cache);
+  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L, KTAIL>, C::THREADS, &occ_cache);
   p.group_m = raster_band(p.K);
   int64_t grid = 0;
   FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
   print_config(what, p, C::BM, C::BN, C::THREADS, grid, occ);
-  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L, KTAIL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
+}
+
+template <class C, int L>
+fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
+  return (p.K & 127) ? launch_big_k<C, L, true>(p, stream, what) : launch_big_k<C, L, false>(p, stream, what);
 }
 
 // ---------------------------------------------------------------------------
@@ -351,8 +358,8 @@ struct SkinnyPlan {
 
 
 bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool may_split, SkinnyPlan* out) {
-  if (M > 128 || K < 128) return false;
-  const int Kb = K / 128;
+  if (M > 128 || K <= 0) return false;
+  const int Kb = (K + 127) / 128;
   SkinnyPlan pl;
   pl.mf = M <= 64 ? 4 : 8;
   // 32-bit lane offsets
@@ -447,7 +454,7 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
                    const uint8_t* B, int64_t ldb, const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K,
                    void* stream, const char* what) {
   if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || N == 0) return FG_OK;
   if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
   FG_TRY(check_ptr(D, 2, "D"));
@@ -463,7 +470,7 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
     FG_TRY(check_row_bytes(lda, ldb));
   }
   p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
-  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128;
   if (p.ld_sb == 0) p.ld_sb = p.Kb;
   if (K > 0) {
     // few activation rows: the weight-streaming kernel
@@ -486,7 +493,7 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
       int cus = 0;
       FG_TRY(device_cus(&cus));
       if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
-      if (L == fg::kDense && want_stream_k(tm * tn, p.Kb, cus)) {
+      if (L == fg::kDense && K % 128 == 0 && want_stream_k(tm * tn, p.Kb, cus)) {
         int all_cus = 0;
         FG_TRY(device_cus(&all_cus));
         Workspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
@@ -534,7 +541,7 @@ fg_status gemm_layout(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
                       void* workspace, int64_t workspace_bytes, void* stream, const char* what) {
   g_err.clear();
   if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || N == 0) return FG_OK;
   if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
   if (C) FG_TRY(check_ptr(C, 4, "C"));
@@ -715,7 +722,7 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
   g_err.clear();
   if (M_total < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_total=%d N=%d K=%d", M_total, N, K);
   if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M_total % 128) return fail(FG_EALIGN, "M_total=%d is not a multiple of 128", M_total);
   if (M_total == 0 || N == 0) return FG_OK;
   if (M_total > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_total or N above 2^30");
@@ -732,7 +739,7 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
   p.m_indices = m_indices;
-  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K > 0) {
     // 256-row tiles: a tile whose halves hold different experts runs as two segments
     return launch_big_width<fg::kContiguous>(p, 1, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
@@ -752,7 +759,7 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
   (void)expected_m;
   if (M_cap < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_cap=%d N=%d K=%d", M_cap, N, K);
   if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M_cap == 0 || N == 0) return FG_OK;
   if (M_cap > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_cap or N above 2^30");
   FG_TRY(check_ptr(D, 2, "D"));
@@ -768,7 +775,7 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
   p.masked_m = masked_m;
-  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K > 0) {
     return launch_big_width<fg::kMasked>(p, G, (hipStream_t)stream, "gemm_fp8_grouped_masked");
   }
@@ -818,14 +825,14 @@ fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa,
                              void* stream) {
   g_err.clear();
   if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || K == 0) return FG_OK;
   FG_TRY(check_ptr(x, 16, "x"));
   FG_TRY(check_ptr(q, 8, "q"));
   FG_TRY(check_ptr(sa, 4, "sa"));
   FG_TRY(check_ld(ldx, K, 4, "ldx"));
   FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
-  const int64_t lanes = (int64_t)M * (K / 128) * 16;
+  const int64_t lanes = (int64_t)M * ((K + 127) / 128) * 16;
   const int64_t blocks = (lanes + 255) / 256;
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_token_kernel<false, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, ldx, q,
@@ -879,14 +886,14 @@ fg_status fp8_cast_per_token_bf16(const uint16_t* x, int64_t ldx, uint8_t* q, fl
                                   void* stream) {
   g_err.clear();
   if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || K == 0) return FG_OK;
   FG_TRY(check_ptr(x, 16, "x"));
   FG_TRY(check_ptr(q, 8, "q"));
   FG_TRY(check_ptr(sa, 4, "sa"));
   FG_TRY(check_ld(ldx, K, 8, "ldx"));
   FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
-  const int64_t lanes = (int64_t)M * (K / 128) * 16;
+  const int64_t lanes = (int64_t)M * ((K + 127) / 128) * 16;
   const int64_t blocks = (lanes + 255) / 256;
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_token_kernel<false, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
@@ -900,13 +907,13 @@ fg_status fp8_cast_per_block_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, fl
                                   void* stream) {
   g_err.clear();
   if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (N == 0 || K == 0) return FG_OK;
   FG_TRY(check_ptr(w, 16, "w"));
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<false, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)stream, w, ldw, q, (void*)sb, N, K);
@@ -918,13 +925,13 @@ fg_status fp8_cast_per_block_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, fl
 fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb, int N, int K, void* stream) {
   g_err.clear();
   if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (N == 0 || K == 0) return FG_OK;
   FG_TRY(check_ptr(w, 16, "w"));
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<false, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
                      sb, N, K);

@@ -224,6 +224,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
+// A lane offset at or past the end of every range make_rsrc builds (they
+// hold at most 2^31 - 1 bytes), read as signed or unsigned, with or without
+// the instruction's scalar offset (at most a 4 MiB row) added, and without
+// 32-bit wrap-around: such a load returns zeros and touches no memory.
+constexpr int kOobOffset = 0x7fffffff;
+
+// K tails (K % 128 != 0, K % 16 == 0): the last slice holds K % 128 columns.
+// A 16-byte chunk that starts at or past column K of its row is read as
+// zeros (the bytes there belong to the next row or to padding), so both
+// operands contribute 0 * 0 past K.  `kcol` is the chunk's first column.
+__device__ __forceinline__ int k_clip(int voff, int kcol, int K) { return kcol < K ? voff : kOobOffset; }
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 template <class C, int L>
 __global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
@@ -304,9 +321,11 @@ __global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
     i32x4 ra[CA], rb[CB];
     if (Kb > 0) {
 #pragma unroll
-      for (int i = 0; i < CA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, a_voff + i * a_pass, 0, 0);
+      for (int i = 0; i < CA; ++i)
+        ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, k_clip(a_voff + i * a_pass, ld_c * 16, p.K), 0, 0);
 #pragma unroll
-      for (int i = 0; i < CB; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, b_voff + i * b_pass, 0, 0);
+      for (int i = 0; i < CB; ++i)
+        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, k_clip(b_voff + i * b_pass, ld_c * 16, p.K), 0, 0);
 #pragma unroll
       for (int i = 0; i < CA; ++i) *(i32x4*)(smem + a_dst0 + i * ROWS_PER_PASS * 128) = ra[i];
 #pragma unroll
@@ -318,10 +337,13 @@ __global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
       const bool more = kb + 1 < Kb;
       if (more) {
         const int ko = (kb + 1) * 128;
+        const int kc = ko + ld_c * 16;
 #pragma unroll
-        for (int i = 0; i < CA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, a_voff + i * a_pass, ko, 0);
+        for (int i = 0; i < CA; ++i)
+          ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, k_clip(a_voff + i * a_pass, kc, p.K), ko, 0);
 #pragma unroll
-        for (int i = 0; i < CB; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, b_voff + i * b_pass, ko, 0);
+        for (int i = 0; i < CB; ++i)
+          rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, k_clip(b_voff + i * b_pass, kc, p.K), ko, 0);
       }
       // slice scales: s = sa[kb][m] * sb[nb][kb]
       const float sbv = sb_wave[kb];
@@ -554,7 +576,9 @@ __device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& i
 
 // sa_k: the row of the activation-factor array that holds slice kb's factors
 // (kb itself for fp32 factors; kb / 4 for packed power-of-two factors).
-template <class C>
+// KTAIL: the kernel is built for K % 128 != 0 (launches with whole slices
+// only use the build without it, whose loads carry no clipping code at all).
+template <class C, bool KTAIL = false>
 __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Work& t, int kb, uint8_t* stage,
                                                   uint8_t* sa_area, int wave, int lane, int sa_k = -1) {
   constexpr int BM = C::BM;
@@ -570,17 +594,27 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
   const int comb0 = q0 * 8 + (lane >> 3);  // combined (A|B) row of this lane in load 0
   const int p_chunk = lane & 7;
+  // A whole slice loads as is; only the partial last slice of a K tail
+  // (wave-uniform branch) clips its chunks at column K.
+  const int kleft = p.K - kb * 128;
+  auto loads = [&](auto clip) {
 #pragma unroll
-  for (int j = 0; j < (LA > LB ? LA : LB); ++j) {
-    if (LA == LB || j < n) {
-      const int comb = comb0 + 8 * j;
-      const int r = row0 + 8 * j + (lane >> 3);
-      const int c = p_chunk ^ swz16(comb);
-      const int voff = r * (int)ld + c * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (q0 + j) * 1024),
-                                               16, voff, kb * 128, 0, 0);
+    for (int j = 0; j < (LA > LB ? LA : LB); ++j) {
+      if (LA == LB || j < n) {
+        const int comb = comb0 + 8 * j;
+        const int r = row0 + 8 * j + (lane >> 3);
+        const int c = p_chunk ^ swz16(comb);
+        int voff = r * (int)ld + c * 16;
+        if (decltype(clip)::value) voff = k_clip(voff, c * 16, kleft);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (q0 + j) * 1024),
+                                                 16, voff, kb * 128, 0, 0);
+      }
     }
-  }
+  };
+  if (!KTAIL || kleft >= 128)
+    loads(BoolC<false>{});
+  else
+    loads(BoolC<true>{});
   if (is_a) {
     // sa[kb][m0 + 64 wave + lane] into the stage's scale area; rows past
     // rows_alloc read as 0 (their outputs are never stored)
@@ -791,7 +825,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
   }
 }
 
-template <class C, int L>
+template <class C, int L, bool KTAIL>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
@@ -832,7 +866,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 
   float sb_c[2];
   load_sb<C>(p, cur, 0, wn, sb_c);
-  issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane);
+  issue_slice_loads<C, KTAIL>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -860,10 +894,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
       float sb_n[2] = {0.f, 0.f};
       if (!last) {
         load_sb<C>(p, cur, kb + 1, wn, sb_n);
-        issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
+        issue_slice_loads<C, KTAIL>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       } else if (nxt.w >= 0) {
         load_sb<C>(p, nxt, 0, wn, sb_n);
-        issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
+        issue_slice_loads<C, KTAIL>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       }
 
       if (active) {

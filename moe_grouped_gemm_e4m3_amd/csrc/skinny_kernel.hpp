@@ -76,23 +76,33 @@ struct SkinnyLanes {
   int sa_voff;         // this lane's activation row, bytes
   int sa_kstep;        // bytes between K slices of sa
   const float* sb;     // sb[nb][.] of the tile's weight-scale block
+  int kq16;            // first column of this lane's 16-byte chunk inside a slice (16 * lane group)
+  int K;
 };
 
 template <class C>
 __device__ __forceinline__ void skinny_load(SkinnySlice<C>& f, const SkinnyLanes& g, int kb) {
   const int k0 = kb * 128;
+  // K tail: chunks at or past column K read as zeros (k_clip).  Always true
+  // for whole slices; the selects cost a few VALU ops in a kernel that waits
+  // on memory.
+  const bool lo_in = k0 + g.kq16 < g.K, hi_in = k0 + 64 + g.kq16 < g.K;
 #pragma unroll
   for (int i = 0; i < C::MF; ++i) {
     const int v = g.a_voff + i * g.a_step;
-    const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.ra, v, k0, 0));
-    const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.ra, v, k0 + 64, 0));
+    const i32x4 lo =
+        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.ra, lo_in ? v : kOobOffset, k0, 0));
+    const i32x4 hi =
+        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.ra, hi_in ? v : kOobOffset, k0 + 64, 0));
     f.a[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 #pragma unroll
   for (int j = 0; j < C::CF; ++j) {
     const int v = g.b_voff + j * g.b_step;
-    const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, v, k0, 0));
-    const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, v, k0 + 64, 0));
+    const i32x4 lo =
+        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, lo_in ? v : kOobOffset, k0, 0));
+    const i32x4 hi =
+        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, hi_in ? v : kOobOffset, k0 + 64, 0));
     f.b[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 #pragma unroll
@@ -170,6 +180,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   g.sa_voff = l16 * 4;
   g.sa_kstep = (int)p.ld_sa * 4;
   g.sb = p.sb + (int64_t)(n0 >> 7) * p.ld_sb;
+  g.kq16 = 16 * q;
+  g.K = p.K;
 
   float acc[C::GROUPS][4];
 #pragma unroll

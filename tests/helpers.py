@@ -79,7 +79,7 @@ def exact_regime(rng, M, N, K, groups=None):
     shapeB = (N, K) if groups is None else (groups[1], N, K)
     A = rng.choice(pool, shapeA)
     B = rng.choice(pool, shapeB)
-    Kb, Nb = K // 128, -(-N // 128)
+    Kb, Nb = -(-K // 128), -(-N // 128)
     pw = np.array([0.5, 1.0, 2.0], np.float32)
     sa = rng.choice(pw, shapeA[:-2] + (Kb, M))
     sb = rng.choice(pw, shapeB[:-2] + (Nb, Kb))

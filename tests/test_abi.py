@@ -135,7 +135,7 @@ def masked(lib, A=P16, sa=P16, ld_sa=256, B=P16, sb=P16, mask=P16, D=P16, G=4, M
     [
         (dict(G=0), FG_EINVAL, "G=0"),
         (dict(Mc=-1), FG_EINVAL, "negative"),
-        (dict(K=64), FG_EALIGN, "K=64"),
+        (dict(K=72), FG_EALIGN, "K=72"),
         (dict(mask=None), FG_EINVAL, "masked_m is NULL"),
         (dict(B=None), FG_EINVAL, "B is NULL"),
         (dict(ld_sa=100), FG_EINVAL, "ld_sa=100"),
@@ -158,6 +158,24 @@ def test_cast_argument_errors(lib):
     assert lib.fp8_cast_per_block(P16, 255, P4, P4, 130, 256, None) == FG_EINVAL
     assert lib.fp8_cast_per_block(P16, 256, None, P4, 130, 256, None) == FG_EINVAL
     assert lib.fp8_cast_per_block(P16, 256, P4, P4, -1, 256, None) == FG_EINVAL
+
+
+def test_k_tail_alignment_rules(lib):
+    """K % 16 == 0 is enough for the fp32-factor calls (a partial last K
+    group); the power-of-two-factor calls keep K % 128 == 0; K % 16 != 0
+    fails everywhere.  Checked before anything touches a device."""
+    for K in (8, 100, 1028):
+        assert dense(lib, K=K, lda=512, ldb=512) == FG_EALIGN
+        assert "multiple of 16" in lib.fg_last_error().decode()
+        assert contig(lib, K=K) == FG_EALIGN
+        assert masked(lib, K=K) == FG_EALIGN
+        assert lib.fp8_cast_per_token(P16, 512, P8, P4, 64, 64, K, None) == FG_EALIGN
+        assert lib.fp8_cast_per_block(P16, 512, P4, P4, 130, K, None) == FG_EALIGN
+    for K in (16, 176, 304):
+        assert lib.gemm_fp8_nt_ue8m0(P16, 512, P4, 64, P16, 512, P4, P16, 256, 64, 256, K, None) == FG_EALIGN
+        assert "multiple of 128" in lib.fg_last_error().decode()
+        assert lib.fp8_cast_per_token_ue8m0(P16, 512, P8, P4, 64, 64, K, None) == FG_EALIGN
+        assert lib.fp8_cast_per_block_ue8m0(P16, 512, P4, P4, 130, K, None) == FG_EALIGN
 
 
 def test_num_cus_setter(lib):
