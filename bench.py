@@ -50,6 +50,12 @@ CSRC = os.path.join(ROOT, "moe_grouped_gemm_e4m3_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_dense_m4096_traffic.json")
 
 
+def progress(msg: str) -> None:
+    """One line on stderr per finished phase (the JSON result goes to stdout)."""
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
@@ -198,6 +204,7 @@ def other_configs():
         nbytes = M * K + N * K + 4 * (M * Kb + -(-N // 128) * Kb) + 2 * M * N
         out.append(shape_entry("dense_small_m", (M, N, K), ms, 2 * M * N * K, nbytes, "hbm"))
         del copies
+        progress(f"small-M dense {M}x{N}x{K}: {ms * 1e3:.2f} us")
     # the dense M=4096 shapes with power-of-two (UE8M0) factors (GPU casts)
     for (M, N, K) in synth.DENSE_M4096.shapes:
         A32, B32 = synth.dense_problem(M, N, K, seed=0)
@@ -210,6 +217,7 @@ def other_configs():
         nbytes = M * K + N * K + 4 * (M * Kb4 + -(-N // 128) * Kb4) + 2 * M * N
         out.append(shape_entry("dense_m4096_ue8m0", (M, N, K), ms, 2 * M * N * K, nbytes, "mfma"))
         del qa, qb, D
+        progress(f"UE8M0 dense {M}x{N}x{K}: {ms * 1e3:.2f} us")
     # the dense M=4096 shapes with an fp32 addend, D = C + A B^T; the plain
     # GEMM on the same operands is timed beside it
     for (M, N, K) in synth.DENSE_M4096.shapes:
@@ -240,6 +248,7 @@ def other_configs():
             out.append(e)
             del As, Bs, ws
         del qa, qb, C, D
+        progress(f"addend and layouts {M}x{N}x{K} done")
     # K-grouped TN (weight gradients of the contiguous workload: 8 experts x
     # 4096 tokens, M = 4096, N = 7168); operands drawn on the GPU from a
     # seeded generator and cast there
@@ -258,6 +267,7 @@ def other_configs():
     e = shape_entry("k_grouped_tn_8x4096", (len(ks), M, N, ks[0]), ms, 2 * M * N * Kt, nbytes, "mfma")
     out.append(e)
     del As, Bs, D, ws
+    progress(f"K-grouped TN: {ms * 1e3:.2f} us")
     G, rows, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
     A32, B32, idx = synth.contiguous_problem([rows] * G, N, K, seed=0)
     qa, sa = fg.fp8_cast_per_token(A32.cuda())
@@ -279,6 +289,7 @@ def other_configs():
     out.append(shape_entry("contiguous_8x4096", (G, rows, N, K), float(np.median(ts)), 2 * Mt * N * K,
                            Mt * K + G * N * K + 2 * Mt * N, "mfma"))
     del A32, B32, qa, qb, D
+    progress("contiguous done")
     for (G, Mc, N, K) in synth.MASKED_16x256.shapes:
         A32, B32, mask = synth.masked_problem(G, Mc, N, K, seed=0)
         qa = torch.empty(G, Mc, K, dtype=torch.uint8, device="cuda")
@@ -297,6 +308,7 @@ def other_configs():
         out.append(shape_entry("masked_16x256", (G, Mc, N, K), ms, 2 * rv * N * K, rv * K + G * N * K + 2 * rv * N,
                                "hbm"))
         del copies, qa, qb, D
+        progress(f"masked {G}x{Mc}x{N}x{K}: {ms * 1e3:.2f} us")
     return out
 
 
@@ -387,7 +399,9 @@ def main():
     problems = [Problem(*s, seed=0) for s in wl.shapes]
     torch.cuda.synchronize()
 
+    progress(f"{len(problems)} problems resident")
     wall, per = time_steps(problems, args.steps, args.warmup)
+    progress(f"{args.steps} timed steps: {wall / args.steps * 1e3:.3f} ms per step")
     casts = time_casts(problems)
     others = None if args.no_other_configs else other_configs()
     gemm_ms = per.sum(axis=1)  # GEMM time per step (sum of launch durations)
