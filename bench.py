@@ -193,6 +193,16 @@ def other_configs():
     memory-bound launches are timed by graph replay (their GPU time is a few
     microseconds, below the host's per-call cost)."""
     out = []
+    # the small dense problem 128x256x512: a launch-latency case, timed by
+    # graph replay like the memory-bound launches
+    for (M, N, K) in synth.SMALL_DENSE.shapes:
+        A32, B32 = synth.dense_problem(M, N, K, seed=0)
+        qa, sa = fg.fp8_cast_per_token(A32.cuda())
+        qb, sb = fg.fp8_cast_per_block(B32.cuda())
+        D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ms = graph_time(lambda i: fg.gemm_fp8_nt(qa, sa, qb, sb, D))
+        out.append(shape_entry("dense_small", (M, N, K), ms, 2 * M * N * K, dense_bytes(M, N, K), "launch"))
+        progress(f"small dense {M}x{N}x{K}: {ms * 1e3:.2f} us")
     for (M, N, K) in synth.DENSE_SMALL_M.shapes:
         A32, B32 = synth.dense_problem(M, N, K, seed=0)
         qa, sa = fg.fp8_cast_per_token(A32.cuda())
@@ -325,6 +335,19 @@ def cpu_baseline(problems, budget_s: float = 15.0):
     except Exception:  # pragma: no cover
         cores = 0
     cores = cores or len(os.sched_getaffinity(0))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = ", ".join(sorted({f"{t.get('internal_api')} {t.get('version')}" for t in threadpool_info()
+                                 if t.get("user_api") == "blas"}))
+    except Exception:  # pragma: no cover
+        blas = ""
     # calibrate on the first shape, then size the sample to the budget
     ms, ns = 64, 256
     samples = []
@@ -349,6 +372,8 @@ def cpu_baseline(problems, budget_s: float = 15.0):
         "unit": "TFLOPS",
         "cores": int(cores),
         "kind": "oracle",
+        "cpu_model": cpu_model,
+        "blas": blas,
         "sample": f"fp64 blockwise oracle on D[0:{ms}, 0:{ns}] at full K of each of the {len(problems)} shapes, "
                   f"{reps} passes, {dt:.1f} s",
     }
