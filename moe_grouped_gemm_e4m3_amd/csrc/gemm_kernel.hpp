@@ -695,10 +695,14 @@ template <class C>
 __device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[2], const int (&b_off)[2],
                                           const float (&s)[C::SM][2], int tb, float (&acc)[C::SM][C::SN][4]) {
   constexpr int SM = C::SM, SN = C::SN;
+  // the first weight fragment, then the activation fragments in the order
+  // the first subtile's MFMAs use them: LDS reads return in order, so the
+  // first MFMA waits for two fragments instead of all SM + 1
+  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
   i32x8 af[SM];
 #pragma unroll
   for (int ms = 0; ms < SM; ++ms) af[ms] = lds_frag(st, a_off[0] + ms * 2048, a_off[1] + ms * 2048);
-  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 prev[SM];
 #pragma unroll
   for (int tt = 0; tt < SN; ++tt) {
@@ -902,20 +906,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
     for (int kb = 0; kb < Kb; ++kb) {
       // prefetch the following slice: this tile's next one, or the first of the next work item
       const bool last = kb + 1 == Kb;
-      float sb_n[2] = {0.f, 0.f};
-      if (!last) {
-        load_sb<C>(p, cur, kb + 1, wn, sb_n);
+      if (!last)
         issue_slice_loads<C, KTAIL>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
-      } else if (nxt.w >= 0) {
-        load_sb<C>(p, nxt, 0, wn, sb_n);
+      else if (nxt.w >= 0)
         issue_slice_loads<C, KTAIL>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
-      }
 
       if (active) {
         float s[SM][2];
         slice_scales<C>(FG_SA(stage), wm, l16, sb_c, s);
         slice_mma<C>(FG_STAGE(stage), a_off, b_off, s, tb, acc);
       }
+
+      // The next slice's weight scales are scalar loads, issued only now:
+      // with one outstanding, every LDS wait inside the slice would have to
+      // be a full lgkmcnt(0) (scalar loads return out of order), so the first
+      // MFMAs could not start before all of the slice's fragment reads land.
+      float sb_n[2] = {0.f, 0.f};
+      if (!last)
+        load_sb<C>(p, cur, kb + 1, wn, sb_n);
+      else if (nxt.w >= 0)
+        load_sb<C>(p, nxt, 0, wn, sb_n);
 
       // This wave's operand loads have landed in LDS; the barrier publishes
       // them to the other waves (and frees the stage just read).
