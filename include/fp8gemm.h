@@ -208,7 +208,8 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
  *   sb       device fp32 [G][Nb][Kb]
  *   masked_m device int32 [G]: valid rows of each group
  *   D        device [G, M_cap, N] bf16, packed
- *   expected_m  host hint of the typical count (0 = unknown); only picks a tile shape
+ *   expected_m  host hint of the typical count (0 = unknown); accepted for interface compatibility,
+ *               the plan does not use it (measured: the tile width chosen from G, M_cap and N is best)
  * Group g computes rows [0, clamp(masked_m[g], 0, M_cap)); every other row of
  * D[g] is left untouched (bit for bit).  K % 16 == 0, G >= 1.
  */
