@@ -271,10 +271,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   for (int y = 0; y < C::GPW; ++y) {
     const int x = wave * C::GPW + y;
     const int off = ((split * C::GROUPS + x) * 64 + lane) * 16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sum[y][r]), prs, off + 4 * r, 0,
-                                            kSysCoherent);
+    const f32x4 v = {sum[y][0], sum[y][1], sum[y][2], sum[y][3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), prs, off, 0, kSysCoherent);
   }
   // the stores are acknowledged at the point of coherence before counting in
   __builtin_amdgcn_s_waitcnt(0);
@@ -287,22 +285,40 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   __syncthreads();
   if (!*last_flag) return;
 
+  // The partials are added in split order.  Their loads are issued in
+  // batches of up to kBatch splits for all of the wave's blocks before any
+  // is used, so a batch costs one memory round trip instead of one per
+  // split and block.
+  constexpr int kBatch = 4;
+  float t[C::GPW][4];
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    i32x4 u[kBatch][C::GPW];
 #pragma unroll
-  for (int y = 0; y < C::GPW; ++y) {
-    const int x = wave * C::GPW + y;
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = s0 + j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float u = s == split ? sum[y][r]
-                                   : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                                   prs, ((s * C::GROUPS + x) * 64 + lane) * 16 + 4 * r,
-                                                                   0, kSysCoherent));
-        t[r] = s == 0 ? u : t[r] + u;
+      for (int y = 0; y < C::GPW; ++y) {
+        const int x = wave * C::GPW + y;
+        if (s < splits && s != split)
+          u[j][y] = __builtin_amdgcn_raw_buffer_load_b128(prs, ((s * C::GROUPS + x) * 64 + lane) * 16, 0,
+                                                          kSysCoherent);
       }
     }
-    skinny_store<C, ADD_C>(p, n0, x, t, lane);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = s0 + j;
+      if (s >= splits) break;
+#pragma unroll
+      for (int y = 0; y < C::GPW; ++y) {
+        const f32x4 v = s == split ? f32x4{sum[y][0], sum[y][1], sum[y][2], sum[y][3]}
+                                   : __builtin_bit_cast(f32x4, u[j][y]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[y][r] = s == 0 ? v[r] : t[y][r] + v[r];
+      }
+    }
   }
+#pragma unroll
+  for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, n0, wave * C::GPW + y, t[y], lane);
   // every workgroup of the tile has counted in: reset for the next launch
   if (tid == 0) __hip_atomic_store(p.sk_flags + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
