@@ -299,11 +299,39 @@ fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream
 
 // Dense GEMM with power-of-two factors: the large kernel's tiles (widths as
 // pick_bn chooses them) on the scaled MFMA; the kernel is in ue8m0.hip.
-fg_status launch_ue8m0(fg::GemmParams& p, int bn, hipStream_t stream, const char* what) {
-  static int occ_cache[2] = {0, 0};
-  int& occ = occ_cache[bn == 160 ? 1 : 0];
-  if (occ == 0) occ = fg::ue8m0_occupancy(bn);
-  p.tiles_m = (p.rows + CfgBig::BM - 1) / CfgBig::BM;
+// Tile shape of the power-of-two-factor GEMM: the one with the least
+// (rounds x tile time).  Tile times are relative, from measurement on the
+// M=4096 shapes: 256x224 = 240, 256x160 = 176, 128x256 = 144 (a 128-row tile
+// reuses each weight byte half as often, so it costs more than half a
+// 256-row one).  FG_FORCE_BN=224|160 keeps the older width-only choice.
+int pick_ue8m0_tile(int M, int N) {
+  const char* f = getenv("FG_FORCE_BN");
+  if (f && *f) return pick_bn((M + 255) / 256, N, false) == 160 ? fg::kUe8m0Tile256x160 : fg::kUe8m0Tile256x224;
+  int cus = 0;
+  if (device_cus(&cus) != FG_OK) return fg::kUe8m0Tile256x224;
+  if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
+  static const int tiles[3] = {fg::kUe8m0Tile256x224, fg::kUe8m0Tile256x160, fg::kUe8m0Tile128x256};
+  static const int cost[3] = {240, 176, 144};
+  int best = tiles[0];
+  int64_t best_cost = -1;
+  for (int i = 0; i < 3; ++i) {
+    const int bm = fg::ue8m0_tile_bm(tiles[i]), bn = fg::ue8m0_tile_bn(tiles[i]);
+    const int64_t n = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const int64_t c = (n + cus - 1) / cus * cost[i];
+    if (best_cost < 0 || c < best_cost) {
+      best = tiles[i];
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
+fg_status launch_ue8m0(fg::GemmParams& p, int tile, hipStream_t stream, const char* what) {
+  static int occ_cache[3] = {0, 0, 0};
+  int& occ = occ_cache[tile];
+  if (occ == 0) occ = fg::ue8m0_occupancy(tile);
+  const int bm = fg::ue8m0_tile_bm(tile), bn = fg::ue8m0_tile_bn(tile);
+  p.tiles_m = (p.rows + bm - 1) / bm;
   p.tiles_n = (p.N + bn - 1) / bn;
   const int64_t slots = (int64_t)p.tiles_m * p.tiles_n;
   if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
@@ -311,8 +339,8 @@ fg_status launch_ue8m0(fg::GemmParams& p, int bn, hipStream_t stream, const char
   p.group_m = raster_band(p.K);
   int64_t grid = 0;
   FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
-  print_config(what, p, CfgBig::BM, bn, CfgBig::THREADS, grid, occ);
-  const hipError_t e = fg::ue8m0_launch(p, bn, grid, stream);
+  print_config(what, p, bm, bn, 512, grid, occ);
+  const hipError_t e = fg::ue8m0_launch(p, tile, grid, stream);
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
 }
@@ -817,8 +845,12 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   FG_TRY(check_ld(ldb, K, 16, "ldb"));
   FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
   FG_TRY(check_row_bytes(lda, ldb));
-  const int64_t row_tiles = (M + CfgBig::BM - 1) / CfgBig::BM;
-  return launch_ue8m0(p, pick_bn(row_tiles, N, false), (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+  int tile = pick_ue8m0_tile(M, N);
+  const char* ft = getenv("FG_UE8M0_TILE");
+  if (ft && strcmp(ft, "128x256") == 0) tile = fg::kUe8m0Tile128x256;
+  if (ft && strcmp(ft, "256x224") == 0) tile = fg::kUe8m0Tile256x224;
+  if (ft && strcmp(ft, "256x160") == 0) tile = fg::kUe8m0Tile256x160;
+  return launch_ue8m0(p, tile, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
 }
 
 fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa, int M, int K,

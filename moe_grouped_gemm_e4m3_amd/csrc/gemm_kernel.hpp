@@ -971,7 +971,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 // in the stage's scale area (the packed word of K groups 4i..4i+3 of each
 // row), the weight factors through the scalar cache.
 //
-// Built for the 256x224 and 256x160 tiles only.  The accumulators are
+// Built for 256x224, 256x160 and 128x256 tiles.  The accumulators are
 // updated in place in VGPRs; with a 256x256 tile's 128 of them plus the
 // operand fragments the register allocator falls back to copying every
 // MFMA result and spills (two waves per SIMD leave 256 registers a wave).
@@ -1013,10 +1013,10 @@ __device__ __forceinline__ void slice_mma_ue8m0(const uint8_t* st, const int (&a
   // fragments: all of A, B one subtile ahead; the fences keep the compiler
   // from reading further ahead (registers: the 128 accumulators are updated
   // in place only while the live fragments stay this few)
+  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
   i32x8 af[SM];
 #pragma unroll
   for (int ms = 0; ms < SM; ++ms) af[ms] = lds_frag(st, a_off[0] + ms * 2048, a_off[1] + ms * 2048);
-  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
 #pragma unroll
   for (int tt = 0; tt < SN; ++tt) {
     i32x8 bn = bf;
@@ -1090,15 +1090,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
 
     for (int kb = 0; kb < Kb; ++kb) {
       const bool last = kb + 1 == Kb;
-      int sb_n[2] = {127, 127};
-      if (!last) {
-        load_sb_ue8m0<C>(p, cur, kb + 1, wn, sb_n);
+      if (!last)
         issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, (kb + 1) >> 2);
-      } else if (nxt.w >= 0) {
-        load_sb_ue8m0<C>(p, nxt, 0, wn, sb_n);
+      else if (nxt.w >= 0)
         issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, 0);
-      }
       if (active) slice_mma_ue8m0<C>(FG_STAGE(stage), a_off, b_off, FG_SA(stage), wm, l16, kb, sb_c, tb, acc);
+      // the next slice's weight factors (scalar loads) only after the MFMAs,
+      // so that the slice's LDS waits can be partial
+      int sb_n[2] = {127, 127};
+      if (!last)
+        load_sb_ue8m0<C>(p, cur, kb + 1, wn, sb_n);
+      else if (nxt.w >= 0)
+        load_sb_ue8m0<C>(p, nxt, 0, wn, sb_n);
 
       __builtin_amdgcn_s_waitcnt(0);
       asm volatile("" ::: "memory");

@@ -23,12 +23,20 @@ hipError_t launch(const GemmParams& p, int64_t grid, hipStream_t stream) {
 
 }  // namespace
 
-int ue8m0_occupancy(int bn) {
-  return bn == 160 ? occupancy<BigCfg<256, 160, 4, 2>>() : occupancy<BigCfg<256, 224, 4, 2>>();
+int ue8m0_occupancy(int tile) {
+  switch (tile) {
+    case kUe8m0Tile256x160: return occupancy<BigCfg<256, 160, 4, 2>>();
+    case kUe8m0Tile128x256: return occupancy<BigCfg<128, 256, 2, 4>>();
+    default: return occupancy<BigCfg<256, 224, 4, 2>>();
+  }
 }
 
-hipError_t ue8m0_launch(const GemmParams& p, int bn, int64_t grid, hipStream_t stream) {
-  return bn == 160 ? launch<BigCfg<256, 160, 4, 2>>(p, grid, stream) : launch<BigCfg<256, 224, 4, 2>>(p, grid, stream);
+hipError_t ue8m0_launch(const GemmParams& p, int tile, int64_t grid, hipStream_t stream) {
+  switch (tile) {
+    case kUe8m0Tile256x160: return launch<BigCfg<256, 160, 4, 2>>(p, grid, stream);
+    case kUe8m0Tile128x256: return launch<BigCfg<128, 256, 2, 4>>(p, grid, stream);
+    default: return launch<BigCfg<256, 224, 4, 2>>(p, grid, stream);
+  }
 }
 
 }  // namespace fg

@@ -3,7 +3,7 @@ casts and the dense GEMM on the scaled MFMA.
 
 The casts must match the oracle byte for byte (codes and factor bytes).  The
 GEMM is compared bit for bit in the exact regime -- its factors {1/2, 1, 2}
-are powers of two already -- for both of its tile widths (FG_FORCE_BN), and within
+are powers of two already -- for each of its tile shapes (FG_UE8M0_TILE), and within
 the oracle's per-element bound on random inputs.  Doubling one factor (its
 byte + 1) must double exactly the outputs it touches."""
 
@@ -76,10 +76,13 @@ def test_cast_per_block_bytes(gpu_lib, N, K):
     assert np.array_equal(quant.unpack_ue8m0(sb.cpu().numpy(), K // 128, axis=1), e_ref)
 
 
-@pytest.fixture(params=[224, 160])
+@pytest.fixture(params=["256x224", "256x160", "128x256"])
 def width(request, monkeypatch):
-    monkeypatch.setenv("FG_FORCE_BN", str(request.param))
-    return request.param
+    """The kernel's tile shapes, forced with FG_UE8M0_TILE; the value is the
+    tile width (used to vary the seeds)."""
+    monkeypatch.delenv("FG_FORCE_BN", raising=False)
+    monkeypatch.setenv("FG_UE8M0_TILE", request.param)
+    return int(request.param.split("x")[1])
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (70, 300, 256), (256, 896, 512), (300, 1000, 640), (513, 2112, 256)])
