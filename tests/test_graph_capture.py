@@ -47,14 +47,27 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
     small = _dense_operands(64, 2112, 7168, seed=1)
     large = _dense_operands(512, 1024, 1024, seed=2)
     masked = _masked_operands(4, 256, 512, 768, seed=3)
+    # K tails (K = 1040) on the few-row and large-tile kernels, and the
+    # power-of-two-factor GEMM (its 128x256 tile at this shape)
+    tail_small = _dense_operands(64, 2112, 1040, seed=4)
+    tail_large = _dense_operands(512, 1024, 1040, seed=5)
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    qa_u, sa_u = gpu_lib.fp8_cast_per_token_ue8m0(torch.randn(512, 1024, device="cuda", generator=gen))
+    qb_u, sb_u = gpu_lib.fp8_cast_per_block_ue8m0(torch.randn(4096, 1024, device="cuda", generator=gen))
     outs = [torch.empty(64, 2112, dtype=torch.bfloat16, device="cuda"),
             torch.empty(512, 1024, dtype=torch.bfloat16, device="cuda"),
-            torch.empty(4, 256, 512, dtype=torch.bfloat16, device="cuda")]
+            torch.empty(4, 256, 512, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(64, 2112, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(512, 1024, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(512, 4096, dtype=torch.bfloat16, device="cuda")]
 
     def run_all(stream=None):
         gpu_lib.gemm_fp8_nt(*small, outs[0], stream=stream)
         gpu_lib.gemm_fp8_nt(*large, outs[1], stream=stream)
         gpu_lib.gemm_fp8_grouped_masked(*masked[:4], masked[4], outs[2], stream=stream)
+        gpu_lib.gemm_fp8_nt(*tail_small, outs[3], stream=stream)
+        gpu_lib.gemm_fp8_nt(*tail_large, outs[4], stream=stream)
+        gpu_lib.gemm_fp8_nt_ue8m0(qa_u, sa_u, qb_u, sb_u, outs[5], stream=stream)
 
     s = torch.cuda.Stream()
     if not fresh_stream:
@@ -89,6 +102,8 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
         assert np.array_equal(got[0], ref[0]), rep
         assert np.array_equal(got[1], ref[1]), rep
         assert np.array_equal(got[2][valid], ref[2][valid]), rep
+        for i in (3, 4, 5):
+            assert np.array_equal(got[i], ref[i]), (rep, i)
         run_all()  # eager work between replays (default plan)
         torch.cuda.synchronize()
 
