@@ -135,9 +135,10 @@ __device__ __forceinline__ void skinny_compute(const SkinnySlice<C>& f, float (&
 // Store 16x16 block g (lane: row 16i + l%16, columns 16j + 4(l/16) .. +3) as bf16.
 // With ADD_C the fp32 addend C is added first (D = C + A B^T).
 template <class C, bool ADD_C>
-__device__ __forceinline__ void skinny_store(const GemmParams& p, int n_tile0, int g, const float (&acc)[4], int lane) {
+__device__ __forceinline__ void skinny_store(const GemmParams& p, int r0, int n_tile0, int g, const float (&acc)[4],
+                                             int lane) {
   const int i = g / C::CF, j = g % C::CF;
-  const int m = 16 * i + (lane & 15);
+  const int m = r0 + 16 * i + (lane & 15);
   const int n = n_tile0 + 16 * j + 4 * (lane >> 4);
   if (m >= p.rows || n >= p.N) return;
   float v[4] = {acc[0], acc[1], acc[2], acc[3]};
@@ -152,16 +153,21 @@ __device__ __forceinline__ void skinny_store(const GemmParams& p, int n_tile0, i
   }
 }
 
-// Grid: (column tiles) x splits workgroups; workgroup b works on column tile
-// b / splits and K split b % splits.
+// Grid: (column tiles) x parts x splits workgroups.  Workgroup b works on K
+// split b % splits of unit u = b / splits: column tile u / parts and rows
+// [16 MF (u % parts), 16 MF (u % parts + 1)) -- activation rows beyond one
+// tile's 16 MF are spread over `parts` workgroups (the two row halves of a
+// column tile run side by side and share its weights in L2).
 template <class C, bool ADD_C>
-__global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(GemmParams p, int splits) {
+__global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(GemmParams p, int splits, int parts) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = blockIdx.x / splits;
-  const int split = blockIdx.x - tile * splits;
+  const int unit = blockIdx.x / splits;
+  const int split = blockIdx.x - unit * splits;
+  const int tile = unit / parts;
+  const int r0 = (unit - tile * parts) * C::ROWS;  // first activation row of this workgroup
   const int n0 = tile * C::COLS;
 
   // this workgroup's K slices, and this wave's quarter of them
@@ -170,13 +176,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
 
   SkinnyLanes g;
   const int l16 = lane & 15, q = lane >> 4;
-  g.ra = make_rsrc(p.A, (int64_t)(p.rows - 1) * p.lda + p.K);
+  g.ra = make_rsrc(p.A + (int64_t)r0 * p.lda, (int64_t)(p.rows - r0 - 1) * p.lda + p.K);
   g.a_voff = l16 * (int)p.lda + 16 * q;
   g.a_step = 16 * (int)p.lda;
   g.rb = make_rsrc(p.B + (int64_t)n0 * p.ldb, (int64_t)(p.N - n0 - 1) * p.ldb + p.K);
   g.b_voff = l16 * (int)p.ldb + 16 * q;
   g.b_step = 16 * (int)p.ldb;
-  g.rsa = make_rsrc(p.sa, ((int64_t)(p.Kb - 1) * p.ld_sa + p.rows) * 4);
+  g.rsa = make_rsrc(p.sa + r0, ((int64_t)(p.Kb - 1) * p.ld_sa + p.rows - r0) * 4);
   g.sa_voff = l16 * 4;
   g.sa_kstep = (int)p.ld_sa * 4;
   g.sb = p.sb + (int64_t)(n0 >> 7) * p.ld_sb;
@@ -257,15 +263,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
 
   if (splits == 1) {
 #pragma unroll
-    for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, n0, wave * C::GPW + y, sum[y], lane);
+    for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, r0, n0, wave * C::GPW + y, sum[y], lane);
     return;
   }
 
   // ---- split K: publish this split's partial, the last arrival adds them ----
-  // partial of (tile, split): [GROUPS][64 lanes] float4, 1 KiB per block
+  // partial of (unit, split): [GROUPS][64 lanes] float4, 1 KiB per block
   const int64_t slot_floats = (int64_t)C::GROUPS * 64 * 4;
   const __amdgpu_buffer_rsrc_t prs =
-      make_rsrc(p.sk_partials + (int64_t)tile * splits * slot_floats,
+      make_rsrc(p.sk_partials + (int64_t)unit * splits * slot_floats,
                 (int64_t)splits * slot_floats * (int64_t)sizeof(float));
 #pragma unroll
   for (int y = 0; y < C::GPW; ++y) {
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   __syncthreads();
   int* last_flag = (int*)(lds + C::LDS - 16);
   if (tid == 0) {
-    const int before = __hip_atomic_fetch_add(p.sk_flags + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int before = __hip_atomic_fetch_add(p.sk_flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     *last_flag = before == splits - 1;
   }
   __syncthreads();
@@ -318,9 +324,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
     }
   }
 #pragma unroll
-  for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, n0, wave * C::GPW + y, t[y], lane);
-  // every workgroup of the tile has counted in: reset for the next launch
-  if (tid == 0) __hip_atomic_store(p.sk_flags + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, r0, n0, wave * C::GPW + y, t[y], lane);
+  // every workgroup of the unit has counted in: reset for the next launch
+  if (tid == 0) __hip_atomic_store(p.sk_flags + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace fg

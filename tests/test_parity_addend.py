@@ -28,6 +28,7 @@ KERNELS = {
     "skinny-2x1": {"FG_SKINNY": "2,1"},
     "skinny-4x1": {"FG_SKINNY": "4,1"},
     "skinny-2x4": {"FG_SKINNY": "2,4"},
+    "skinny-2x2-128rows": {"FG_SKINNY": "2,2,8"},
     "small": {"FG_FORCE_CONFIG": "small"},
     "big-256": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "256"},
     "big-224": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "224"},
@@ -48,8 +49,10 @@ def kernel(request, monkeypatch):
 def _applies(kernel: str, M: int, K: int) -> bool:
     if not kernel.startswith("skinny"):
         return True
-    cf, sp = map(int, KERNELS[kernel]["FG_SKINNY"].split(","))
-    return M <= (64 if cf == 4 else 128) and K // 128 >= sp
+    cf, sp, *rest = map(int, KERNELS[kernel]["FG_SKINNY"].split(","))
+    if rest and rest[0] == 8 and M <= 64:
+        return False  # 128-row fragments only for more than 64 rows
+    return M <= 128 and K // 128 >= sp
 
 
 def grid_addend(rng, M, N) -> np.ndarray:

@@ -1,7 +1,8 @@
 """The dense GEMM for few activation rows (M <= 128: the weight-streaming
 kernel), on the GPU against the CPU oracle.
 
-Every column-tile width and a range of K splits are forced with FG_SKINNY.
+Every column-tile width, a range of K splits and both activation-fragment
+heights are forced with FG_SKINNY.
 The exact regime (integer codes, power-of-two scales) is compared bit for
 bit, which also pins the split-K reduction: a partial added twice or left out
 changes the result.  Random inputs use the oracle's per-element bound."""
@@ -21,8 +22,10 @@ from tests.helpers import (
 
 pytestmark = pytest.mark.gpu
 
-# (column fragments, K splits); 4 column fragments only for M <= 64
-PLANS = ["1,1", "2,1", "4,1", "1,2", "2,4", "1,8", "2,3"]
+# (column fragments, K splits[, activation fragments]): 64-row fragments by
+# default, rows beyond 64 in a second row part; the third field 8 selects
+# 128-row fragments in one part (M > 64 only, at most 2 column fragments)
+PLANS = ["1,1", "2,1", "4,1", "1,2", "2,4", "1,8", "2,3", "2,2,8", "1,3,8"]
 
 
 @pytest.fixture(params=PLANS)
@@ -33,8 +36,11 @@ def plan(request, monkeypatch):
 
 
 def _usable(plan: str, M: int, K: int) -> bool:
-    cf, sp = map(int, plan.split(","))
-    return not (cf == 4 and M > 64) and K // 128 >= sp
+    cf, sp, *rest = map(int, plan.split(","))
+    mf = rest[0] if rest else 4
+    if mf == 8 and (M <= 64 or cf > 2):
+        return False
+    return -(-K // 128) >= sp
 
 
 @pytest.mark.parametrize(
