@@ -15,13 +15,14 @@
 //    row, where the MFMA expects [32q, 32q+32)); a dot product over the slice
 //    does not depend on the order of its terms' pairing, and each load
 //    instruction then covers 64 contiguous bytes of 16 rows.
-//  * A workgroup is four waves on one column tile (16 * CF weight rows, all
-//    16 * MF activation rows), each wave on a quarter of the workgroup's K
-//    range.  The four fp32 partials are added in LDS in wave order.
-//  * When the column tiles alone cannot occupy the device, the K range is
-//    also split over `splits` workgroups.  Their partials go to a workspace
-//    with system-coherent stores; the last workgroup to arrive at a column
-//    tile (an arrival counter) adds them in split order and stores bf16.
+//  * A workgroup is four waves on one column tile (16 * CF weight rows) and
+//    one row part (16 * MF activation rows; more rows go to further parts),
+//    each wave on a quarter of the workgroup's K range.  The four fp32
+//    partials are added in LDS in wave order.
+//  * When the tiles alone cannot occupy the device, the K range is also
+//    split over `splits` workgroups.  Their partials go to a workspace with
+//    system-coherent stores; the last workgroup to arrive at a (tile, part)
+//    unit (an arrival counter) adds them in split order and stores bf16.
 //    Both additions have a fixed order, so results are reproducible.
 #pragma once
 
