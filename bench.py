@@ -113,21 +113,12 @@ def time_steps(problems, steps, warmup):
     return wall, per
 
 
-def time_casts(problems, reps=10):
-    stream = torch.cuda.current_stream()
+def time_casts(problems):
+    """Activation-cast time per problem: GPU time per launch from graph
+    replay, so that a short cast is not charged the host's submit time."""
     out = []
     for pb in problems:
-        pb.cast(stream)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            pb.cast(stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        ms = float(np.median(ts))
+        ms = graph_time(lambda i, pb=pb: pb.cast(torch.cuda.current_stream()))
         nbytes = pb.M * pb.K * 5 + 4 * pb.M * (pb.K // 128)
         out.append({"M": pb.M, "K": pb.K, "us": round(ms * 1e3, 2), "gbs": round(nbytes / ms / 1e6, 1),
                     "pct_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS * 100, 1)})
