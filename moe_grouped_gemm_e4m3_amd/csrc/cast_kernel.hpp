@@ -83,36 +83,65 @@ __device__ __forceinline__ float4 load4(const uint16_t* src) {
                      bf16_to_f32(u.y >> 16));
 }
 
-// One 16-lane group per (row, 128-column group); each lane handles 8 inputs.
+// LPG lanes per (row, 128-column group); each lane makes CH loads of 16 bytes
+// (4 fp32 or 8 bf16 inputs), strided by LPG * 16 bytes, so every load
+// instruction reads whole groups' 16*LPG-byte runs back to back and a lane
+// keeps CH loads in flight.  The factor is the max over the LPG lanes.
 // UE8M0: sa is int32 [ceil(Kb/4)][ld_sa], the factor of K group kb of row m in
 // byte kb % 4 of element [kb / 4][m] (one byte store per group).
 // K tails (K % 128 != 0, K % 16 == 0): the last group holds K % 128 columns;
-// lanes past K load nothing, add nothing to the amax and store nothing.
-template <bool UE8M0, typename T>
+// loads past K are skipped (a load's 4 or 8 columns are all in or all out),
+// add nothing to the amax and store nothing.
+template <bool UE8M0, typename T, int LPG>
 __global__ __launch_bounds__(256) void cast_per_token_kernel(const T* __restrict__ x, int64_t ldx,
                                                              uint8_t* __restrict__ q, void* __restrict__ sa,
                                                              int64_t ld_sa, int M, int K, int64_t total_lanes) {
+  constexpr int VE = 16 / sizeof(T);    // inputs per 16-byte load
+  constexpr int CH = 128 / (LPG * VE);  // loads per lane
+  static_assert(CH >= 1 && CH * LPG * VE == 128, "LPG must split a group into whole 16-byte loads");
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total_lanes) return;  // total_lanes % 16 == 0: a group is all in or all out
+  if (gid >= total_lanes) return;  // total_lanes % LPG == 0: a group is all in or all out
   const int Kb = (K + 127) >> 7;
-  const int64_t grp = gid >> 4;
-  const int sub = (int)(gid & 15);
+  const int64_t grp = gid / LPG;
+  const int sub = (int)(gid & (LPG - 1));
   const int m = (int)(grp / Kb);
   const int kb = (int)(grp - (int64_t)m * Kb);
-  const bool in_k = kb * 128 + sub * 8 < K;  // K % 16 == 0: all 8 columns or none
-  float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-  if (in_k) load8(x + (int64_t)m * ldx + kb * 128 + sub * 8, v0, v1);
-  float amax = absmax4(v1, absmax4(v0, 0.f));
+  const T* src = x + (int64_t)m * ldx;
+  float4 v[CH][VE / 4];
+  float amax = 0.f;
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  for (int j = 0; j < CH; ++j) {
+    const int col = kb * 128 + j * LPG * VE + sub * VE;
+#pragma unroll
+    for (int t = 0; t < VE / 4; ++t) v[j][t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (col < K) {
+      if constexpr (VE == 8)
+        load8(src + col, v[j][0], v[j][VE / 4 - 1]);
+      else
+        v[j][0] = load4(src + col);
+    }
+#pragma unroll
+    for (int t = 0; t < VE / 4; ++t) amax = absmax4(v[j][t], amax);
+  }
+#pragma unroll
+  for (int o = LPG / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, LPG));
   const float s32 = scale_of(amax);
   const uint32_t e = UE8M0 ? ue8m0_of(s32) : 0u;
   const float s = UE8M0 ? ue8m0_value(e) : s32;
-  if (in_k) {
-    uint2 out;
-    out.x = encode4(v0, s);
-    out.y = encode4(v1, s);
-    *(uint2*)(q + (int64_t)m * K + kb * 128 + sub * 8) = out;
+  uint8_t* dst = q + (int64_t)m * K;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int col = kb * 128 + j * LPG * VE + sub * VE;
+    if (col < K) {
+      if constexpr (VE == 8) {
+        uint2 out;
+        out.x = encode4(v[j][0], s);
+        out.y = encode4(v[j][VE / 4 - 1], s);
+        *(uint2*)(dst + col) = out;
+      } else {
+        *(uint32_t*)(dst + col) = encode4(v[j][0], s);
+      }
+    }
   }
   if (sub == 0) {
     if (UE8M0)

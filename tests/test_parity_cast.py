@@ -31,7 +31,8 @@ def special_values(rng, shape):
     return x
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (129, 7168), (1000, 2048)])
+# 1000 x 4352 has 34000 row groups: the launch takes the 8-lane split; the others the 16-lane one.
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (129, 7168), (1000, 2048), (1000, 4352)])
 def test_per_token_bytes(gpu_lib, M, K):
     announce(f"cast per-token {M}x{K}")
     rng = np.random.default_rng(M + K)
@@ -98,7 +99,7 @@ def dev_bf16(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (129, 7168), (257, 1024)])
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (129, 7168), (257, 1024), (600, 7168)])
 def test_per_token_bf16_input_bytes(gpu_lib, M, K):
     """bf16 input quantises exactly as its fp32 widening does in the oracle."""
     announce(f"cast per-token bf16 {M}x{K}")

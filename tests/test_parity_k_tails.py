@@ -174,7 +174,7 @@ def test_masked_tail_exact(gpu_lib):
     assert (bits[~valid] == SENTINEL_BF16).all()
 
 
-@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (129, 176), (300, 7184)])
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (129, 176), (300, 7184), (512, 8208)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_cast_per_token_tail_bytes(gpu_lib, M, K, dtype):
     announce(f"k-tail cast per-token {M}x{K} {dtype}")

@@ -51,7 +51,7 @@ def run(fg, qa, ea, qb, eb, out=None):
     return D
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (37, 640), (256, 1536), (130, 512)])
+@pytest.mark.parametrize("M,K", [(1, 128), (37, 640), (256, 1536), (130, 512), (300, 14336)])
 def test_cast_per_token_bytes(gpu_lib, M, K):
     announce(f"ue8m0 cast per token {M}x{K}")
     A32, _ = synth.dense_problem(M, 8, K, seed=M + K)
