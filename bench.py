@@ -18,10 +18,11 @@ measured with rocprofv3 counters when the committed counter summary matches
 the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
 oracle timed on a bounded sample of output blocks of the same workload.
 ``other_configs`` adds per-shape figures for the small-M dense, contiguous
-and masked workloads, and for the dense M=4096 shapes with power-of-two
-(UE8M0) factors on the scaled MFMA, with an fp32 addend (D = C + A B^T) and
-in the NN and TN storage layouts, each timed beside the plain GEMM, and for
-the K-grouped TN GEMM of weight gradients; skip them with --no-other-configs.
+and masked workloads; for the dense M=4096 shapes and the masked decode with
+power-of-two (UE8M0) factors on the scaled MFMA; for the dense shapes with an
+fp32 addend (D = C + A B^T) and in the NN and TN storage layouts, each timed
+beside the plain GEMM; and for the K-grouped TN GEMM of weight gradients.
+Skip them with --no-other-configs.
 """
 
 from __future__ import annotations
@@ -308,8 +309,23 @@ def other_configs():
         rv = int(np.sum(mask))
         out.append(shape_entry("masked_16x256", (G, Mc, N, K), ms, 2 * rv * N * K, rv * K + G * N * K + 2 * rv * N,
                                "hbm"))
-        del copies, qa, qb, D
+        del copies, qa, qb
         progress(f"masked {G}x{Mc}x{N}x{K}: {ms * 1e3:.2f} us")
+        # the same decode step with power-of-two (UE8M0) factors
+        kb4 = (K // 128 + 3) // 4
+        qa = torch.empty(G, Mc, K, dtype=torch.uint8, device="cuda")
+        sa = torch.empty(G, kb4, fg.aligned_scale_ld(Mc), dtype=torch.int32, device="cuda")[:, :, :Mc]
+        for g in range(G):
+            fg.fp8_cast_per_token_ue8m0(A32[g].cuda(), qa[g], sa[g])
+        qb, sb = fg.fp8_cast_per_block_ue8m0(B32.reshape(G * N, K).cuda())
+        qb, sb = qb.view(G, N, K), sb.view(G, -(-N // 128), kb4)
+        copies = [qb] + [qb.clone() for _ in range(max(1, int(700e6 // (G * N * K))))]
+        ms = graph_time(lambda i: fg.gemm_fp8_grouped_masked_ue8m0(qa, sa, copies[i % len(copies)], sb, mt, D),
+                        launches=10)
+        out.append(shape_entry("masked_16x256_ue8m0", (G, Mc, N, K), ms, 2 * rv * N * K,
+                               rv * K + G * N * K + 2 * rv * N, "hbm"))
+        del copies, qa, qb, D
+        progress(f"masked ue8m0 {G}x{Mc}x{N}x{K}: {ms * 1e3:.2f} us")
     return out
 
 

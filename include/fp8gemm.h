@@ -287,6 +287,28 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
                             uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
 
 /*
+ * Masked grouped GEMM (decode; digest, "Dense ve Grouped GEMM") with
+ * power-of-two factors: gemm_fp8_grouped_masked's layout and row masking,
+ * with the factors of gemm_fp8_nt_ue8m0 packed per group.
+ *   A        device [G, M_cap, K] e4m3, packed
+ *   sa       device int32 [G][Kb4][ld_sa], ld_sa >= M_cap (packed as for gemm_fp8_nt_ue8m0)
+ *   B        device [G, N, K] e4m3, packed
+ *   sb       device int32 [G][Nb][Kb4]
+ *   masked_m device int32 [G]: valid rows of each group
+ *   D        device [G, M_cap, N] bf16, packed
+ *   expected_m  accepted for interface compatibility; not used
+ * Group g computes rows [0, clamp(masked_m[g], 0, M_cap)) as gemm_fp8_nt_ue8m0
+ * computes them; every other row of D[g] is left untouched (bit for bit).
+ * K % 128 == 0, G >= 1.  Allocates nothing; errors as for
+ * gemm_fp8_grouped_masked.
+ */
+fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa,
+                                        const uint8_t* B, const int32_t* sb,
+                                        const int32_t* masked_m,
+                                        uint16_t* D, int G, int M_cap, int N, int K,
+                                        int expected_m, void* stream);
+
+/*
  * Per-token (1 x 128) cast with power-of-two factors: as fp8_cast_per_token,
  * but the fp32 factor max(amax, 1e-4f) / 448 is rounded up to the next power
  * of two 2^(e - 127) (so no code saturates) and e is written as a byte:

@@ -40,6 +40,7 @@ __all__ = [
     "fp8_cast_per_token",
     "fp8_cast_per_block",
     "gemm_fp8_nt_ue8m0",
+    "gemm_fp8_grouped_masked_ue8m0",
     "fp8_cast_per_token_ue8m0",
     "fp8_cast_per_block_ue8m0",
     "empty_activation_scales_ue8m0",
@@ -72,6 +73,7 @@ _SIGNATURES = {
     "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "gemm_fp8_nt_ue8m0": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
+    "gemm_fp8_grouped_masked_ue8m0": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fp8_cast_per_token_ue8m0": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block_ue8m0": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "fp8_cast_per_token_bf16": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
@@ -442,6 +444,35 @@ def gemm_fp8_nt_ue8m0(A, sa, B, sb, D, stream=None):
         "gemm_fp8_nt_ue8m0",
         _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
         _ptr(D), D.stride(0), M, N, K, _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_grouped_masked_ue8m0(A, sa, B, sb, masked_m, D, expected_m: int = 0, stream=None):
+    """Masked M-grouped GEMM with packed power-of-two (UE8M0) factors: sa int32
+    [G, ceil(Kb/4), M_cap] view of a [G, ceil(Kb/4), ld_sa] buffer, sb int32
+    [G, Nb, ceil(Kb/4)]; group g computes rows [0, masked_m[g]), other rows of D untouched."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _i32(sa, "sa"), _i32(sb, "sb")
+    if masked_m.dtype != torch.int32 or not masked_m.is_cuda or not masked_m.is_contiguous():
+        raise TypeError("masked_m must be a contiguous int32 CUDA tensor")
+    if D.dtype != torch.bfloat16 or not D.is_contiguous():
+        raise TypeError("D must be a contiguous bfloat16 CUDA tensor")
+    if not (A.is_contiguous() and B.is_contiguous() and sb.is_contiguous()):
+        raise ValueError("A, B and sb must be contiguous")
+    G, Mc, K = A.shape
+    N = B.shape[1]
+    kb4 = (K // 128 + 3) // 4
+    if sa.dim() != 3 or sa.shape[0] != G or sa.stride(2) != 1 or sa.stride(0) != sa.shape[1] * sa.stride(1):
+        raise ValueError("sa must be a [G, ceil(Kb/4), M_cap] view of a [G, ceil(Kb/4), ld_sa] buffer")
+    if B.shape != (G, N, K) or tuple(D.shape) != (G, Mc, N) or masked_m.shape[0] != G:
+        raise ValueError("shape mismatch")
+    if K and (tuple(sa.shape) != (G, kb4, Mc) or tuple(sb.shape) != (G, (N + 127) // 128, kb4)):
+        raise ValueError("factor shapes must be sa [G, ceil(Kb/4), M_cap] and sb [G, Nb, ceil(Kb/4)]")
+    _call(
+        "gemm_fp8_grouped_masked_ue8m0",
+        _ptr(A), _ptr(sa), sa.stride(1), _ptr(B), _ptr(sb), _ptr(masked_m), _ptr(D),
+        G, Mc, N, K, int(expected_m), _stream(stream),
     )
     return D
 

@@ -304,9 +304,19 @@ fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream
 // M=4096 shapes: 256x224 = 240, 256x160 = 176, 128x256 = 144 (a 128-row tile
 // reuses each weight byte half as often, so it costs more than half a
 // 256-row one).  FG_FORCE_BN=224|160 keeps the older width-only choice.
-int pick_ue8m0_tile(int M, int N) {
+// Masked groups count as `groups` stacks of M rows; they take 256-row tiles
+// only, so that a group's weights stream once (measured on the 16 x 256
+// decode shapes: the 128-row tile was 6-35 % slower than the best 256-row
+// one).  FG_UE8M0_TILE=256x224|256x160|128x256 forces a shape (tuning and
+// tests).
+int pick_ue8m0_tile(int M, int N, int64_t groups, bool masked) {
+  const char* ft = getenv("FG_UE8M0_TILE");
+  if (ft && strcmp(ft, "128x256") == 0) return fg::kUe8m0Tile128x256;
+  if (ft && strcmp(ft, "256x224") == 0) return fg::kUe8m0Tile256x224;
+  if (ft && strcmp(ft, "256x160") == 0) return fg::kUe8m0Tile256x160;
   const char* f = getenv("FG_FORCE_BN");
-  if (f && *f) return pick_bn((M + 255) / 256, N, false) == 160 ? fg::kUe8m0Tile256x160 : fg::kUe8m0Tile256x224;
+  if (f && *f)
+    return pick_bn(groups * ((M + 255) / 256), N, false) == 160 ? fg::kUe8m0Tile256x160 : fg::kUe8m0Tile256x224;
   int cus = 0;
   if (device_cus(&cus) != FG_OK) return fg::kUe8m0Tile256x224;
   if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
@@ -314,9 +324,9 @@ int pick_ue8m0_tile(int M, int N) {
   static const int cost[3] = {240, 176, 144};
   int best = tiles[0];
   int64_t best_cost = -1;
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < (masked ? 2 : 3); ++i) {
     const int bm = fg::ue8m0_tile_bm(tiles[i]), bn = fg::ue8m0_tile_bn(tiles[i]);
-    const int64_t n = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const int64_t n = groups * ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t c = (n + cus - 1) / cus * cost[i];
     if (best_cost < 0 || c < best_cost) {
       best = tiles[i];
@@ -326,21 +336,22 @@ int pick_ue8m0_tile(int M, int N) {
   return best;
 }
 
-fg_status launch_ue8m0(fg::GemmParams& p, int tile, hipStream_t stream, const char* what) {
-  static int occ_cache[3] = {0, 0, 0};
-  int& occ = occ_cache[tile];
-  if (occ == 0) occ = fg::ue8m0_occupancy(tile);
+fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, bool masked, hipStream_t stream,
+                       const char* what) {
+  static int occ_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
+  int& occ = occ_cache[masked ? 1 : 0][tile];
+  if (occ == 0) occ = fg::ue8m0_occupancy(tile, masked);
   const int bm = fg::ue8m0_tile_bm(tile), bn = fg::ue8m0_tile_bn(tile);
   p.tiles_m = (p.rows + bm - 1) / bm;
   p.tiles_n = (p.N + bn - 1) / bn;
-  const int64_t slots = (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t slots = groups * p.tiles_m * p.tiles_n;
   if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
   p.num_tiles = (int)slots;
   p.group_m = raster_band(p.K);
   int64_t grid = 0;
   FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
   print_config(what, p, bm, bn, 512, grid, occ);
-  const hipError_t e = fg::ue8m0_launch(p, tile, grid, stream);
+  const hipError_t e = fg::ue8m0_launch(p, tile, masked, grid, stream);
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
 }
@@ -879,12 +890,44 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   FG_TRY(check_ld(ldb, K, 16, "ldb"));
   FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
   FG_TRY(check_row_bytes(lda, ldb));
-  int tile = pick_ue8m0_tile(M, N);
-  const char* ft = getenv("FG_UE8M0_TILE");
-  if (ft && strcmp(ft, "128x256") == 0) tile = fg::kUe8m0Tile128x256;
-  if (ft && strcmp(ft, "256x224") == 0) tile = fg::kUe8m0Tile256x224;
-  if (ft && strcmp(ft, "256x160") == 0) tile = fg::kUe8m0Tile256x160;
-  return launch_ue8m0(p, tile, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+  return launch_ue8m0(p, pick_ue8m0_tile(M, N, 1, false), 1, false, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+}
+
+fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa, const uint8_t* B,
+                                        const int32_t* sb, const int32_t* masked_m, uint16_t* D, int G, int M_cap,
+                                        int N, int K, int expected_m, void* stream) {
+  g_err.clear();
+  (void)expected_m;
+  if (M_cap < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_cap=%d N=%d K=%d", M_cap, N, K);
+  if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M_cap == 0 || N == 0) return FG_OK;
+  if (M_cap > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_cap or N above 2^30");
+  FG_TRY(check_ptr(D, 2, "D"));
+  FG_TRY(check_ptr(masked_m, 4, "masked_m"));
+  fg::GemmParams p{};
+  p.A = A; p.lda = K; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K;
+  p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = N;
+  p.masked_m = masked_m;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  if (K == 0) {  // no factors are read: the plain kernel writes the zeros of the valid rows
+    using C = CfgDefault;
+    p.tiles_m = (M_cap + C::BM - 1) / C::BM;
+    p.tiles_n = (N + C::BN - 1) / C::BN;
+    const int64_t slots = (int64_t)G * p.tiles_m * p.tiles_n;
+    if (slots > (int64_t)1 << 30) return fail(FG_EUNSUPPORTED, "too many tiles");
+    p.num_tiles = (int)slots;
+    return launch_gemm<C, fg::kMasked>(p, (hipStream_t)stream, "gemm_fp8_grouped_masked_ue8m0");
+  }
+  FG_TRY(check_ptr(A, 16, "A"));
+  FG_TRY(check_ptr(B, 16, "B"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(ld_sa, M_cap, 1, "ld_sa"));
+  FG_TRY(check_row_bytes(K, K));
+  p.kb_factor = (p.Kb + 3) / 4;  // packed words per row of one group's factor arrays
+  return launch_ue8m0(p, pick_ue8m0_tile(M_cap, N, G, true), G, true, (hipStream_t)stream,
+                      "gemm_fp8_grouped_masked_ue8m0");
 }
 
 fg_status fp8_cast_per_token(const float* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa, int M, int K,

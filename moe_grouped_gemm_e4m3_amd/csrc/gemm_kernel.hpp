@@ -61,11 +61,16 @@ struct GemmParams {
   int tiles_m, tiles_n;  // per group
   int num_tiles;         // tile slots walked by the persistent grid
   int group_m;           // raster band height in tiles
+  int kb_factor;         // K extent of one group's factor arrays: 0 = Kb (fp32 factors), ceil(Kb/4) (packed UE8M0)
   // stream-K (dense only): fp32 partial tiles, one slot per workgroup, and
   // one arrival counter per tile (zero between launches)
   float* sk_partials;
   int* sk_flags;
 };
+
+// Group stride, in K groups (fp32 factors) or packed words (UE8M0), of the
+// masked layout's sa and of the grouped layouts' sb.
+__device__ __forceinline__ int64_t factor_kb(const GemmParams& p) { return p.kb_factor > 0 ? p.kb_factor : p.Kb; }
 
 // A value that no kernel writes while this one runs (the masked counts),
 // read through the scalar cache: a vector load would make the wave wait for
@@ -512,7 +517,7 @@ __device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t)
     raster(w - g * per_group, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int valid = min(max(load_invariant(p.masked_m + g), 0), p.rows);
     if (tm * BM >= valid) return false;
-    const int64_t Kb = p.Kb;
+    const int64_t Kb = factor_kb(p);
     t.A = p.A + (int64_t)g * p.rows * p.K;
     t.sa = p.sa + (int64_t)g * Kb * p.ld_sa;
     t.B = p.B + (int64_t)g * p.N * p.K;
@@ -543,7 +548,7 @@ __device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t)
       }
       const int e = lo >= 0 ? lo : hi;
       t.B = p.B + (int64_t)e * p.N * p.K;
-      t.sb = p.sb + (int64_t)e * p.Nb * p.Kb;
+      t.sb = p.sb + (int64_t)e * p.Nb * factor_kb(p);
     }
   }
   t.m0 = tm * BM;
@@ -560,7 +565,7 @@ __device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& i
     t.seg += 1;
     t.half_mask = 2;
     t.B = p.B + (int64_t)t.e_hi * p.N * p.K;
-    t.sb = p.sb + (int64_t)t.e_hi * p.Nb * p.Kb;
+    t.sb = p.sb + (int64_t)t.e_hi * p.Nb * factor_kb(p);
     return;
   }
   for (;;) {
@@ -959,7 +964,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 
 
 // ===========================================================================
-// Power-of-two (UE8M0) factors on the scaled MFMA (dense).  The digest's
+// Power-of-two (UE8M0) factors on the scaled MFMA (dense and masked).  The digest's
 // layout section gives the newer architecture's factors as UE8M0 bytes packed
 // four to an int32.  gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes such a
 // byte per lane for each operand (lane l: operand row l % 16, 32-wide K block
@@ -971,6 +976,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 // in the stage's scale area (the packed word of K groups 4i..4i+3 of each
 // row), the weight factors through the scalar cache.
 //
+// Dense and masked layouts (the masked form takes each group's packed
+// factors at a stride of ceil(Kb/4) words, kb_factor).
 // Built for 256x224, 256x160 and 128x256 tiles.  The accumulators are
 // updated in place in VGPRs; with a 256x256 tile's 128 of them plus the
 // operand fragments the register allocator falls back to copying every
@@ -1030,10 +1037,11 @@ __device__ __forceinline__ void slice_mma_ue8m0(const uint8_t* st, const int (&a
   }
 }
 
-template <class C>
+template <class C, int L>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
+  static_assert(L == kDense || L == kMasked, "power-of-two factors: dense and masked layouts");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 #define FG_STAGE(i) (lds + (i) * C::STAGE)
@@ -1063,8 +1071,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
   Work cur;
   int it = 0;
   cur.w = -1;
-  if (!(local < p.num_tiles && resolve_big<kDense, BM, BN>(p, local, cur)))
-    advance_big<kDense, BM, BN>(p, cur, it, local, grid);
+  if (!(local < p.num_tiles && resolve_big<L, BM, BN>(p, local, cur)))
+    advance_big<L, BM, BN>(p, cur, it, local, grid);
   if (cur.w < 0) return;
 
   int sb_c[2];
@@ -1084,7 +1092,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
   while (cur.w >= 0) {
     Work nxt = cur;
     int it_n = it;
-    advance_big<kDense, BM, BN>(p, nxt, it_n, local, grid);
+    advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
     const bool active = cur.m0 + wm * WM < cur.rows_valid;
     const int tb = second_block_subtile<C>(cur, wn);
 
@@ -1119,7 +1127,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
       for (int tt = 0; tt < SN; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) accf[ms][tt][r] = acc[ms][tt][r];
-    store_tile<C, kDense>(p, cur, accf, FG_STAGE(stage ^ 1), wave, lane);
+    store_tile<C, L>(p, cur, accf, FG_STAGE(stage ^ 1), wave, lane);
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms)
 #pragma unroll

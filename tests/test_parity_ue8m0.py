@@ -1,5 +1,5 @@
 """Power-of-two (UE8M0) factors on the GPU against the CPU oracle: the two
-casts and the dense GEMM on the scaled MFMA.
+casts, and the dense and masked grouped GEMMs on the scaled MFMA.
 
 The casts must match the oracle byte for byte (codes and factor bytes).  The
 GEMM is compared bit for bit in the exact regime -- its factors {1/2, 1, 2}
@@ -158,8 +158,9 @@ def test_gemm_strided_output_and_tails(gpu_lib):
 
 @pytest.mark.parametrize("shape", synth.DENSE_M4096.shapes, ids=lambda s: "x".join(map(str, s)))
 def test_full_size_gpu_cast_sampled(gpu_lib, monkeypatch, shape):
-    """GPU casts + GEMM at the dense M=4096 sizes; sampled rows x column blocks
-    against the oracle on the same codes."""
+    """GPU casts + GEMM at the dense M=4096 sizes; sampled rows x column
+    blocks against the oracle, which quantises those rows and blocks itself
+    (the GPU's codes and factor bytes must equal its own)."""
     monkeypatch.delenv("FG_FORCE_BN", raising=False)
     M, N, K = shape
     announce(f"ue8m0 full size {M}x{N}x{K}")
@@ -170,15 +171,134 @@ def test_full_size_gpu_cast_sampled(gpu_lib, monkeypatch, shape):
     gpu_lib.gemm_fp8_nt_ue8m0(qa_d, sa_d, qb_d, sb_d, D)
     torch.cuda.synchronize()
     Kb = K // 128
-    ea = quant.unpack_ue8m0(sa_d.cpu().numpy(), Kb, axis=0)
-    eb = quant.unpack_ue8m0(sb_d.cpu().numpy(), Kb, axis=1)
+    ea_d = quant.unpack_ue8m0(sa_d.cpu().numpy(), Kb, axis=0)
+    eb_d = quant.unpack_ue8m0(sb_d.cpu().numpy(), Kb, axis=1)
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False)]))
-    qa = qa_d[torch.from_numpy(rows).cuda()].cpu().numpy()
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy()[rows])
+    assert np.array_equal(qa_d[torch.from_numpy(rows).cuda()].cpu().numpy(), qa)
+    assert np.array_equal(ea_d[:, rows], ea)
     for nb in np.unique(np.concatenate([[0, -(-N // 128) - 1], rng.choice(N // 128, 2, replace=False)])):
         cols = slice(nb * 128, min(N, nb * 128 + 128))
-        qb = qb_d[cols].cpu().numpy()
-        X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea[:, rows]), qb, quant.ue8m0_decode(eb[nb:nb + 1]),
-                             with_magnitude=True)
+        qb, eb = quant.quantize_per_block_ue8m0(B32.numpy()[cols])
+        assert np.array_equal(eb_d[nb:nb + 1], eb)
+        X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
         y = bf16_to_f64(D[torch.from_numpy(rows).cuda(), cols])
         assert_close(y, X, S, Kb, f"ue8m0 full size block {nb}")
+
+
+# ---------------------------------------------------------------------------
+# Masked grouped GEMM with UE8M0 factors: each group as the dense definition
+# with factors 2^(e - 127), rows past the group's count untouched.
+
+
+def run_masked(fg, qa, ea, qb, eb, mask):
+    """qa [G, Mc, K], ea bytes [G, Kb, Mc], qb [G, N, K], eb bytes [G, Nb, Kb]."""
+    G, Mc, K = qa.shape
+    N = qb.shape[1]
+    kb4 = (K // 128 + 3) // 4
+    ld = (Mc + 3) // 4 * 4 + 4
+    buf = np.full((G, kb4, ld), -1, np.int32)  # padding never read
+    for g in range(G):
+        buf[g, :, :Mc] = quant.pack_ue8m0(ea[g], axis=0)
+    sa = dev_i32(buf)[:, :, :Mc]
+    sb = dev_i32(np.stack([quant.pack_ue8m0(eb[g], axis=1) for g in range(G)]))
+    D = sentinel_like((G, Mc, N))
+    fg.gemm_fp8_grouped_masked_ue8m0(dev_u8(qa), sa, dev_u8(qb), sb,
+                                     torch.tensor(list(mask), dtype=torch.int32, device="cuda"), D)
+    torch.cuda.synchronize()
+    return D
+
+
+def test_masked_exact_regime_bitwise(gpu_lib, width):
+    """Counts of 0, 1, partial, more than one 128-row tile, the capacity, above
+    it and negative; K = 640 leaves the last packed word half used."""
+    announce(f"ue8m0 masked width {width} exact regime")
+    rng = np.random.default_rng(width)
+    G, Mc, N, K = 7, 200, 300, 640
+    qa, sa, qb, sb = exact_regime(rng, Mc, N, K, groups=(G, G))
+    mask = [200, 0, 33, 130, 1, 999, -5]
+    D = run_masked(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb), mask)
+    X, valid = ogemm.gemm_grouped_masked(qa, sa, qb, sb, mask)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
+def test_masked_random(gpu_lib, width):
+    announce(f"ue8m0 masked width {width} random")
+    G, Mc, N, K = 4, 256, 1024, 1024
+    g = torch.Generator().manual_seed(width)
+    A32 = torch.randn(G, Mc, K, generator=g).numpy()
+    B32 = torch.randn(G, N, K, generator=g).numpy()
+    qs = [quant.quantize_per_token_ue8m0(a) for a in A32]
+    ws = [quant.quantize_per_block_ue8m0(b) for b in B32]
+    qa, ea = np.stack([q for q, _ in qs]), np.stack([e for _, e in qs])
+    qb, eb = np.stack([q for q, _ in ws]), np.stack([e for _, e in ws])
+    mask = [256, 1, 130, 64]
+    D = run_masked(gpu_lib, qa, ea, qb, eb, mask)
+    X, valid, S = ogemm.gemm_grouped_masked(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), mask,
+                                            with_magnitude=True)
+    bits = bf16_bits(D)
+    assert (bits[~valid] == SENTINEL_BF16).all()
+    assert_close(bf16_to_f64(D)[valid], X[valid], S[valid], K // 128, f"ue8m0 masked width {width}")
+
+
+def test_masked_full_equals_dense(gpu_lib, width):
+    """With every count at the capacity each group equals the dense call on
+    its operands bit for bit (same tile shape, same summation order)."""
+    announce(f"ue8m0 masked width {width} vs dense")
+    G, Mc, N, K = 3, 130, 264, 512
+    g = torch.Generator().manual_seed(6)
+    A32 = torch.randn(G, Mc, K, generator=g).numpy()
+    B32 = torch.randn(G, N, K, generator=g).numpy()
+    qs = [quant.quantize_per_token_ue8m0(a) for a in A32]
+    ws = [quant.quantize_per_block_ue8m0(b) for b in B32]
+    qa, ea = np.stack([q for q, _ in qs]), np.stack([e for _, e in qs])
+    qb, eb = np.stack([q for q, _ in ws]), np.stack([e for _, e in ws])
+    Dm = bf16_bits(run_masked(gpu_lib, qa, ea, qb, eb, [Mc] * G))
+    for e in range(G):
+        assert np.array_equal(Dm[e], bf16_bits(run(gpu_lib, qa[e], ea[e], qb[e], eb[e]))), e
+
+
+@pytest.mark.parametrize("shape", synth.MASKED_16x256.shapes, ids=lambda s: "x".join(map(str, s)))
+def test_masked_decode_full_size(gpu_lib, monkeypatch, shape):
+    """16 experts x capacity 256 with the seed-0 counts: GPU casts with UE8M0
+    factors and the masked GEMM; sampled valid rows of every group against the
+    oracle on the same codes, every invalid row untouched."""
+    monkeypatch.delenv("FG_FORCE_BN", raising=False)
+    monkeypatch.delenv("FG_UE8M0_TILE", raising=False)
+    G, Mc, N, K = shape
+    Kb, kb4 = K // 128, (K // 128 + 3) // 4
+    announce(f"ue8m0 masked full-size {G}x{Mc} N={N} K={K}")
+    A32, B32, mask = synth.masked_problem(G, Mc, N, K, seed=0)
+    qa_d, sa_d = gpu_lib.fp8_cast_per_token_ue8m0(A32.cuda().view(G * Mc, K))
+    qa_d = qa_d.view(G, Mc, K)
+    sa_g = torch.empty(G, kb4, Mc, dtype=torch.int32, device="cuda")
+    sa_g.copy_(sa_d.reshape(kb4, G, Mc).permute(1, 0, 2))
+    qb_d, sb_d = gpu_lib.fp8_cast_per_block_ue8m0(B32.cuda().view(G * N, K))
+    qb_d, sb_d = qb_d.view(G, N, K), sb_d.view(G, N // 128, kb4)
+    D = sentinel_like((G, Mc, N))
+    gpu_lib.gemm_fp8_grouped_masked_ue8m0(qa_d, sa_g, qb_d, sb_d, torch.from_numpy(mask).cuda(), D)
+    torch.cuda.synchronize()
+    bits = bf16_bits(D)
+    ea_d = quant.unpack_ue8m0(sa_d.cpu().numpy(), Kb, axis=0).reshape(Kb, G, Mc)
+    eb_d = quant.unpack_ue8m0(sb_d.cpu().numpy().reshape(G * (N // 128), kb4), Kb, axis=1).reshape(G, N // 128, Kb)
+    rng = np.random.default_rng(2)
+    for g in range(G):
+        v = int(mask[g])
+        assert (bits[g, v:] == SENTINEL_BF16).all(), g
+        if v == 0:
+            continue
+        rows = np.unique(np.concatenate([[0, v - 1], rng.choice(v, min(v, 4), replace=False)]))
+        qa, ea = quant.quantize_per_token_ue8m0(A32.numpy()[g, rows])
+        assert np.array_equal(qa_d[g, torch.from_numpy(rows).cuda()].cpu().numpy(), qa)
+        assert np.array_equal(ea_d[:, g, rows], ea)
+        nbs = range(N // 128) if g < 2 else rng.choice(N // 128, 2, replace=False)
+        for nb in nbs:
+            cols = slice(nb * 128, nb * 128 + 128)
+            qb, eb = quant.quantize_per_block_ue8m0(B32.numpy()[g, cols])
+            assert np.array_equal(eb_d[g, nb:nb + 1], eb)
+            X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
+            y = bf16_to_f64(D[g, torch.from_numpy(rows).cuda(), cols])
+            assert_close(y, X, S, Kb, f"ue8m0 masked group {g} block {nb}")
