@@ -18,10 +18,11 @@ measured with rocprofv3 counters when the committed counter summary matches
 the current kernel sources, else null) and a ``cpu_baseline`` object: the CPU
 oracle timed on a bounded sample of output blocks of the same workload.
 ``other_configs`` adds per-shape figures for the small-M dense, contiguous
-and masked workloads; for the dense M=4096 shapes and the masked decode with
-power-of-two (UE8M0) factors on the scaled MFMA; for the dense shapes with an
-fp32 addend (D = C + A B^T) and in the NN and TN storage layouts, each timed
-beside the plain GEMM; and for the K-grouped TN GEMM of weight gradients.
+and masked workloads; for the dense M=4096 shapes, the contiguous GEMM and
+the masked decode with power-of-two (UE8M0) factors on the scaled MFMA; for
+the dense shapes with an fp32 addend (D = C + A B^T) and in the NN and TN
+storage layouts, each timed beside the plain GEMM; and for the K-grouped TN
+GEMM of weight gradients.
 Skip them with --no-other-configs.
 """
 
@@ -289,6 +290,14 @@ def other_configs():
         ts.append(a.elapsed_time(b))
     Mt = idx.shape[0]
     out.append(shape_entry("contiguous_8x4096", (G, rows, N, K), float(np.median(ts)), 2 * Mt * N * K,
+                           Mt * K + G * N * K + 2 * Mt * N, "mfma"))
+    del qa, qb
+    # the same GEMM with power-of-two (UE8M0) factors
+    qa, sa = fg.fp8_cast_per_token_ue8m0(A32.cuda())
+    qb, sb = fg.fp8_cast_per_block_ue8m0(B32.reshape(G * N, K).cuda())
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, -1)
+    ms = event_time(lambda: fg.gemm_fp8_grouped_contiguous_ue8m0(qa, sa, qb, sb, mi, D), reps=5)
+    out.append(shape_entry("contiguous_8x4096_ue8m0", (G, rows, N, K), ms, 2 * Mt * N * K,
                            Mt * K + G * N * K + 2 * Mt * N, "mfma"))
     del A32, B32, qa, qb, D
     progress("contiguous done")

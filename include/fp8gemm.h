@@ -287,6 +287,27 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
                             uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
 
 /*
+ * Contiguous M-grouped GEMM (digest, "Dense ve Grouped GEMM") with
+ * power-of-two factors: gemm_fp8_grouped_contiguous's layout and row mapping,
+ * with the factors of gemm_fp8_nt_ue8m0.
+ *   A          device [M_total, K] e4m3, packed
+ *   sa         device int32 [Kb4][ld_sa], ld_sa >= M_total (packed as for gemm_fp8_nt_ue8m0)
+ *   B          device [G, N, K] e4m3, packed
+ *   sb         device int32 [G][Nb][Kb4]
+ *   m_indices  device int32 [M_total]: expert of each row, -1 = padding row
+ *   D          device [M_total, N] bf16, packed
+ * Row m with m_indices[m] = e in [0, G) is computed with expert e's weights
+ * as gemm_fp8_nt_ue8m0 computes it; padding rows of D are left untouched.
+ * Each 128-row block holds one expert (or padding).  K % 128 == 0,
+ * M_total % 128 == 0, G >= 1.  Allocates nothing; errors as for
+ * gemm_fp8_grouped_contiguous.
+ */
+fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa,
+                                            const uint8_t* B, const int32_t* sb,
+                                            const int32_t* m_indices,
+                                            uint16_t* D, int M_total, int N, int K, int G, void* stream);
+
+/*
  * Masked grouped GEMM (decode; digest, "Dense ve Grouped GEMM") with
  * power-of-two factors: gemm_fp8_grouped_masked's layout and row masking,
  * with the factors of gemm_fp8_nt_ue8m0 packed per group.

@@ -40,6 +40,7 @@ __all__ = [
     "fp8_cast_per_token",
     "fp8_cast_per_block",
     "gemm_fp8_nt_ue8m0",
+    "gemm_fp8_grouped_contiguous_ue8m0",
     "gemm_fp8_grouped_masked_ue8m0",
     "fp8_cast_per_token_ue8m0",
     "fp8_cast_per_block_ue8m0",
@@ -73,6 +74,7 @@ _SIGNATURES = {
     "fp8_cast_per_token": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "gemm_fp8_nt_ue8m0": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
+    "gemm_fp8_grouped_contiguous_ue8m0": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gemm_fp8_grouped_masked_ue8m0": (_I, [_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fp8_cast_per_token_ue8m0": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block_ue8m0": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
@@ -444,6 +446,34 @@ def gemm_fp8_nt_ue8m0(A, sa, B, sb, D, stream=None):
         "gemm_fp8_nt_ue8m0",
         _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
         _ptr(D), D.stride(0), M, N, K, _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_grouped_contiguous_ue8m0(A, sa, B, sb, m_indices, D, stream=None):
+    """Contiguous M-grouped GEMM with packed power-of-two (UE8M0) factors: sa
+    int32 [ceil(Kb/4), M_total] view (row stride ld_sa), sb int32 [G, Nb,
+    ceil(Kb/4)]; row r of A uses expert m_indices[r] (-1 = padding, untouched)."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _i32(sa, "sa"), _i32(sb, "sb")
+    if m_indices.dtype != torch.int32 or not m_indices.is_cuda or not m_indices.is_contiguous():
+        raise TypeError("m_indices must be a contiguous int32 CUDA tensor")
+    if D.dtype != torch.bfloat16 or not D.is_contiguous():
+        raise TypeError("D must be a contiguous bfloat16 CUDA tensor")
+    if not (A.is_contiguous() and B.is_contiguous() and sb.is_contiguous()):
+        raise ValueError("A, B and sb must be contiguous")
+    _unit_inner(sa, "sa")
+    M, K = A.shape
+    G, N, K2 = B.shape
+    kb4 = (K // 128 + 3) // 4
+    if K2 != K or tuple(D.shape) != (M, N) or m_indices.shape[0] != M:
+        raise ValueError("shape mismatch")
+    if K and (tuple(sa.shape) != (kb4, M) or tuple(sb.shape) != (G, (N + 127) // 128, kb4)):
+        raise ValueError("factor shapes must be sa [ceil(Kb/4), M_total] and sb [G, Nb, ceil(Kb/4)]")
+    _call(
+        "gemm_fp8_grouped_contiguous_ue8m0",
+        _ptr(A), _ptr(sa), sa.stride(0), _ptr(B), _ptr(sb), _ptr(m_indices), _ptr(D),
+        M, N, K, G, _stream(stream),
     )
     return D
 

@@ -305,11 +305,11 @@ fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream
 // reuses each weight byte half as often, so it costs more than half a
 // 256-row one).  FG_FORCE_BN=224|160 keeps the older width-only choice.
 // Masked groups count as `groups` stacks of M rows; they take 256-row tiles
-// only, so that a group's weights stream once (measured on the 16 x 256
-// decode shapes: the 128-row tile was 6-35 % slower than the best 256-row
-// one).  FG_UE8M0_TILE=256x224|256x160|128x256 forces a shape (tuning and
-// tests).
-int pick_ue8m0_tile(int M, int N, int64_t groups, bool masked) {
+// only (rows256_only), so that a group's weights stream once (measured on the
+// 16 x 256 decode shapes: the 128-row tile was 6-35 % slower than the best
+// 256-row one).  FG_UE8M0_TILE=256x224|256x160|128x256 forces a shape (tuning
+// and tests).
+int pick_ue8m0_tile(int M, int N, int64_t groups, bool rows256_only) {
   const char* ft = getenv("FG_UE8M0_TILE");
   if (ft && strcmp(ft, "128x256") == 0) return fg::kUe8m0Tile128x256;
   if (ft && strcmp(ft, "256x224") == 0) return fg::kUe8m0Tile256x224;
@@ -324,7 +324,7 @@ int pick_ue8m0_tile(int M, int N, int64_t groups, bool masked) {
   static const int cost[3] = {240, 176, 144};
   int best = tiles[0];
   int64_t best_cost = -1;
-  for (int i = 0; i < (masked ? 2 : 3); ++i) {
+  for (int i = 0; i < (rows256_only ? 2 : 3); ++i) {
     const int bm = fg::ue8m0_tile_bm(tiles[i]), bn = fg::ue8m0_tile_bn(tiles[i]);
     const int64_t n = groups * ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const int64_t c = (n + cus - 1) / cus * cost[i];
@@ -336,11 +336,12 @@ int pick_ue8m0_tile(int M, int N, int64_t groups, bool masked) {
   return best;
 }
 
-fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, bool masked, hipStream_t stream,
+// layout: fg::kDense, kContiguous or kMasked.
+fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, int layout, hipStream_t stream,
                        const char* what) {
-  static int occ_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
-  int& occ = occ_cache[masked ? 1 : 0][tile];
-  if (occ == 0) occ = fg::ue8m0_occupancy(tile, masked);
+  static int occ_cache[4][3] = {};
+  int& occ = occ_cache[layout & 3][tile];
+  if (occ == 0) occ = fg::ue8m0_occupancy(tile, layout);
   const int bm = fg::ue8m0_tile_bm(tile), bn = fg::ue8m0_tile_bn(tile);
   p.tiles_m = (p.rows + bm - 1) / bm;
   p.tiles_n = (p.N + bn - 1) / bn;
@@ -351,7 +352,7 @@ fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, bool masked,
   int64_t grid = 0;
   FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
   print_config(what, p, bm, bn, 512, grid, occ);
-  const hipError_t e = fg::ue8m0_launch(p, tile, masked, grid, stream);
+  const hipError_t e = fg::ue8m0_launch(p, tile, layout, grid, stream);
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
 }
@@ -890,7 +891,43 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   FG_TRY(check_ld(ldb, K, 16, "ldb"));
   FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
   FG_TRY(check_row_bytes(lda, ldb));
-  return launch_ue8m0(p, pick_ue8m0_tile(M, N, 1, false), 1, false, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+  return launch_ue8m0(p, pick_ue8m0_tile(M, N, 1, false), 1, fg::kDense, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
+}
+
+fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa, const uint8_t* B,
+                                            const int32_t* sb, const int32_t* m_indices, uint16_t* D, int M_total,
+                                            int N, int K, int G, void* stream) {
+  g_err.clear();
+  if (M_total < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_total=%d N=%d K=%d", M_total, N, K);
+  if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
+  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (M_total % 128) return fail(FG_EALIGN, "M_total=%d is not a multiple of 128", M_total);
+  if (M_total == 0 || N == 0) return FG_OK;
+  if (M_total > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_total or N above 2^30");
+  FG_TRY(check_ptr(D, 2, "D"));
+  FG_TRY(check_ptr(m_indices, 4, "m_indices"));
+  fg::GemmParams p{};
+  p.A = A; p.lda = K; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K;
+  p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = N;
+  p.m_indices = m_indices;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  if (K == 0) {  // no factors are read: the plain kernel writes the zeros of the mapped rows
+    using C = CfgDefault;
+    p.tiles_m = M_total / C::BM;
+    p.tiles_n = (N + C::BN - 1) / C::BN;
+    p.num_tiles = p.tiles_m * p.tiles_n;
+    return launch_gemm<C, fg::kContiguous>(p, (hipStream_t)stream, "gemm_fp8_grouped_contiguous_ue8m0");
+  }
+  FG_TRY(check_ptr(A, 16, "A"));
+  FG_TRY(check_ptr(B, 16, "B"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(ld_sa, M_total, 1, "ld_sa"));
+  FG_TRY(check_row_bytes(K, K));
+  p.kb_factor = (p.Kb + 3) / 4;  // packed words per row of one expert's weight factors
+  // 256-row tiles: a tile whose halves hold different experts runs as two segments
+  return launch_ue8m0(p, pick_ue8m0_tile(M_total, N, 1, false), 1, fg::kContiguous, (hipStream_t)stream,
+                      "gemm_fp8_grouped_contiguous_ue8m0");
 }
 
 fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa, const uint8_t* B,
@@ -926,7 +963,7 @@ fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int
   FG_TRY(check_ld(ld_sa, M_cap, 1, "ld_sa"));
   FG_TRY(check_row_bytes(K, K));
   p.kb_factor = (p.Kb + 3) / 4;  // packed words per row of one group's factor arrays
-  return launch_ue8m0(p, pick_ue8m0_tile(M_cap, N, G, true), G, true, (hipStream_t)stream,
+  return launch_ue8m0(p, pick_ue8m0_tile(M_cap, N, G, true), G, fg::kMasked, (hipStream_t)stream,
                       "gemm_fp8_grouped_masked_ue8m0");
 }
 

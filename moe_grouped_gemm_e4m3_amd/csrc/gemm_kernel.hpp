@@ -964,7 +964,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 
 
 // ===========================================================================
-// Power-of-two (UE8M0) factors on the scaled MFMA (dense and masked).  The digest's
+// Power-of-two (UE8M0) factors on the scaled MFMA (dense and grouped).  The digest's
 // layout section gives the newer architecture's factors as UE8M0 bytes packed
 // four to an int32.  gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes such a
 // byte per lane for each operand (lane l: operand row l % 16, 32-wide K block
@@ -976,8 +976,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 // in the stage's scale area (the packed word of K groups 4i..4i+3 of each
 // row), the weight factors through the scalar cache.
 //
-// Dense and masked layouts (the masked form takes each group's packed
-// factors at a stride of ceil(Kb/4) words, kb_factor).
+// Dense, contiguous and masked layouts (the grouped forms take each group's
+// packed factors at a stride of ceil(Kb/4) words, kb_factor).
 // Built for 256x224, 256x160 and 128x256 tiles.  The accumulators are
 // updated in place in VGPRs; with a 256x256 tile's 128 of them plus the
 // operand fragments the register allocator falls back to copying every
@@ -1041,7 +1041,6 @@ template <class C, int L>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
-  static_assert(L == kDense || L == kMasked, "power-of-two factors: dense and masked layouts");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 #define FG_STAGE(i) (lds + (i) * C::STAGE)
@@ -1054,6 +1053,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
   const int wn = wave % C::WAVES_N;
   const int l16 = lane & 15;
   const int kq = lane >> 4;
+  const int half = (wm * WM) / 128;  // 128-row half of the tile this wave's rows lie in
 
   int a_off[2], b_off[2];
 #pragma unroll
@@ -1093,7 +1093,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
     Work nxt = cur;
     int it_n = it;
     advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
-    const bool active = cur.m0 + wm * WM < cur.rows_valid;
+    const bool active = (L == kContiguous) ? (((cur.half_mask >> half) & 1) != 0)
+                                           : (cur.m0 + wm * WM < cur.rows_valid);
     const int tb = second_block_subtile<C>(cur, wn);
 
     for (int kb = 0; kb < Kb; ++kb) {
@@ -1120,18 +1121,23 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
       sb_c[1] = sb_n[1];
     }
 
-    float accf[SM][SN][4];
+    // contiguous: a tile whose halves hold different experts runs as two
+    // segments on the same accumulators (each half active in its own) and
+    // is stored after the second
+    if (cur.seg == cur.nseg - 1) {
+      float accf[SM][SN][4];
 #pragma unroll
-    for (int ms = 0; ms < SM; ++ms)
+      for (int ms = 0; ms < SM; ++ms)
 #pragma unroll
-      for (int tt = 0; tt < SN; ++tt)
+        for (int tt = 0; tt < SN; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accf[ms][tt][r] = acc[ms][tt][r];
-    store_tile<C, L>(p, cur, accf, FG_STAGE(stage ^ 1), wave, lane);
+          for (int r = 0; r < 4; ++r) accf[ms][tt][r] = acc[ms][tt][r];
+      store_tile<C, L>(p, cur, accf, FG_STAGE(stage ^ 1), wave, lane);
 #pragma unroll
-    for (int ms = 0; ms < SM; ++ms)
+      for (int ms = 0; ms < SM; ++ms)
 #pragma unroll
-      for (int tt = 0; tt < SN; ++tt) acc[ms][tt] = zero;
+        for (int tt = 0; tt < SN; ++tt) acc[ms][tt] = zero;
+    }
     cur = nxt;
     it = it_n;
   }

@@ -1,5 +1,5 @@
-// ue8m0.hip -- the dense and masked GEMMs with power-of-two (UE8M0) factors,
-// in a translation unit of its own so that it is compiled without the VGPR-form
+// ue8m0.hip -- the dense and grouped GEMMs with power-of-two (UE8M0)
+// factors, in a translation unit of its own so that it is compiled without the VGPR-form
 // MFMA option (see ue8m0_launch.hpp).  The kernel is gemm_fp8_ue8m0_kernel in
 // gemm_kernel.hpp; the C entry point and its checks are in fp8gemm.hip.
 
@@ -41,12 +41,20 @@ hipError_t launch_of(const GemmParams& p, int tile, int64_t grid, hipStream_t st
 
 }  // namespace
 
-int ue8m0_occupancy(int tile, bool masked) {
-  return masked ? occupancy_of<kMasked>(tile) : occupancy_of<kDense>(tile);
+int ue8m0_occupancy(int tile, int layout) {
+  switch (layout) {
+    case kMasked: return occupancy_of<kMasked>(tile);
+    case kContiguous: return occupancy_of<kContiguous>(tile);
+    default: return occupancy_of<kDense>(tile);
+  }
 }
 
-hipError_t ue8m0_launch(const GemmParams& p, int tile, bool masked, int64_t grid, hipStream_t stream) {
-  return masked ? launch_of<kMasked>(p, tile, grid, stream) : launch_of<kDense>(p, tile, grid, stream);
+hipError_t ue8m0_launch(const GemmParams& p, int tile, int layout, int64_t grid, hipStream_t stream) {
+  switch (layout) {
+    case kMasked: return launch_of<kMasked>(p, tile, grid, stream);
+    case kContiguous: return launch_of<kContiguous>(p, tile, grid, stream);
+    default: return launch_of<kDense>(p, tile, grid, stream);
+  }
 }
 
 }  // namespace fg

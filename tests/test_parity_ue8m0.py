@@ -302,3 +302,102 @@ def test_masked_decode_full_size(gpu_lib, monkeypatch, shape):
             X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
             y = bf16_to_f64(D[g, torch.from_numpy(rows).cuda(), cols])
             assert_close(y, X, S, Kb, f"ue8m0 masked group {g} block {nb}")
+
+
+# ---------------------------------------------------------------------------
+# Contiguous grouped GEMM with UE8M0 factors: each row as the dense definition
+# with its expert's weights, padding rows untouched.
+
+
+def run_contig(fg, qa, ea, qb, eb, idx):
+    """qa [M, K], ea bytes [Kb, M], qb [G, N, K], eb bytes [G, Nb, Kb]."""
+    M, N = qa.shape[0], qb.shape[1]
+    G = qb.shape[0]
+    sb = dev_i32(np.stack([quant.pack_ue8m0(eb[g], axis=1) for g in range(G)]))
+    D = sentinel_like((M, N))
+    fg.gemm_fp8_grouped_contiguous_ue8m0(dev_u8(qa), dev_sa_packed(ea), dev_u8(qb), sb,
+                                         torch.from_numpy(np.asarray(idx, np.int32)).cuda(), D)
+    torch.cuda.synchronize()
+    return D
+
+
+def quantize_experts_ue8m0(B32):
+    ws = [quant.quantize_per_block_ue8m0(b) for b in B32]
+    return np.stack([q for q, _ in ws]), np.stack([e for _, e in ws])
+
+
+def test_contig_exact_regime_bitwise(gpu_lib, width):
+    """Expert blocks of 256, 128, 0, 128 and 128 rows (the 256-row tile over
+    rows 256..511 holds two experts and runs as two segments; the last tile is
+    half past M_total); N = 264 leaves a ragged column tile, K = 640 a
+    half-used packed word."""
+    announce(f"ue8m0 contiguous width {width} exact regime")
+    rng = np.random.default_rng(width + 1)
+    idx = synth.contiguous_indices([200, 60, 0, 128, 1], pad_to=128)
+    M, N, K, G = idx.shape[0], 264, 640, 5
+    qa, sa, _, _ = exact_regime(rng, M, N, K)
+    _, _, qb, sb = exact_regime(rng, 1, N, K, groups=(1, G))
+    D = run_contig(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb), idx)
+    X, valid = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, idx)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
+@pytest.mark.parametrize("rows,N,K", [([130, 0, 100, 1], 520, 384), ([384], 136, 1024)])
+def test_contig_random(gpu_lib, width, rows, N, K):
+    announce(f"ue8m0 contiguous width {width} rows={rows} N={N} K={K}")
+    A32, B32, idx = synth.contiguous_problem(rows, N, K, seed=len(rows) + width)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quantize_experts_ue8m0(B32.numpy())
+    D = run_contig(gpu_lib, qa, ea, qb, eb, idx)
+    X, valid, S = ogemm.gemm_grouped_contiguous(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), idx,
+                                                with_magnitude=True)
+    assert (bf16_bits(D)[~valid] == SENTINEL_BF16).all()
+    assert_close(bf16_to_f64(D)[valid], X[valid], S[valid], K // 128, f"ue8m0 contiguous width {width}")
+
+
+def test_contig_equals_dense_per_group(gpu_lib, width):
+    """Each expert's rows equal the dense call on them bit for bit."""
+    announce(f"ue8m0 contiguous width {width} vs dense")
+    A32, B32, idx = synth.contiguous_problem([256, 128, 384], 384, 768, seed=8)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quantize_experts_ue8m0(B32.numpy())
+    Dc = bf16_bits(run_contig(gpu_lib, qa, ea, qb, eb, idx))
+    for e in range(3):
+        rows = np.nonzero(idx == e)[0]
+        assert np.array_equal(Dc[rows], bf16_bits(run(gpu_lib, qa[rows], ea[:, rows], qb[e], eb[e]))), e
+
+
+def test_contig_8_experts_full_size_sampled(gpu_lib, monkeypatch):
+    """8 experts x 4096 rows, N=4096, K=7168 with UE8M0 factors: GPU casts and
+    the grouped GEMM; the oracle quantises sampled rows and column blocks
+    itself and checks the GPU's codes, factor bytes and outputs."""
+    monkeypatch.delenv("FG_FORCE_BN", raising=False)
+    monkeypatch.delenv("FG_UE8M0_TILE", raising=False)
+    G, R, N, K = synth.CONTIGUOUS_8x4096.shapes[0]
+    Kb, kb4 = K // 128, (K // 128 + 3) // 4
+    announce(f"ue8m0 contiguous full-size {G}x{R} N={N} K={K}")
+    A32, B32, idx = synth.contiguous_problem([R] * G, N, K, seed=0)
+    qa_d, sa_d = gpu_lib.fp8_cast_per_token_ue8m0(A32.cuda())
+    qb_d, sb_d = gpu_lib.fp8_cast_per_block_ue8m0(B32.cuda().view(G * N, K))
+    qb_d, sb_d = qb_d.view(G, N, K), sb_d.view(G, N // 128, kb4)
+    D = torch.empty(G * R, N, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.gemm_fp8_grouped_contiguous_ue8m0(qa_d, sa_d, qb_d, sb_d, torch.from_numpy(idx).cuda(), D)
+    torch.cuda.synchronize()
+    ea_d = quant.unpack_ue8m0(sa_d.cpu().numpy(), Kb, axis=0)
+    eb_d = quant.unpack_ue8m0(sb_d.cpu().numpy().reshape(G * (N // 128), kb4), Kb, axis=1).reshape(G, N // 128, Kb)
+    rng = np.random.default_rng(1)
+    blocks = [0, N // 128 - 1, int(rng.integers(1, N // 128 - 1))]
+    for e in range(G):
+        rows = np.sort(rng.choice(np.arange(e * R, (e + 1) * R), 6, replace=False))
+        qa, ea = quant.quantize_per_token_ue8m0(A32.numpy()[rows])
+        assert np.array_equal(qa_d[torch.from_numpy(rows).cuda()].cpu().numpy(), qa)
+        assert np.array_equal(ea_d[:, rows], ea)
+        Dr = D[torch.from_numpy(rows).cuda()]
+        for nb in blocks:
+            cols = slice(nb * 128, nb * 128 + 128)
+            qb, eb = quant.quantize_per_block_ue8m0(B32.numpy()[e, cols])
+            assert np.array_equal(eb_d[e, nb:nb + 1], eb)
+            X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
+            assert_close(bf16_to_f64(Dr[:, cols]), X, S, Kb, f"ue8m0 expert {e} block {nb}")
