@@ -133,39 +133,41 @@ def ue8m0_decode(b) -> np.ndarray:
 def quantize_per_token_ue8m0(x) -> tuple[np.ndarray, np.ndarray]:
     """1x128 quantisation with power-of-two factors.
 
-    Returns (q uint8 [M, K], UE8M0 bytes uint8 [K/128, M]) -- K-group-major,
-    unpacked (see pack_ue8m0)."""
+    A partial last K group (K % 128 != 0) takes its factor from its own
+    columns, as in quantize_per_token.
+    Returns (q uint8 [M, K], UE8M0 bytes uint8 [ceil(K/128), M]) --
+    K-group-major, unpacked (see pack_ue8m0)."""
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
-    Kb = K // GROUP
-    xg = x.reshape(M, Kb, GROUP)
+    xp = _pad_k(x)
+    Kb = xp.shape[1] // GROUP
+    xg = xp.reshape(M, Kb, GROUP)
     amax = np.abs(xg).max(axis=2) if M else np.zeros((0, Kb), np.float32)
     e = ue8m0_round_up(_scale_from_amax(amax))  # [M, Kb]
-    q = _encode_scaled(xg, ue8m0_decode(e)[:, :, None]).reshape(M, K)
-    return q, np.ascontiguousarray(e.T)
+    q = _encode_scaled(xg, ue8m0_decode(e)[:, :, None]).reshape(M, Kb * GROUP)[:, :K]
+    return np.ascontiguousarray(q), np.ascontiguousarray(e.T)
 
 
 def quantize_per_block_ue8m0(w) -> tuple[np.ndarray, np.ndarray]:
     """128x128 quantisation with power-of-two factors.
 
-    Returns (q uint8 [N, K], UE8M0 bytes uint8 [ceil(N/128), K/128])."""
+    The last row and column blocks may be partial (N % 128, K % 128), each
+    with its own factor, as in quantize_per_block.
+    Returns (q uint8 [N, K], UE8M0 bytes uint8 [ceil(N/128), ceil(K/128)])."""
     w = np.asarray(w, dtype=np.float32)
     N, K = w.shape
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
-    Kb = K // GROUP
+    wp = _pad_k(w)
+    Kb = wp.shape[1] // GROUP
     Nb = -(-N // GROUP)
-    q = np.empty((N, K), dtype=np.uint8)
+    q = np.empty((N, Kb * GROUP), dtype=np.uint8)
     eb = np.empty((Nb, Kb), dtype=np.uint8)
     for nb in range(Nb):
         rows = slice(nb * GROUP, min(N, (nb + 1) * GROUP))
-        blk = w[rows].reshape(-1, Kb, GROUP)
+        blk = wp[rows].reshape(-1, Kb, GROUP)
         e = ue8m0_round_up(_scale_from_amax(np.abs(blk).max(axis=(0, 2))))
         eb[nb] = e
-        q[rows] = _encode_scaled(blk, ue8m0_decode(e)[None, :, None]).reshape(-1, K)
-    return q, eb
+        q[rows] = _encode_scaled(blk, ue8m0_decode(e)[None, :, None]).reshape(-1, Kb * GROUP)
+    return np.ascontiguousarray(q[:, :K]), eb
 
 
 def pack_ue8m0(b, axis: int) -> np.ndarray:

@@ -609,6 +609,36 @@ def test_ue8m0_per_block_tail_and_gemm_definition():
     assert np.allclose(X, a @ b.T, rtol=1e-12, atol=1e-12)
 
 
+def test_ue8m0_k_tail_quantisers_on_their_own_columns():
+    """K % 128 != 0 with power-of-two factors: the partial last group's factor
+    is the smallest power of two at or above max(amax, 1e-4)/448 over its own
+    columns (amax from torch), its codes torch's RNE of x / s; the full groups
+    equal the quantisation of the first 128 columns alone."""
+    A, B = synth.dense_problem(5, 130, 208, seed=9)
+    x, w = A.numpy(), B.numpy()
+    q, e = quant.quantize_per_token_ue8m0(x)
+    assert q.shape == (5, 208) and e.shape == (2, 5)
+    tail = torch.from_numpy(x[:, 128:])
+    s32 = (torch.clamp(tail.abs().amax(dim=1), min=torch.tensor(1e-4, dtype=torch.float32)) / 448.0).numpy()
+    s = quant.ue8m0_decode(e[1])
+    assert (s >= s32).all() and (s / 2 < s32).all()
+    ref = (tail / torch.from_numpy(s)[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q[:, 128:], ref)
+    q0, e0 = quant.quantize_per_token_ue8m0(x[:, :128])
+    assert np.array_equal(q[:, :128], q0) and np.array_equal(e[:1], e0)
+    qb, eb = quant.quantize_per_block_ue8m0(w)
+    assert qb.shape == (130, 208) and eb.shape == (2, 2)
+    for nb, rows in [(0, slice(0, 128)), (1, slice(128, 130))]:
+        blk = torch.from_numpy(w[rows, 128:])
+        s32 = float(max(blk.abs().max().item(), 1e-4)) / 448.0
+        sbk = float(quant.ue8m0_decode(eb[nb, 1]))
+        assert sbk >= np.float32(s32) and sbk / 2 < np.float32(s32)
+        refb = (blk / sbk).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(qb[rows, 128:], refb)
+    qb0, eb0 = quant.quantize_per_block_ue8m0(w[:, :128])
+    assert np.array_equal(qb[:, :128], qb0) and np.array_equal(eb[:, :1], eb0)
+
+
 def test_bf16_widening_matches_torch():
     """bf16 -> fp32 is exact: every pattern against torch's conversion."""
     bits = np.arange(1 << 16, dtype=np.uint16)
