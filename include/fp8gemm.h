@@ -21,8 +21,9 @@
  * K tails.  The digest leaves K % 128 != 0 open.  Reading taken here: K must
  * be a multiple of 16 (the 16-byte row granularity of the operand loads); the
  * last K group is then partial and holds the K % 128 remaining columns, with
- * its own factors (the casts take its amax over those columns alone).  The
- * power-of-two (UE8M0) calls and the K-grouped GEMM keep K % 128 == 0.
+ * its own factors (the casts take its amax over those columns alone).  This
+ * holds for the power-of-two (UE8M0) calls too; the K-grouped GEMM keeps
+ * K % 128 == 0.
  *
  * Scale layouts.  Activation scales are per (row, 128-wide K group) and are
  * stored K-group-major ("transposed", as the digest requires for the LHS
@@ -279,8 +280,9 @@ fg_status fp8_cast_per_block_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, fl
  * The matrix cores apply the factors (gfx950's scaled FP8 MFMA) and add each
  * 128-deep slice into fp32 accumulators; the output is the same definition
  * as gemm_fp8_nt with factors 2^(e - 127).  Factor bytes 0 and 255 are not
- * meaningful inputs (the casts below never write them).  K % 128 == 0,
- * lda, ldb <= 4 MiB.  Allocates nothing; errors as for gemm_fp8_nt.
+ * meaningful inputs (the casts below never write them).  K % 16 == 0 (a
+ * partial last K group when K % 128 != 0), lda, ldb <= 4 MiB.  Allocates
+ * nothing; errors as for gemm_fp8_nt.
  */
 fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, int64_t ld_sa,
                             const uint8_t* B, int64_t ldb, const int32_t* sb,
@@ -298,7 +300,7 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
  *   D          device [M_total, N] bf16, packed
  * Row m with m_indices[m] = e in [0, G) is computed with expert e's weights
  * as gemm_fp8_nt_ue8m0 computes it; padding rows of D are left untouched.
- * Each 128-row block holds one expert (or padding).  K % 128 == 0,
+ * Each 128-row block holds one expert (or padding).  K % 16 == 0,
  * M_total % 128 == 0, G >= 1.  Allocates nothing; errors as for
  * gemm_fp8_grouped_contiguous.
  */
@@ -320,7 +322,7 @@ fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa,
  *   expected_m  accepted for interface compatibility; not used
  * Group g computes rows [0, clamp(masked_m[g], 0, M_cap)) as gemm_fp8_nt_ue8m0
  * computes them; every other row of D[g] is left untouched (bit for bit).
- * K % 128 == 0, G >= 1.  Allocates nothing; errors as for
+ * K % 16 == 0, G >= 1.  Allocates nothing; errors as for
  * gemm_fp8_grouped_masked.
  */
 fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa,

@@ -420,7 +420,7 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
 
 def empty_activation_scales_ue8m0(rows: int, K: int, device="cuda") -> torch.Tensor:
     """A [ceil(Kb/4), rows] view of a padded int32 buffer for packed UE8M0 activation factors."""
-    kb4 = (K // 128 + 3) // 4
+    kb4 = (-(-K // 128) + 3) // 4
     return torch.empty(kb4, aligned_scale_ld(rows), dtype=torch.int32, device=device)[:, :rows]
 
 
@@ -437,7 +437,7 @@ def gemm_fp8_nt_ue8m0(A, sa, B, sb, D, stream=None):
         raise ValueError("sb must be contiguous [Nb, ceil(Kb/4)]")
     M, K = A.shape
     N = B.shape[0]
-    kb4 = (K // 128 + 3) // 4
+    kb4 = (-(-K // 128) + 3) // 4
     if B.shape[1] != K or tuple(D.shape) != (M, N):
         raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)}")
     if K and (tuple(sa.shape) != (kb4, M) or tuple(sb.shape) != ((N + 127) // 128, kb4)):
@@ -465,7 +465,7 @@ def gemm_fp8_grouped_contiguous_ue8m0(A, sa, B, sb, m_indices, D, stream=None):
     _unit_inner(sa, "sa")
     M, K = A.shape
     G, N, K2 = B.shape
-    kb4 = (K // 128 + 3) // 4
+    kb4 = (-(-K // 128) + 3) // 4
     if K2 != K or tuple(D.shape) != (M, N) or m_indices.shape[0] != M:
         raise ValueError("shape mismatch")
     if K and (tuple(sa.shape) != (kb4, M) or tuple(sb.shape) != (G, (N + 127) // 128, kb4)):
@@ -492,7 +492,7 @@ def gemm_fp8_grouped_masked_ue8m0(A, sa, B, sb, masked_m, D, expected_m: int = 0
         raise ValueError("A, B and sb must be contiguous")
     G, Mc, K = A.shape
     N = B.shape[1]
-    kb4 = (K // 128 + 3) // 4
+    kb4 = (-(-K // 128) + 3) // 4
     if sa.dim() != 3 or sa.shape[0] != G or sa.stride(2) != 1 or sa.stride(0) != sa.shape[1] * sa.stride(1):
         raise ValueError("sa must be a [G, ceil(Kb/4), M_cap] view of a [G, ceil(Kb/4), ld_sa] buffer")
     if B.shape != (G, N, K) or tuple(D.shape) != (G, Mc, N) or masked_m.shape[0] != G:
@@ -533,7 +533,7 @@ def fp8_cast_per_block_ue8m0(w, q=None, sb=None, stream=None):
     if q is None:
         q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if sb is None:
-        sb = torch.empty((N + 127) // 128, (K // 128 + 3) // 4, dtype=torch.int32, device=w.device)
+        sb = torch.empty((N + 127) // 128, (-(-K // 128) + 3) // 4, dtype=torch.int32, device=w.device)
     q = _fp8(q, "q")
     sb = _i32(sb, "sb")
     if not (q.is_contiguous() and sb.is_contiguous()):

@@ -339,9 +339,10 @@ int pick_ue8m0_tile(int M, int N, int64_t groups, bool rows256_only) {
 // layout: fg::kDense, kContiguous or kMasked.
 fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, int layout, hipStream_t stream,
                        const char* what) {
-  static int occ_cache[4][3] = {};
-  int& occ = occ_cache[layout & 3][tile];
-  if (occ == 0) occ = fg::ue8m0_occupancy(tile, layout);
+  static int occ_cache[2][4][3] = {};
+  const bool ktail = (p.K & 127) != 0;
+  int& occ = occ_cache[ktail ? 1 : 0][layout & 3][tile];
+  if (occ == 0) occ = fg::ue8m0_occupancy(tile, layout, ktail);
   const int bm = fg::ue8m0_tile_bm(tile), bn = fg::ue8m0_tile_bn(tile);
   p.tiles_m = (p.rows + bm - 1) / bm;
   p.tiles_n = (p.N + bn - 1) / bn;
@@ -867,7 +868,7 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
                             void* stream) {
   g_err.clear();
   if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || N == 0) return FG_OK;
   if (M > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M or N above 2^30");
   FG_TRY(check_ptr(D, 2, "D"));
@@ -875,7 +876,7 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   fg::GemmParams p{};
   p.A = A; p.lda = lda; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = ldd;
-  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros
     using C = CfgDefault;
     p.tiles_m = (M + C::BM - 1) / C::BM;
@@ -900,7 +901,7 @@ fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa,
   g_err.clear();
   if (M_total < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_total=%d N=%d K=%d", M_total, N, K);
   if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M_total % 128) return fail(FG_EALIGN, "M_total=%d is not a multiple of 128", M_total);
   if (M_total == 0 || N == 0) return FG_OK;
   if (M_total > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_total or N above 2^30");
@@ -910,7 +911,7 @@ fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa,
   p.A = A; p.lda = K; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = N;
   p.m_indices = m_indices;
-  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros of the mapped rows
     using C = CfgDefault;
     p.tiles_m = M_total / C::BM;
@@ -937,7 +938,7 @@ fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int
   (void)expected_m;
   if (M_cap < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M_cap=%d N=%d K=%d", M_cap, N, K);
   if (G <= 0) return fail(FG_EINVAL, "G=%d must be positive", G);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M_cap == 0 || N == 0) return FG_OK;
   if (M_cap > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_cap or N above 2^30");
   FG_TRY(check_ptr(D, 2, "D"));
@@ -946,7 +947,7 @@ fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int
   p.A = A; p.lda = K; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = N;
   p.masked_m = masked_m;
-  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = K / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros of the valid rows
     using C = CfgDefault;
     p.tiles_m = (M_cap + C::BM - 1) / C::BM;
@@ -985,7 +986,7 @@ fg_status fp8_cast_per_token_ue8m0(const float* x, int64_t ldx, uint8_t* q, int3
                                    void* stream) {
   g_err.clear();
   if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || K == 0) return FG_OK;
   FG_TRY(check_ptr(x, 16, "x"));
   FG_TRY(check_ptr(q, 8, "q"));
@@ -999,13 +1000,13 @@ fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int3
                                    void* stream) {
   g_err.clear();
   if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
-  if (K % 128) return fail(FG_EALIGN, "K=%d is not a multiple of 128", K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (N == 0 || K == 0) return FG_OK;
   FG_TRY(check_ptr(w, 16, "w"));
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<true, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
                      ldw, q, (void*)sb, N, K);

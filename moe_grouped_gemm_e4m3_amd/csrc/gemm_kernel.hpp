@@ -977,7 +977,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
 // row), the weight factors through the scalar cache.
 //
 // Dense, contiguous and masked layouts (the grouped forms take each group's
-// packed factors at a stride of ceil(Kb/4) words, kb_factor).
+// packed factors at a stride of ceil(Kb/4) words, kb_factor).  KTAIL: K % 128
+// != 0, the partial last slice's chunks past column K load as zeros, as in
+// the fp32-factor kernel.
 // Built for 256x224, 256x160 and 128x256 tiles.  The accumulators are
 // updated in place in VGPRs; with a 256x256 tile's 128 of them plus the
 // operand fragments the register allocator falls back to copying every
@@ -1037,7 +1039,7 @@ __device__ __forceinline__ void slice_mma_ue8m0(const uint8_t* st, const int (&a
   }
 }
 
-template <class C, int L>
+template <class C, int L, bool KTAIL>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
@@ -1077,7 +1079,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
 
   int sb_c[2];
   load_sb_ue8m0<C>(p, cur, 0, wn, sb_c);
-  issue_slice_loads<C>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane, 0);
+  issue_slice_loads<C, KTAIL>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -1100,9 +1102,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
     for (int kb = 0; kb < Kb; ++kb) {
       const bool last = kb + 1 == Kb;
       if (!last)
-        issue_slice_loads<C>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, (kb + 1) >> 2);
+        issue_slice_loads<C, KTAIL>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, (kb + 1) >> 2);
       else if (nxt.w >= 0)
-        issue_slice_loads<C>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, 0);
+        issue_slice_loads<C, KTAIL>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane, 0);
       if (active) slice_mma_ue8m0<C>(FG_STAGE(stage), a_off, b_off, FG_SA(stage), wm, l16, kb, sb_c, tb, acc);
       // the next slice's weight factors (scalar loads) only after the MFMAs,
       // so that the slice's LDS waits can be partial

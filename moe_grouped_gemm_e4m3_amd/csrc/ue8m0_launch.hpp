@@ -19,13 +19,13 @@ enum { kUe8m0Tile256x224 = 0, kUe8m0Tile256x160 = 1, kUe8m0Tile128x256 = 2 };
 constexpr int ue8m0_tile_bm(int tile) { return tile == kUe8m0Tile128x256 ? 128 : 256; }
 constexpr int ue8m0_tile_bn(int tile) { return tile == kUe8m0Tile256x160 ? 160 : tile == kUe8m0Tile128x256 ? 256 : 224; }
 
-// Workgroups per CU of the kernel for a tile shape and layout (kDense,
-// kContiguous or kMasked).
-__attribute__((visibility("hidden"))) int ue8m0_occupancy(int tile, int layout);
+// Workgroups per CU of the kernel for a tile shape, layout (kDense,
+// kContiguous or kMasked) and K (ktail: K % 128 != 0).
+__attribute__((visibility("hidden"))) int ue8m0_occupancy(int tile, int layout, bool ktail);
 
 // Launch on `grid` workgroups; p.tiles_m, tiles_n, num_tiles and group_m set
 // (grouped layouts: p.kb_factor = ceil(Kb/4); masked: num_tiles covers all
-// groups).
+// groups).  K % 128 != 0 takes the build that clips the last slice at K.
 __attribute__((visibility("hidden"))) hipError_t ue8m0_launch(const GemmParams& p, int tile, int layout,
                                                               int64_t grid, hipStream_t stream);
 

@@ -161,9 +161,9 @@ def test_cast_argument_errors(lib):
 
 
 def test_k_tail_alignment_rules(lib):
-    """K % 16 == 0 is enough for the fp32-factor calls (a partial last K
-    group); the power-of-two-factor calls keep K % 128 == 0; K % 16 != 0
-    fails everywhere.  Checked before anything touches a device."""
+    """K % 16 == 0 is enough for the fp32- and power-of-two-factor calls (a
+    partial last K group); K % 16 != 0 fails everywhere.  Checked before
+    anything touches a device."""
     for K in (8, 100, 1028):
         assert dense(lib, K=K, lda=512, ldb=512) == FG_EALIGN
         assert "multiple of 16" in lib.fg_last_error().decode()
@@ -171,9 +171,12 @@ def test_k_tail_alignment_rules(lib):
         assert masked(lib, K=K) == FG_EALIGN
         assert lib.fp8_cast_per_token(P16, 512, P8, P4, 64, 64, K, None) == FG_EALIGN
         assert lib.fp8_cast_per_block(P16, 512, P4, P4, 130, K, None) == FG_EALIGN
-    for K in (16, 176, 304):
         assert lib.gemm_fp8_nt_ue8m0(P16, 512, P4, 64, P16, 512, P4, P16, 256, 64, 256, K, None) == FG_EALIGN
-        assert "multiple of 128" in lib.fg_last_error().decode()
+        assert "multiple of 16" in lib.fg_last_error().decode()
+        assert lib.gemm_fp8_grouped_contiguous_ue8m0(P16, P4, 256, P16, P4, P4, P16, 256, 256, K, 2,
+                                                     None) == FG_EALIGN
+        assert lib.gemm_fp8_grouped_masked_ue8m0(P16, P4, 64, P16, P4, P4, P16, 2, 64, 256, K, 0,
+                                                 None) == FG_EALIGN
         assert lib.fp8_cast_per_token_ue8m0(P16, 512, P8, P4, 64, 64, K, None) == FG_EALIGN
         assert lib.fp8_cast_per_block_ue8m0(P16, 512, P4, P4, 130, K, None) == FG_EALIGN
 

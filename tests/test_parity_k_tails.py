@@ -226,3 +226,97 @@ def test_cast_then_gemm_tail(gpu_lib):
     qa, sa, qb, sb = quantize_dense(A32, B32)
     X, S = ogemm.gemm_nt(qa, sa, qb, sb, with_magnitude=True)
     assert_close(bf16_to_f64(D), X, S, kb_of(K), "cast+gemm tail")
+
+
+# ---------------------------------------------------------------------------
+# Power-of-two (UE8M0) factors with a K tail: the casts byte for byte, the
+# dense, contiguous and masked GEMMs bit for bit in the exact regime (for each
+# tile shape) and within the bound on N(0,1) inputs.
+
+from tests.test_parity_ue8m0 import (  # noqa: E402
+    run as run_ue8m0, run_contig as run_contig_ue8m0, run_masked as run_masked_ue8m0, to_bytes,
+)
+
+UE8M0_TILES = ["256x224", "256x160", "128x256"]
+
+
+@pytest.mark.parametrize("M,K", [(5, 48), (129, 176), (300, 7184), (512, 8208)])
+def test_ue8m0_cast_per_token_tail_bytes(gpu_lib, M, K):
+    announce(f"k-tail ue8m0 cast per-token {M}x{K}")
+    rng = np.random.default_rng(M + K + 1)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, -1] *= np.float32(40.0)
+    q_ref, e_ref = quant.quantize_per_token_ue8m0(x)
+    q, sa = gpu_lib.fp8_cast_per_token_ue8m0(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert tuple(sa.shape) == ((kb_of(K) + 3) // 4, M)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(quant.unpack_ue8m0(sa.cpu().numpy(), kb_of(K), axis=0), e_ref)
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (130, 176), (256, 7184)])
+def test_ue8m0_cast_per_block_tail_bytes(gpu_lib, N, K):
+    announce(f"k-tail ue8m0 cast per-block {N}x{K}")
+    rng = np.random.default_rng(N + K + 2)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    w[:, -3] *= np.float32(40.0)
+    q_ref, e_ref = quant.quantize_per_block_ue8m0(w)
+    q, sb = gpu_lib.fp8_cast_per_block_ue8m0(torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert tuple(sb.shape) == (-(-N // 128), (kb_of(K) + 3) // 4)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(quant.unpack_ue8m0(sb.cpu().numpy(), kb_of(K), axis=1), e_ref)
+
+
+@pytest.mark.parametrize("tile", UE8M0_TILES)
+@pytest.mark.parametrize("K", [48, 1040])
+def test_ue8m0_dense_tail_exact_regime_bitwise(gpu_lib, monkeypatch, tile, K):
+    monkeypatch.setenv("FG_UE8M0_TILE", tile)
+    M, N = 300, 520
+    announce(f"k-tail ue8m0 dense {tile} {M}x{N}x{K}")
+    rng = np.random.default_rng(K + len(tile))
+    qa, sa, qb, sb = exact_regime(rng, M, N, K)
+    D = run_ue8m0(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb))
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_nt(qa, sa, qb, sb)))
+
+
+def test_ue8m0_dense_tail_random(gpu_lib):
+    M, N, K = 257, 1030, 1360
+    announce(f"k-tail ue8m0 dense random {M}x{N}x{K}")
+    A32, B32 = synth.dense_problem(M, N, K, seed=17)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quant.quantize_per_block_ue8m0(B32.numpy())
+    D = run_ue8m0(gpu_lib, qa, ea, qb, eb)
+    X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
+    assert_close(bf16_to_f64(D), X, S, kb_of(K), "ue8m0 tail random")
+
+
+@pytest.mark.parametrize("tile", UE8M0_TILES)
+def test_ue8m0_contiguous_tail_exact_regime_bitwise(gpu_lib, monkeypatch, tile):
+    monkeypatch.setenv("FG_UE8M0_TILE", tile)
+    announce(f"k-tail ue8m0 contiguous {tile}")
+    rng = np.random.default_rng(11 + len(tile))
+    idx = synth.contiguous_indices([200, 60, 128, 1], pad_to=128)
+    M, N, K, G = idx.shape[0], 264, 1040, 4
+    qa, sa, _, _ = exact_regime(rng, M, N, K)
+    _, _, qb, sb = exact_regime(rng, 1, N, K, groups=(1, G))
+    D = run_contig_ue8m0(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb), idx)
+    X, valid = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, idx)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
+@pytest.mark.parametrize("tile", UE8M0_TILES)
+def test_ue8m0_masked_tail_exact_regime_bitwise(gpu_lib, monkeypatch, tile):
+    monkeypatch.setenv("FG_UE8M0_TILE", tile)
+    announce(f"k-tail ue8m0 masked {tile}")
+    rng = np.random.default_rng(13 + len(tile))
+    G, Mc, N, K = 4, 200, 300, 176
+    qa, sa, qb, sb = exact_regime(rng, Mc, N, K, groups=(G, G))
+    mask = [200, 0, 130, 7]
+    D = run_masked_ue8m0(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb), mask)
+    X, valid = ogemm.gemm_grouped_masked(qa, sa, qb, sb, mask)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
