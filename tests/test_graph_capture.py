@@ -38,8 +38,8 @@ def _masked_operands(G, Mc, N, K, seed):
 
 @pytest.mark.parametrize("fresh_stream", [False, True], ids=["warm-stream", "fresh-stream"])
 def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
-    """Dense few-row (split K), dense large-tile and masked calls captured
-    together.  On the fresh stream nothing has run before the capture, so the
+    """Dense few-row (split K), dense large-tile and masked calls, and the
+    power-of-two-factor dense, masked and contiguous calls, captured together.  On the fresh stream nothing has run before the capture, so the
     split-K path must fall back to no split rather than allocate."""
     monkeypatch.delenv("FG_FORCE_CONFIG", raising=False)
     monkeypatch.delenv("FG_SKINNY", raising=False)
@@ -54,12 +54,27 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
     gen = torch.Generator(device="cuda").manual_seed(6)
     qa_u, sa_u = gpu_lib.fp8_cast_per_token_ue8m0(torch.randn(512, 1024, device="cuda", generator=gen))
     qb_u, sb_u = gpu_lib.fp8_cast_per_block_ue8m0(torch.randn(4096, 1024, device="cuda", generator=gen))
+    # grouped GEMMs with power-of-two factors: masked (the masked problem's
+    # counts) and contiguous with a K tail (K = 1040)
+    G, Mc, Nm, Km = 4, 256, 512, 768
+    kb4 = (Km // 128 + 3) // 4
+    qa_m, sa_m = gpu_lib.fp8_cast_per_token_ue8m0(torch.randn(G * Mc, Km, device="cuda", generator=gen))
+    sa_m = sa_m.reshape(kb4, G, Mc).permute(1, 0, 2).contiguous()
+    qb_m, sb_m = gpu_lib.fp8_cast_per_block_ue8m0(torch.randn(G * Nm, Km, device="cuda", generator=gen))
+    masked_u = (qa_m.view(G, Mc, Km), sa_m, qb_m.view(G, Nm, Km), sb_m.view(G, Nm // 128, kb4))
+    idx = torch.from_numpy(synth.contiguous_indices([200, 60, 128], pad_to=128)).cuda()
+    Mt, Nc, Kc = idx.shape[0], 256, 1040
+    qa_c, sa_c = gpu_lib.fp8_cast_per_token_ue8m0(torch.randn(Mt, Kc, device="cuda", generator=gen))
+    qb_c, sb_c = gpu_lib.fp8_cast_per_block_ue8m0(torch.randn(3 * Nc, Kc, device="cuda", generator=gen))
+    contig_u = (qa_c, sa_c, qb_c.view(3, Nc, Kc), sb_c.view(3, Nc // 128, -1))
     outs = [torch.empty(64, 2112, dtype=torch.bfloat16, device="cuda"),
             torch.empty(512, 1024, dtype=torch.bfloat16, device="cuda"),
             torch.empty(4, 256, 512, dtype=torch.bfloat16, device="cuda"),
             torch.empty(64, 2112, dtype=torch.bfloat16, device="cuda"),
             torch.empty(512, 1024, dtype=torch.bfloat16, device="cuda"),
-            torch.empty(512, 4096, dtype=torch.bfloat16, device="cuda")]
+            torch.empty(512, 4096, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(G, Mc, Nm, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(Mt, Nc, dtype=torch.bfloat16, device="cuda")]
 
     def run_all(stream=None):
         gpu_lib.gemm_fp8_nt(*small, outs[0], stream=stream)
@@ -68,6 +83,8 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
         gpu_lib.gemm_fp8_nt(*tail_small, outs[3], stream=stream)
         gpu_lib.gemm_fp8_nt(*tail_large, outs[4], stream=stream)
         gpu_lib.gemm_fp8_nt_ue8m0(qa_u, sa_u, qb_u, sb_u, outs[5], stream=stream)
+        gpu_lib.gemm_fp8_grouped_masked_ue8m0(*masked_u, masked[4], outs[6], stream=stream)
+        gpu_lib.gemm_fp8_grouped_contiguous_ue8m0(*contig_u, idx, outs[7], stream=stream)
 
     s = torch.cuda.Stream()
     if not fresh_stream:
@@ -91,6 +108,7 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
     monkeypatch.delenv("FG_SKINNY", raising=False)
     ref = [bf16_bits(o) for o in outs]
     valid = np.arange(256)[None, :] < masked[4].cpu().numpy()[:, None]
+    mapped = idx.cpu().numpy() >= 0
 
     for rep in range(4):
         for o in outs:
@@ -104,6 +122,8 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
         assert np.array_equal(got[2][valid], ref[2][valid]), rep
         for i in (3, 4, 5):
             assert np.array_equal(got[i], ref[i]), (rep, i)
+        assert np.array_equal(got[6][valid], ref[6][valid]), rep
+        assert np.array_equal(got[7][mapped], ref[7][mapped]), rep
         run_all()  # eager work between replays (default plan)
         torch.cuda.synchronize()
 
