@@ -348,6 +348,20 @@ fg_status fp8_cast_per_token_ue8m0(const float* x, int64_t ldx, uint8_t* q, int3
 fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int32_t* sb,
                                    int N, int K, void* stream);
 
+/*
+ * The two power-of-two-factor casts from BF16 inputs (raw bf16 bit patterns),
+ * widened to fp32 exactly first, as fp8_cast_per_token_bf16 /
+ * fp8_cast_per_block_bf16 do:
+ *   x   device bf16 [M, K], row stride ldx elements (ldx >= K, ldx % 8 == 0), 16-byte aligned
+ *   w   device bf16 [N, K], row stride ldw elements (ldw >= K, ldw % 4 == 0), 16-byte aligned
+ * Other arguments, outputs and errors as for fp8_cast_per_token_ue8m0 /
+ * fp8_cast_per_block_ue8m0.
+ */
+fg_status fp8_cast_per_token_ue8m0_bf16(const uint16_t* x, int64_t ldx, uint8_t* q, int32_t* sa, int64_t ld_sa,
+                                        int M, int K, void* stream);
+fg_status fp8_cast_per_block_ue8m0_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, int32_t* sb,
+                                        int N, int K, void* stream);
+
 /* Row alignment of each expert segment in the contiguous layout: 128. */
 int fg_get_mk_alignment_for_contiguous_layout(void);
 

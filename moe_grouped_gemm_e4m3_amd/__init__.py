@@ -80,6 +80,8 @@ _SIGNATURES = {
     "fp8_cast_per_block_ue8m0": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "fp8_cast_per_token_bf16": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
     "fp8_cast_per_block_bf16": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
+    "fp8_cast_per_token_ue8m0_bf16": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _P]),
+    "fp8_cast_per_block_ue8m0_bf16": (_I, [_P, _I64, _P, _P, _I, _I, _P]),
     "fg_get_mk_alignment_for_contiguous_layout": (_I, []),
     "fg_set_num_cus": (None, [_I]),
     "fg_get_num_cus": (_I, []),
@@ -508,8 +510,9 @@ def gemm_fp8_grouped_masked_ue8m0(A, sa, B, sb, masked_m, D, expected_m: int = 0
 
 
 def fp8_cast_per_token_ue8m0(x, q=None, sa=None, stream=None):
-    """1x128 cast with power-of-two factors -> (q uint8 [M, K], sa int32 [ceil(Kb/4), M] view)."""
-    x = _f32(x, "x")
+    """1x128 cast of fp32 or bf16 activations with power-of-two factors ->
+    (q uint8 [M, K], sa int32 [ceil(Kb/4), M] view)."""
+    x, sfx = _f32_or_bf16(x, "x")
     _unit_inner(x, "x")
     M, K = x.shape
     if q is None:
@@ -521,13 +524,14 @@ def fp8_cast_per_token_ue8m0(x, q=None, sa=None, stream=None):
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     _unit_inner(sa, "sa")
-    _call("fp8_cast_per_token_ue8m0", _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
+    _call("fp8_cast_per_token_ue8m0" + sfx, _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
     return q, sa
 
 
 def fp8_cast_per_block_ue8m0(w, q=None, sb=None, stream=None):
-    """128x128 cast with power-of-two factors -> (q uint8 [N, K], sb int32 [Nb, ceil(Kb/4)])."""
-    w = _f32(w, "w")
+    """128x128 cast of fp32 or bf16 weights with power-of-two factors ->
+    (q uint8 [N, K], sb int32 [Nb, ceil(Kb/4)])."""
+    w, sfx = _f32_or_bf16(w, "w")
     _unit_inner(w, "w")
     N, K = w.shape
     if q is None:
@@ -538,7 +542,7 @@ def fp8_cast_per_block_ue8m0(w, q=None, sb=None, stream=None):
     sb = _i32(sb, "sb")
     if not (q.is_contiguous() and sb.is_contiguous()):
         raise ValueError("q and sb must be contiguous")
-    _call("fp8_cast_per_block_ue8m0", _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
+    _call("fp8_cast_per_block_ue8m0" + sfx, _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
     return q, sb
 
 

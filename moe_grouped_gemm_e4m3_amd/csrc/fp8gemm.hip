@@ -1015,6 +1015,39 @@ fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int3
   return FG_OK;
 }
 
+fg_status fp8_cast_per_token_ue8m0_bf16(const uint16_t* x, int64_t ldx, uint8_t* q, int32_t* sa, int64_t ld_sa,
+                                        int M, int K, void* stream) {
+  g_err.clear();
+  if (M < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d K=%d", M, K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
+  if (M == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(x, 16, "x"));
+  FG_TRY(check_ptr(q, 8, "q"));
+  FG_TRY(check_ptr(sa, 4, "sa"));
+  FG_TRY(check_ld(ldx, K, 8, "ldx"));
+  FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+  return launch_cast_per_token<true>(x, ldx, q, (void*)sa, ld_sa, M, K, stream, "fp8_cast_per_token_ue8m0_bf16");
+}
+
+fg_status fp8_cast_per_block_ue8m0_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, int32_t* sb, int N, int K,
+                                        void* stream) {
+  g_err.clear();
+  if (N < 0 || K < 0) return fail(FG_EINVAL, "negative size N=%d K=%d", N, K);
+  if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
+  if (N == 0 || K == 0) return FG_OK;
+  FG_TRY(check_ptr(w, 16, "w"));
+  FG_TRY(check_ptr(q, 4, "q"));
+  FG_TRY(check_ptr(sb, 4, "sb"));
+  FG_TRY(check_ld(ldw, K, 4, "ldw"));
+  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
+  if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
+  hipLaunchKernelGGL((fg::cast_per_block_kernel<true, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, w, ldw, q, (void*)sb, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "fp8_cast_per_block_ue8m0_bf16 launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
 fg_status fp8_cast_per_token_bf16(const uint16_t* x, int64_t ldx, uint8_t* q, float* sa, int64_t ld_sa, int M, int K,
                                   void* stream) {
   g_err.clear();

@@ -401,3 +401,33 @@ def test_contig_8_experts_full_size_sampled(gpu_lib, monkeypatch):
             assert np.array_equal(eb_d[e, nb:nb + 1], eb)
             X, S = ogemm.gemm_nt(qa, quant.ue8m0_decode(ea), qb, quant.ue8m0_decode(eb), with_magnitude=True)
             assert_close(bf16_to_f64(Dr[:, cols]), X, S, Kb, f"ue8m0 expert {e} block {nb}")
+
+
+# ---------------------------------------------------------------------------
+# BF16 inputs: widened to fp32 exactly, then cast as that fp32 value is.
+
+from tests.test_parity_cast import bf16_values, dev_bf16  # noqa: E402
+from oracle import e4m3  # noqa: E402
+
+
+@pytest.mark.parametrize("M,K", [(3, 384), (128, 7184), (600, 7168)])
+def test_cast_per_token_bf16_input_bytes(gpu_lib, M, K):
+    """600 x 7168 has 33600 row groups (the 8-lane split); 7184 a K tail."""
+    announce(f"ue8m0 cast per token bf16 {M}x{K}")
+    bits = bf16_values(np.random.default_rng(M + K + 5), (M, K))
+    q_ref, e_ref = quant.quantize_per_token_ue8m0(e4m3.bf16_bits_to_f32(bits))
+    q, sa = gpu_lib.fp8_cast_per_token_ue8m0(dev_bf16(bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(quant.unpack_ue8m0(sa.cpu().numpy(), -(-K // 128), axis=0), e_ref)
+
+
+@pytest.mark.parametrize("N,K", [(136, 176), (2112, 512)])
+def test_cast_per_block_bf16_input_bytes(gpu_lib, N, K):
+    announce(f"ue8m0 cast per block bf16 {N}x{K}")
+    bits = bf16_values(np.random.default_rng(N + K + 6), (N, K))
+    q_ref, e_ref = quant.quantize_per_block_ue8m0(e4m3.bf16_bits_to_f32(bits))
+    q, sb = gpu_lib.fp8_cast_per_block_ue8m0(dev_bf16(bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(quant.unpack_ue8m0(sb.cpu().numpy(), -(-K // 128), axis=1), e_ref)
