@@ -926,9 +926,13 @@ fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa,
   FG_TRY(check_ld(ld_sa, M_total, 1, "ld_sa"));
   FG_TRY(check_row_bytes(K, K));
   p.kb_factor = (p.Kb + 3) / 4;  // packed words per row of one expert's weight factors
-  // 256-row tiles: a tile whose halves hold different experts runs as two segments
-  return launch_ue8m0(p, pick_ue8m0_tile(M_total, N, 1, false), 1, fg::kContiguous, (hipStream_t)stream,
-                      "gemm_fp8_grouped_contiguous_ue8m0");
+  // 256-row tiles: a tile whose halves hold different experts runs as two
+  // segments.  The widest tile: a prefill GEMM runs many rounds of tiles, so
+  // per-tile reuse outweighs the rounding of the last round (measured at
+  // 8 x 4096 rows, N=4096, K=7168: 256x224 849-968 us, 256x160 935-974,
+  // 128x256 1116-1127).  FG_UE8M0_TILE still forces a shape.
+  const int tile = getenv("FG_UE8M0_TILE") ? pick_ue8m0_tile(M_total, N, 1, false) : fg::kUe8m0Tile256x224;
+  return launch_ue8m0(p, tile, 1, fg::kContiguous, (hipStream_t)stream, "gemm_fp8_grouped_contiguous_ue8m0");
 }
 
 fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int64_t ld_sa, const uint8_t* B,
