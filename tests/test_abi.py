@@ -195,3 +195,23 @@ def test_python_wrappers_reject_cpu_tensors():
     a = torch.zeros(4, 128, dtype=torch.uint8)
     with pytest.raises((TypeError, ValueError)):
         fg.gemm_fp8_nt(a, torch.zeros(1, 4), a, torch.zeros(1, 1), torch.zeros(4, 4, dtype=torch.bfloat16))
+
+
+def test_python_ue8m0_wrappers_reject_cpu_tensors():
+    """The power-of-two-factor wrappers check dtypes and devices before any
+    call into the library (CPU tensors never reach a kernel)."""
+    import torch
+
+    a = torch.zeros(2, 128, 128, dtype=torch.uint8)
+    i32 = torch.zeros(2, 1, 128, dtype=torch.int32)
+    mask = torch.zeros(2, dtype=torch.int32)
+    d = torch.zeros(2, 128, 128, dtype=torch.bfloat16)
+    with pytest.raises((TypeError, ValueError)):
+        fg.gemm_fp8_grouped_masked_ue8m0(a, i32, a, torch.zeros(2, 1, 1, dtype=torch.int32), mask, d)
+    with pytest.raises((TypeError, ValueError)):
+        fg.gemm_fp8_grouped_contiguous_ue8m0(a[0], i32[0], a, torch.zeros(2, 1, 1, dtype=torch.int32),
+                                             torch.zeros(128, dtype=torch.int32), d[0])
+    with pytest.raises((TypeError, ValueError)):
+        fg.fp8_cast_per_token_ue8m0(torch.zeros(4, 128, dtype=torch.bfloat16))
+    with pytest.raises((TypeError, ValueError)):
+        fg.fp8_cast_per_block_ue8m0(torch.zeros(4, 128))
