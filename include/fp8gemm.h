@@ -33,13 +33,13 @@
  * Ownership.  Every pointer named "device" is device memory owned by the
  * caller; the library never frees or retains caller pointers.  Each GEMM or
  * cast call only enqueues kernels on `stream` (a hipStream_t; NULL is the
- * default stream) and returns.  The one exception to "allocates nothing" is
- * the split-K workspace of gemm_fp8_nt (see there): 16 MiB of fp32 partials
- * and 64 KiB of counters, allocated by the first call that needs it on a
- * (device, stream) pair and kept until the process ends.  A call whose stream
- * is being captured into a HIP graph never allocates (it takes a path without
- * a workspace), so every call is safe to capture; the masked form, whose
- * counts the host never learns, is made for that.
+ * default stream) and returns: no call allocates device memory or
+ * synchronises, so every call can be captured into a HIP graph (the masked
+ * form, whose counts the host never learns, is made for that).  Scratch
+ * memory, where a plan needs it, comes from the caller as a `workspace`
+ * argument (gemm_fp8_nt_ws, the NN/TN/TT layouts, the K-grouped GEMM).  The
+ * one exception is the opt-in debug check FG_CHECK_DEVICE (see the grouped
+ * calls), which reads a result back.
  *
  * Errors.  Preconditions that the host can check are checked before anything
  * is launched; on failure the call returns the status, launches nothing, and
@@ -48,7 +48,8 @@
  * N == 0, M_total == 0, M_cap == 0) returns FG_OK without launching.  A
  * launch failure returns FG_EHIP with the HIP error string.  Preconditions on
  * device-resident metadata (expert indices, masks) are documented per call
- * and are not checked (checking would need a host synchronisation).
+ * and are not checked by default (checking needs a host synchronisation);
+ * the debug mode FG_CHECK_DEVICE=1 checks them (see the grouped calls).
  */
 #ifndef FP8GEMM_H
 #define FP8GEMM_H
@@ -78,22 +79,47 @@ typedef enum {
  * M, N >= 0 arbitrary; K % 16 == 0 (a partial last K group when K % 128 != 0).
  * K == 0 writes D = 0 (sa, sb may then be NULL).
  * Only D[0:M, 0:N] is written.  lda, ldb <= 4 MiB (FG_EUNSUPPORTED beyond).
- * Few rows (M <= 128): a weight-streaming kernel that may split K over
- * several workgroups; their fp32 partials meet in the library's workspace for
- * (device, stream) and are added in a fixed order (results do not depend on
- * the CU cap).  Calls on one stream are ordered; calls on different streams
- * use different workspaces.
- * Optional stream-K (environment FG_STREAM_K=1; off by default): the K
- * slices of all tiles are split evenly over the workgroups and fp32 partial
- * tiles are exchanged through a workspace that the library allocates on the
- * first such call for a (device, stream) pair (64 MiB of partials plus
- * 256 KiB of counters) and keeps until the process ends.  That first call
- * must not be inside a HIP graph capture; later calls allocate nothing.
- * Different streams get different workspaces.
+ * Few rows (M <= 128) run a weight-streaming kernel; this call never splits
+ * its K range over workgroups (gemm_fp8_nt_ws does, with a workspace).  The
+ * kernel and plan depend only on the arguments and the device (not on the CU
+ * cap, earlier calls or graph capture), so results are bit-for-bit
+ * reproducible.  Allocates nothing.
  */
 fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const uint8_t* B, int64_t ldb, const float* sb,
                       uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
+
+/*
+ * gemm_fp8_nt with a caller's workspace, which lets the few-row plan
+ * (M <= 128) split the K range over several workgroups when the column tiles
+ * alone cannot occupy the device (decode shapes); the fp32 partials of the
+ * splits meet in the workspace and are added in a fixed split order, so the
+ * result is reproducible and does not depend on the workspace's history.
+ *   workspace        device, 256-byte aligned, or NULL (then the plan of gemm_fp8_nt)
+ *   workspace_bytes  >= fg_nt_workspace_bytes(M, N, K) (FG_EINVAL otherwise); any
+ *                    size works for a shape whose plan does not split (need 0)
+ * Workspace contract: its first 64 KiB are arrival counters and must be zero
+ * before the workspace is first used (e.g. allocate it zero-filled); every
+ * call leaves them zero.  The rest holds partials and needs no
+ * initialisation.  A workspace is in use until the call's work on `stream`
+ * has finished; calls that may run at the same time (other streams, a graph
+ * replayed on another stream) must use different workspaces.  Everything
+ * else as gemm_fp8_nt; the output equals gemm_fp8_nt's within the stated
+ * tolerance (bit for bit when the plan does not split).  Allocates nothing.
+ */
+fg_status gemm_fp8_nt_ws(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                         const uint8_t* B, int64_t ldb, const float* sb,
+                         uint16_t* D, int64_t ldd, int M, int N, int K,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes gemm_fp8_nt_ws needs for (M, N, K) on the current device:
+ * 0 when its plan does not split K, else 64 KiB of counters plus the
+ * partials.  -1 for a negative size or when the device cannot be queried. */
+int64_t fg_nt_workspace_bytes(int M, int N, int K);
+
+/* Upper bound of fg_nt_workspace_bytes over every shape (8 MiB + 64 KiB):
+ * a workspace of this size serves every call. */
+int64_t fg_nt_workspace_max_bytes(void);
 
 /*
  * Dense NT GEMM with an addend, D = C + A . B^T (the digest, "GEMM arayuzu ve
@@ -103,9 +129,8 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
  *       16-byte aligned get vector loads); read only, may not overlap D
  *   every other argument as in gemm_fp8_nt.
  * C is added to the fp32 accumulator once, after the last K slice, and the sum
- * is rounded to BF16 once.  K == 0 writes D = bf16(C).  Same kernels, plans
- * and workspace rules as gemm_fp8_nt, except that the optional stream-K path
- * is never taken.  C == NULL is FG_EINVAL when M, N > 0.
+ * is rounded to BF16 once.  K == 0 writes D = bf16(C).  Same kernels and
+ * plans as gemm_fp8_nt (no K split).  C == NULL is FG_EINVAL when M, N > 0.
  */
 fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                         const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
@@ -193,6 +218,12 @@ int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total);
  * every non-negative index is the same value e < G.  The block is computed
  * against B[e], where e is the largest index in the block; rows whose index
  * is not e (padding) are left untouched; a block of padding only is skipped.
+ * Debug mode: with the environment variable FG_CHECK_DEVICE=1 a check kernel
+ * validates m_indices first and the host reads its result back (this
+ * synchronises the stream, and the call returns FG_EINVAL while the stream
+ * is being captured); an index outside [-1, G), or one that differs from the
+ * other non-negative indices of its 128-row block, returns FG_EINVAL naming
+ * the row, and the GEMM is not launched.
  */
 fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t ld_sa,
                                       const uint8_t* B, const float* sb,
@@ -213,6 +244,9 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
  *               the plan does not use it (measured: the tile width chosen from G, M_cap and N is best)
  * Group g computes rows [0, clamp(masked_m[g], 0, M_cap)); every other row of
  * D[g] is left untouched (bit for bit).  K % 16 == 0, G >= 1.
+ * Debug mode (FG_CHECK_DEVICE=1, as for the contiguous form): a count
+ * outside [0, M_cap], which the unchecked call clamps, returns FG_EINVAL
+ * naming the group, and the GEMM is not launched.
  */
 fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_sa,
                                   const uint8_t* B, const float* sb,
@@ -367,10 +401,8 @@ int fg_get_mk_alignment_for_contiguous_layout(void);
 
 /* Cap on the compute units the GEMM kernels spread their persistent workgroups
  * over (the digest's set_num_sms); 0 (the default) means all of them.
- * Results are bit-for-bit reproducible for a fixed cap.  With whole-tile
- * scheduling (the default) they do not depend on the cap at all; with the
- * optional stream-K split the cap sets the split and so the fp32 summation
- * order.  Process-wide, not thread-safe against concurrent launches. */
+ * Results do not depend on the cap (every tile is computed whole by one
+ * workgroup).  Process-wide, not thread-safe against concurrent launches. */
 void fg_set_num_cus(int n);
 int fg_get_num_cus(void);
 

@@ -28,6 +28,9 @@ __all__ = [
     "load_library",
     "library_path",
     "gemm_fp8_nt",
+    "gemm_fp8_nt_unsplit",
+    "nt_workspace_bytes",
+    "nt_workspace",
     "gemm_fp8_nt_c",
     "gemm_fp8_nn",
     "gemm_fp8_tn",
@@ -61,6 +64,9 @@ _I64 = ctypes.c_int64
 _I = ctypes.c_int
 _SIGNATURES = {
     "gemm_fp8_nt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
+    "gemm_fp8_nt_ws": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P, _I64, _P]),
+    "fg_nt_workspace_bytes": (_I64, [_I, _I, _I]),
+    "fg_nt_workspace_max_bytes": (_I64, []),
     "gemm_fp8_nt_c": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P]),
     "gemm_fp8_nn": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
     "gemm_fp8_tn": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P]),
@@ -178,8 +184,67 @@ def empty_activation_scales(rows: int, K: int, device="cuda", groups: int | None
     return torch.empty(groups, Kb, ld, dtype=torch.float32, device=device)[:, :, :rows]
 
 
-def gemm_fp8_nt(A, sa, B, sb, D, stream=None):
-    """D[M,N] = bf16(A . B^T) with 1x128 activation and 128x128 weight scales."""
+def nt_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes gemm_fp8_nt's K-split plan needs for (M, N, K) (0: no split)."""
+    n = load_library().fg_nt_workspace_bytes(M, N, K)
+    if n < 0:
+        raise ValueError(f"sizes {(M, N, K)} not accepted, or the device cannot be queried")
+    return n
+
+
+# Split-K workspaces of gemm_fp8_nt, one per (device, stream): zero-filled
+# once (the library keeps the counters at zero between calls) and kept for the
+# life of the process, so a graph that captured one keeps a valid buffer.
+_NT_WS: dict = {}
+
+
+def nt_workspace(device=None, stream=None) -> torch.Tensor:
+    """The cached split-K workspace of `stream` (current stream by default),
+    created zero-filled by torch's allocator on first use."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = (dev.index, _stream(stream))
+    ws = _NT_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(load_library().fg_nt_workspace_max_bytes(), dtype=torch.uint8, device=dev)
+        _NT_WS[key] = ws
+    return ws
+
+
+def gemm_fp8_nt(A, sa, B, sb, D, stream=None, workspace=None):
+    """D[M,N] = bf16(A . B^T) with 1x128 activation and 128x128 weight scales.
+
+    Calls gemm_fp8_nt_ws: for few rows (M <= 128) the K range may be split
+    over workgroups, with the partials in `workspace` (a uint8 CUDA tensor
+    whose first 64 KiB are zero; by default the cached one of the stream)."""
+    A, B = _fp8(A, "A"), _fp8(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    if D.dtype != torch.bfloat16 or not D.is_cuda:
+        raise TypeError("D must be a bfloat16 CUDA tensor")
+    for t, n in ((A, "A"), (B, "B"), (sa, "sa"), (D, "D")):
+        _unit_inner(t, n)
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous [Nb, Kb]")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(D.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)}")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is None and M <= 128 and nt_workspace_bytes(M, N, K) > 0:
+        workspace = nt_workspace(D.device, stream)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous uint8 CUDA tensor")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    _call(
+        "gemm_fp8_nt_ws",
+        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        _ptr(D), D.stride(0), M, N, K, ws_ptr, ws_bytes, _stream(stream),
+    )
+    return D
+
+
+def gemm_fp8_nt_unsplit(A, sa, B, sb, D, stream=None):
+    """gemm_fp8_nt's C entry point itself: never splits K, needs no workspace."""
     A, B = _fp8(A, "A"), _fp8(B, "B")
     sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
     if D.dtype != torch.bfloat16 or not D.is_cuda:

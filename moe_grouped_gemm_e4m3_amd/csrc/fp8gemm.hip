@@ -2,8 +2,9 @@
 //
 // Host side: argument validation (nothing is launched on a failed check),
 // tile-configuration choice, persistent-grid sizing and asynchronous launch
-// on the caller's stream.  The only device memory the library holds is the
-// partial-sum workspace of the split-K kernels (see Workspace below).
+// on the caller's stream.  The library allocates no device memory: the
+// few-row split-K's exchange buffers come in a caller's workspace, and the
+// only device data it owns is a result word of the opt-in metadata check.
 // The API mirrors the operations of the DeepGEMM digest (GeekNews topic
 // 19459): "GEMM arayuzu ve yerlesim kisitlari" (NT dense GEMM, fp32 scale
 // factors with a transposed LHS layout), "Dense ve Grouped GEMM" (contiguous
@@ -27,6 +28,7 @@
 #include "ue8m0_launch.hpp"
 #include "skinny_kernel.hpp"
 #include "transpose_kernel.hpp"
+#include "check_kernel.hpp"
 
 #define FG_TRY(x)                    \
   do {                               \
@@ -52,10 +54,17 @@ fg_status fail(fg_status st, const char* fmt, ...) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// ceil(x / 128) without int overflow near INT_MAX
+int ceil128(int x) { return (int)(((int64_t)x + 127) / 128); }
+
+// Result word of the opt-in metadata check (one copy per device).
+__device__ int g_check_word[2];
+
 // Per-device properties, looked up once per device.
 struct DeviceInfo {
   int cus = 0;
   bool ok = false;
+  int* check_word = nullptr;  // device address of this device's g_check_word
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
@@ -81,6 +90,91 @@ fg_status device_cus(int* cus) {
 bool env_flag(const char* name) {
   const char* v = getenv(name);
   return v && *v && strcmp(v, "0") != 0;
+}
+
+bool stream_capturing(void* stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
+// ---------------------------------------------------------------------------
+// Debug mode (environment FG_CHECK_DEVICE=1): before a grouped GEMM is
+// launched, a check kernel validates its device-resident row mapping and the
+// host reads the result back, which synchronises the stream.  A bad value is
+// reported as FG_EINVAL and the GEMM is not launched, so an out-of-range
+// expert index never reaches the weight addressing.  Not allowed while the
+// stream is being captured.
+
+fg_status check_word_ptr(int** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FG_EHIP, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev[dev].check_word) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_check_word));
+    if (e != hipSuccess) return fail(FG_EHIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_dev[dev].check_word = (int*)ptr;
+  }
+  *out = g_dev[dev].check_word;
+  return FG_OK;
+}
+
+// Runs `check` (a launch on `stream` that records into the word) and returns
+// the first offending position, or -1.
+template <class F>
+fg_status run_device_check(void* stream, const char* what, F check, int* bad) {
+  *bad = -1;
+  if (stream_capturing(stream))
+    return fail(FG_EINVAL, "%s: FG_CHECK_DEVICE reads results back and cannot run while the stream is captured", what);
+  int* word = nullptr;
+  FG_TRY(check_word_ptr(&word));
+  hipLaunchKernelGGL(fg::check_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, word);
+  check(word);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_EHIP, "%s check launch: %s", what, hipGetErrorString(e));
+  int host[2] = {0, 0};
+  e = hipMemcpyAsync(host, word, sizeof host, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(FG_EHIP, "%s check read-back: %s", what, hipGetErrorString(e));
+  if (host[0] != fg::kCheckNone) *bad = host[0];
+  return FG_OK;
+}
+
+int32_t read_device_int(const int32_t* p, void* stream) {
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, p, 4, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+      hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return 0;
+  return v;
+}
+
+fg_status check_m_indices(const int32_t* idx, int M_total, int G, void* stream, const char* what) {
+  if (!env_flag("FG_CHECK_DEVICE")) return FG_OK;
+  int bad = -1;
+  FG_TRY(run_device_check(stream, what, [&](int* word) {
+    hipLaunchKernelGGL(fg::check_m_indices_kernel, dim3((unsigned)(M_total / 128)), dim3(128), 0, (hipStream_t)stream,
+                       idx, M_total, G, word);
+  }, &bad));
+  if (bad >= 0)
+    return fail(FG_EINVAL,
+                "%s: m_indices[%d] = %d is outside [-1, %d) or differs from the other indices of its 128-row block",
+                what, bad, read_device_int(idx + bad, stream), G);
+  return FG_OK;
+}
+
+fg_status check_masked_m(const int32_t* mask, int G, int M_cap, void* stream, const char* what) {
+  if (!env_flag("FG_CHECK_DEVICE")) return FG_OK;
+  int bad = -1;
+  FG_TRY(run_device_check(stream, what, [&](int* word) {
+    hipLaunchKernelGGL(fg::check_masked_m_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, mask, G, M_cap, word);
+  }, &bad));
+  if (bad >= 0)
+    return fail(FG_EINVAL, "%s: masked_m[%d] = %d is outside [0, %d]", what, bad, read_device_int(mask + bad, stream),
+                M_cap);
+  return FG_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -162,92 +256,21 @@ fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspaces of the kernels that exchange fp32 partials between workgroups
-// (stream-K and the split-K skinny kernel): partial slots and arrival
-// counters.  One per (kind, device, stream), allocated on the first call that
-// needs it and kept for the life of the process; the counters are zeroed once
-// at allocation and every launch leaves them zero.  Later calls allocate
-// nothing.  A call made while its stream is being captured into a graph never
-// allocates: it takes a path without a workspace instead.
+// Split-K exchange buffers of the few-row kernel, in a workspace the caller
+// owns: a fixed counter region (one int per output unit; it must be zero
+// before a workspace is first used, and every launch leaves the counters it
+// used at zero), then the fp32 partial slots.  The counter region has a fixed
+// size so that calls of different shapes on one workspace never read old
+// partials as counters.
 
-struct Workspace {
-  int kind = -1;
-  int dev = -1;
-  void* stream = nullptr;
-  float* partials = nullptr;
-  int* flags = nullptr;
+constexpr int kSkinnyMaxUnits = 1 << 14;
+constexpr int64_t kSplitCounterBytes = (int64_t)kSkinnyMaxUnits * 4;  // 64 KiB
+constexpr int64_t kSplitPartialMax = (int64_t)8 << 20;                // 8 MiB
+
+struct SplitWs {
+  void* base = nullptr;  // counters, then partials
+  int64_t bytes = 0;
 };
-constexpr int kWsSlots = 64;
-constexpr int kSkMaxTiles = 1 << 16;
-Workspace g_ws[kWsSlots];
-std::mutex g_ws_mu;
-
-enum { kWsStreamK = 0, kWsSkinny = 1 };
-
-bool stream_capturing(void* stream) {
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) return true;
-  return cs != hipStreamCaptureStatusNone;
-}
-
-Workspace* workspace(int kind, void* stream, size_t partial_bytes, int nflags) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  for (auto& w : g_ws)
-    if (w.partials && w.kind == kind && w.dev == dev && w.stream == stream) return &w;
-  if (stream_capturing(stream)) return nullptr;
-  for (auto& w : g_ws) {
-    if (w.partials) continue;
-    if (hipMalloc(&w.partials, partial_bytes) != hipSuccess) { w.partials = nullptr; return nullptr; }
-    if (hipMalloc(&w.flags, nflags * sizeof(int)) != hipSuccess ||
-        hipMemset(w.flags, 0, nflags * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      (void)hipFree(w.partials);
-      w.partials = nullptr;
-      return nullptr;
-    }
-    w.kind = kind;
-    w.dev = dev;
-    w.stream = stream;
-    return &w;
-  }
-  return nullptr;
-}
-
-template <class C>
-Workspace* sk_workspace(void* stream, int grid) {
-  const size_t pbytes = (size_t)grid * C::THREADS * C::SM * C::SN * 4 * sizeof(float);
-  return workspace(kWsStreamK, stream, pbytes, kSkMaxTiles);
-}
-
-// Stream-K pays off when whole-tile rounds would leave CUs idle: the tile
-// count is not a multiple of the grid and there are few rounds.  Each XCD's
-// block of tiles must give every one of its workgroups at least one K slice.
-// Opt-in (FG_STREAM_K=1).  Measured on MI355X it loses to whole-tile rounds
-// on the M=4096 shapes: an XCD's workgroups then work on different K offsets
-// of different tiles, so they stop sharing A/B in L2, and the fp32 partial
-// tiles add traffic.  Tile widths that fill whole rounds are used instead.
-bool want_stream_k(int64_t tiles, int Kb, int grid) {
-  const char* f = getenv("FG_STREAM_K");
-  if (!(f && strcmp(f, "1") == 0)) return false;
-  if (grid % 8 || tiles < 8 || tiles > kSkMaxTiles) return false;
-  const int nx = grid / 8;
-  if ((tiles / 8) * (int64_t)Kb < nx) return false;
-  if ((tiles / 8 + 1) * (int64_t)Kb * (nx + 1) >= ((int64_t)1 << 31)) return false;  // 32-bit bookkeeping
-  return true;
-}
-
-template <class C>
-fg_status launch_stream_k(fg::GemmParams& p, hipStream_t stream, int grid, Workspace* ws, const char* what) {
-  p.group_m = 8;
-  p.sk_partials = ws->partials;
-  p.sk_flags = ws->flags;
-  print_config(what, p, C::BM, C::BN, C::THREADS, grid, -1);
-  hipLaunchKernelGGL((fg::gemm_fp8_sk_kernel<C>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
-  return FG_OK;
-}
 
 // Width of the large kernel's 256-row tile.  The persistent grid runs whole
 // tiles in rounds and a tile's time grows with its width, so the width with
@@ -390,20 +413,21 @@ bool prefer_big(int64_t big_tiles) {
 // 64-column tiles are, 13 % faster than one part of 128 rows with 32-column
 // tiles.  The K split only has to bring the workgroup count near the CU
 // count; each further split adds fp32 partial traffic and a reduction.
-// FG_SKINNY="CF,SPLITS[,MF]" overrides the choice (tuning and tests; MF = 8
-// keeps 128 rows in one part).
-
-constexpr size_t kSkinnyPartialBytes = (size_t)16 << 20;
-constexpr int kSkinnyMaxTiles = 1 << 14;
+// The plan depends only on the shape, the device's CU count and whether the
+// call brings split-K buffers (`split_ok`), never on earlier calls or on
+// stream capture, so a call's summation order (and its bits) is fixed by its
+// arguments.  FG_SKINNY="CF,SPLITS[,MF]" overrides the choice (tuning and
+// tests; MF = 8 keeps 128 rows in one part).
 
 struct SkinnyPlan {
   int mf = 0, cf = 0, splits = 1, parts = 1;
+  int64_t units = 0;
+  int64_t partial_bytes() const { return splits > 1 ? (int64_t)splits * units * mf * cf * 1024 : 0; }
 };
 
-
-bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool may_split, SkinnyPlan* out) {
+bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool split_ok, SkinnyPlan* out) {
   if (M > 128 || K <= 0) return false;
-  const int Kb = (K + 127) / 128;
+  const int Kb = ceil128(K);
   SkinnyPlan pl;
   // 64-row activation fragments; more rows are spread over row parts
   pl.mf = 4;
@@ -415,15 +439,17 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
   // 32-bit lane offsets
   if ((int64_t)16 * pl.mf * lda + K >= ((int64_t)1 << 31)) return false;
   if (((int64_t)(Kb - 1) * ld_sa + M) * 4 >= ((int64_t)1 << 31)) return false;
+  auto units_of = [&](int cf) { return (int64_t)((N + 16 * cf - 1) / (16 * cf)) * pl.parts; };
   auto fits = [&](int cf, int sp) {
-    const int64_t units = (int64_t)((N + 16 * cf - 1) / (16 * cf)) * pl.parts;
-    return sp == 1 || (units <= kSkinnyMaxTiles && (size_t)sp * units * pl.mf * cf * 1024 <= kSkinnyPartialBytes);
+    const int64_t units = units_of(cf);
+    return sp == 1 || (units <= kSkinnyMaxUnits && (int64_t)sp * units * pl.mf * cf * 1024 <= kSplitPartialMax);
   };
   if (nenv >= 2 && (cf_env == 1 || cf_env == 2 || cf_env == 4) && pl.mf * cf_env <= 16 && sp_env >= 1 &&
-      (sp_env == 1 || may_split)) {
+      (sp_env == 1 || split_ok)) {
     if (!fits(cf_env, sp_env)) return false;
     pl.cf = cf_env;
     pl.splits = sp_env;
+    pl.units = units_of(pl.cf);
     *out = pl;
     return true;
   }
@@ -431,9 +457,9 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
   // workgroup then reads as many weight bytes per activation byte as a
   // one-part 32-column tile, and the parts double the workgroups)
   pl.cf = pl.parts > 1 ? 4 : 2;
-  const int64_t units = (int64_t)((N + 16 * pl.cf - 1) / (16 * pl.cf)) * pl.parts;
+  pl.units = units_of(pl.cf);
   int sp = 1;
-  if (may_split && units * 4 < (int64_t)cus * 3) sp = units * 4 >= cus ? 2 : 4;
+  if (split_ok && pl.units * 4 < (int64_t)cus * 3) sp = pl.units * 4 >= cus ? 2 : 4;
   while (sp > 1 && (Kb < 4 * sp || !fits(pl.cf, sp))) sp /= 2;
   pl.splits = sp;
   *out = pl;
@@ -458,12 +484,17 @@ fg_status launch_skinny_cfg(fg::GemmParams& p, int splits, int parts, hipStream_
 }
 
 template <bool ADD_C>
-fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, hipStream_t stream, const char* what) {
+fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, const SplitWs* ws, hipStream_t stream,
+                        const char* what) {
   if (pl.splits > 1) {
-    Workspace* ws = workspace(kWsSkinny, (void*)stream, kSkinnyPartialBytes, kSkinnyMaxTiles);
-    if (!ws) return fail(FG_EHIP, "%s: split-K workspace unavailable", what);
-    p.sk_partials = ws->partials;
-    p.sk_flags = ws->flags;
+    // the plan only splits when the call brought a workspace
+    const int64_t need = kSplitCounterBytes + pl.partial_bytes();
+    if (!ws || pl.units > kSkinnyMaxUnits) return fail(FG_EINVAL, "%s: the K split needs a workspace", what);
+    if (ws->bytes < need)
+      return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
+                  (long long)ws->bytes, (long long)need);
+    p.ws_counters = (int*)ws->base;
+    p.ws_partials = (float*)((uint8_t*)ws->base + kSplitCounterBytes);
   }
 #define FG_SKINNY_CASE(MF, CF) \
   if (pl.mf == MF && pl.cf == CF) return launch_skinny_cfg<MF, CF, ADD_C>(p, pl.splits, pl.parts, stream, what);
@@ -471,6 +502,19 @@ fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, hipStream_t str
   FG_SKINNY_CASE(8, 1) FG_SKINNY_CASE(8, 2)
 #undef FG_SKINNY_CASE
   return fail(FG_EUNSUPPORTED, "%s: no skinny configuration", what);
+}
+
+// Split-K partial bytes the few-row plan takes for (M, N, K) with
+// buffers available; 0 when it does not split (or does not apply).
+int64_t nt_split_partial_bytes(int M, int N, int K, int64_t lda, int64_t ld_sa) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const char* force = getenv("FG_FORCE_CONFIG");
+  if (force && (strcmp(force, "big") == 0 || strcmp(force, "small") == 0)) return 0;
+  int cus = 0;
+  if (device_cus(&cus) != FG_OK) return -1;
+  SkinnyPlan pl;
+  if (!plan_skinny(M, N, K, lda, ld_sa, cus, true, &pl)) return 0;
+  return pl.partial_bytes();
 }
 
 fg_status check_ld(int64_t ld, int64_t row, int64_t mult, const char* name) {
@@ -498,10 +542,11 @@ fg_status check_row_bytes(int64_t lda, int64_t ldb) {
 
 // Validation and dispatch shared by D = A B^T (kDense) and D = C + A B^T
 // (kDenseC, C already checked and set in the parameters).
+// `ws`: split-K buffers for the few-row kernel, or NULL (no K split).
 template <int L>
 fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                    const uint8_t* B, int64_t ldb, const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K,
-                   void* stream, const char* what) {
+                   const SplitWs* ws, void* stream, const char* what) {
   if (M < 0 || N < 0 || K < 0) return fail(FG_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
   if (K % 16) return fail(FG_EALIGN, "K=%d is not a multiple of 16", K);
   if (M == 0 || N == 0) return FG_OK;
@@ -519,7 +564,7 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
     FG_TRY(check_row_bytes(lda, ldb));
   }
   p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
-  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = ceil128(K); p.Nb = ceil128(N);
   if (p.ld_sb == 0) p.ld_sb = p.Kb;
   if (K > 0) {
     // few activation rows: the weight-streaming kernel
@@ -528,10 +573,8 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
       int all_cus = 0;
       FG_TRY(device_cus(&all_cus));  // the plan (and so the summation order) does not depend on the CU cap
       SkinnyPlan pl;
-      const bool may_split = !stream_capturing(stream) ||
-                             workspace(kWsSkinny, stream, kSkinnyPartialBytes, kSkinnyMaxTiles) != nullptr;
-      if (plan_skinny(M, N, K, lda, ld_sa, all_cus, may_split, &pl))
-        return launch_skinny<L == fg::kDenseC>(p, pl, (hipStream_t)stream, what);
+      if (plan_skinny(M, N, K, lda, ld_sa, all_cus, ws != nullptr, &pl))
+        return launch_skinny<L == fg::kDenseC>(p, pl, ws, (hipStream_t)stream, what);
     }
     using C = CfgBig;
     const int64_t tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
@@ -539,15 +582,6 @@ fg_status dense_nt(fg::GemmParams& p, const uint8_t* A, int64_t lda, const float
       p.tiles_m = (int)tm;
       p.tiles_n = (int)tn;
       p.num_tiles = (int)(tm * tn);
-      int cus = 0;
-      FG_TRY(device_cus(&cus));
-      if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
-      if (L == fg::kDense && K % 128 == 0 && want_stream_k(tm * tn, p.Kb, cus)) {
-        int all_cus = 0;
-        FG_TRY(device_cus(&all_cus));
-        Workspace* ws = sk_workspace<C>(stream, all_cus);  // slots for the uncapped grid
-        if (ws) return launch_stream_k<C>(p, (hipStream_t)stream, cus, ws, "gemm_fp8_nt[stream-k]");
-      }
       return launch_big_width<L>(p, 1, (hipStream_t)stream, what);
     }
   }
@@ -629,9 +663,9 @@ fg_status gemm_layout(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
   if (C) {
     p.Cin = C;
     p.ldc = ldc;
-    return dense_nt<fg::kDenseC>(p, a, lda, sa, ld_sa, b, ldb, sb, D, ldd, M, N, K, stream, what);
+    return dense_nt<fg::kDenseC>(p, a, lda, sa, ld_sa, b, ldb, sb, D, ldd, M, N, K, nullptr, stream, what);
   }
-  return dense_nt<fg::kDense>(p, a, lda, sa, ld_sa, b, ldb, sb, D, ldd, M, N, K, stream, what);
+  return dense_nt<fg::kDense>(p, a, lda, sa, ld_sa, b, ldb, sb, D, ldd, M, N, K, nullptr, stream, what);
 }
 }  // namespace
 
@@ -645,7 +679,7 @@ constexpr int64_t kCastWideGroups = 32768;
 template <bool UE8M0, typename T>
 static fg_status launch_cast_per_token(const T* x, int64_t ldx, uint8_t* q, void* sa, int64_t ld_sa, int M, int K,
                                        void* stream, const char* name) {
-  const int64_t groups = (int64_t)M * ((K + 127) / 128);
+  const int64_t groups = (int64_t)M * (ceil128(K));
   const int lpg = groups >= kCastWideGroups ? 8 : 16;
   const int64_t lanes = groups * lpg;
   const int64_t blocks = (lanes + 255) / 256;
@@ -665,6 +699,7 @@ extern "C" {
 
 int64_t fg_layout_workspace_bytes(const char* layout, int M, int N, int K) {
   if (!layout || M < 0 || N < 0 || K < 0) return -1;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxLd) return -1;  // sizes the calls reject
   if (strcmp(layout, "nt") == 0) return 0;
   if (strcmp(layout, "nn") == 0) return layout_ws_bytes(false, true, M, N, K);
   if (strcmp(layout, "tn") == 0) return layout_ws_bytes(true, true, M, N, K);
@@ -695,6 +730,7 @@ fg_status gemm_fp8_tt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
 
 int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total) {
   if (M < 0 || N < 0 || K_total < 0) return -1;
+  if (M > kMaxDim || N > kMaxDim || K_total > kMaxLd) return -1;  // sizes the call rejects
   return ws_round((int64_t)M * K_total) + ws_round((int64_t)N * K_total);
 }
 
@@ -760,9 +796,9 @@ fg_status gemm_fp8_k_grouped_tn_contiguous(const uint8_t* A, int64_t lda, const 
     if (C) {
       p.Cin = C + (int64_t)g * M * N;
       p.ldc = N;
-      st = dense_nt<fg::kDenseC>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, stream, what);
+      st = dense_nt<fg::kDenseC>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, nullptr, stream, what);
     } else {
-      st = dense_nt<fg::kDense>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, stream, what);
+      st = dense_nt<fg::kDense>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, nullptr, stream, what);
     }
     if (st != FG_OK) return st;
     k0 += kg;
@@ -774,7 +810,32 @@ fg_status gemm_fp8_nt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
                       const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* stream) {
   g_err.clear();
   fg::GemmParams p{};
-  return dense_nt<fg::kDense>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, "gemm_fp8_nt");
+  return dense_nt<fg::kDense>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, nullptr, stream, "gemm_fp8_nt");
+}
+
+int64_t fg_nt_workspace_max_bytes(void) { return kSplitCounterBytes + kSplitPartialMax; }
+
+int64_t fg_nt_workspace_bytes(int M, int N, int K) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  const int64_t part = nt_split_partial_bytes(M, N, K, ((int64_t)K + 15) / 16 * 16, ((int64_t)M + 3) / 4 * 4);
+  if (part < 0) return -1;
+  return part > 0 ? kSplitCounterBytes + part : 0;
+}
+
+fg_status gemm_fp8_nt_ws(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B,
+                         int64_t ldb, const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  const char* what = "gemm_fp8_nt_ws";
+  g_err.clear();
+  if (workspace_bytes < 0) return fail(FG_EINVAL, "%s: workspace_bytes=%lld is negative", what, (long long)workspace_bytes);
+  if (!workspace && workspace_bytes > 0) return fail(FG_EINVAL, "%s: workspace is NULL", what);
+  if (workspace && !aligned(workspace, 256)) return fail(FG_EALIGN, "%s: workspace is not 256-byte aligned", what);
+  SplitWs ws;
+  ws.base = workspace;
+  ws.bytes = workspace_bytes;
+  fg::GemmParams p{};
+  return dense_nt<fg::kDense>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace ? &ws : nullptr, stream,
+                              what);
 }
 
 fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B,
@@ -788,7 +849,7 @@ fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t 
   fg::GemmParams p{};
   p.Cin = C;
   p.ldc = ldc;
-  return dense_nt<fg::kDenseC>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, stream, "gemm_fp8_nt_c");
+  return dense_nt<fg::kDenseC>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, nullptr, stream, "gemm_fp8_nt_c");
 }
 
 fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t ld_sa, const uint8_t* B,
@@ -811,10 +872,11 @@ fg_status gemm_fp8_grouped_contiguous(const uint8_t* A, const float* sa, int64_t
     FG_TRY(check_ld(ld_sa, M_total, 1, "ld_sa"));
     FG_TRY(check_row_bytes(K, K));
   }
+  FG_TRY(check_m_indices(m_indices, M_total, G, stream, "gemm_fp8_grouped_contiguous"));
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
   p.m_indices = m_indices;
-  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = ceil128(K); p.Nb = ceil128(N); p.ld_sb = p.Kb;
   if (K > 0) {
     // 256-row tiles: a tile whose halves hold different experts runs as two segments
     return launch_big_width<fg::kContiguous>(p, 1, (hipStream_t)stream, "gemm_fp8_grouped_contiguous");
@@ -847,10 +909,11 @@ fg_status gemm_fp8_grouped_masked(const uint8_t* A, const float* sa, int64_t ld_
     FG_TRY(check_ld(ld_sa, M_cap, 1, "ld_sa"));
     FG_TRY(check_row_bytes(K, K));
   }
+  FG_TRY(check_masked_m(masked_m, G, M_cap, stream, "gemm_fp8_grouped_masked"));
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K; p.sb = sb; p.D = D; p.ldd = N;
   p.masked_m = masked_m;
-  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = ceil128(K); p.Nb = ceil128(N); p.ld_sb = p.Kb;
   if (K > 0) {
     return launch_big_width<fg::kMasked>(p, G, (hipStream_t)stream, "gemm_fp8_grouped_masked");
   }
@@ -876,7 +939,7 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   fg::GemmParams p{};
   p.A = A; p.lda = lda; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = ldd;
-  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = ceil128(K); p.Nb = ceil128(N); p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros
     using C = CfgDefault;
     p.tiles_m = (M + C::BM - 1) / C::BM;
@@ -907,11 +970,12 @@ fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa,
   if (M_total > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_total or N above 2^30");
   FG_TRY(check_ptr(D, 2, "D"));
   FG_TRY(check_ptr(m_indices, 4, "m_indices"));
+  FG_TRY(check_m_indices(m_indices, M_total, G, stream, "gemm_fp8_grouped_contiguous_ue8m0"));
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = N;
   p.m_indices = m_indices;
-  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_total; p.N = N; p.K = K; p.G = G; p.Kb = ceil128(K); p.Nb = ceil128(N); p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros of the mapped rows
     using C = CfgDefault;
     p.tiles_m = M_total / C::BM;
@@ -947,11 +1011,12 @@ fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int
   if (M_cap > kMaxDim || N > kMaxDim) return fail(FG_EUNSUPPORTED, "M_cap or N above 2^30");
   FG_TRY(check_ptr(D, 2, "D"));
   FG_TRY(check_ptr(masked_m, 4, "masked_m"));
+  FG_TRY(check_masked_m(masked_m, G, M_cap, stream, "gemm_fp8_grouped_masked_ue8m0"));
   fg::GemmParams p{};
   p.A = A; p.lda = K; p.sa = (const float*)(const void*)sa; p.ld_sa = ld_sa; p.B = B; p.ldb = K;
   p.sb = (const float*)(const void*)sb; p.D = D; p.ldd = N;
   p.masked_m = masked_m;
-  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = (K + 127) / 128; p.Nb = (N + 127) / 128; p.ld_sb = p.Kb;
+  p.rows = M_cap; p.N = N; p.K = K; p.G = G; p.Kb = ceil128(K); p.Nb = ceil128(N); p.ld_sb = p.Kb;
   if (K == 0) {  // no factors are read: the plain kernel writes the zeros of the valid rows
     using C = CfgDefault;
     p.tiles_m = (M_cap + C::BM - 1) / C::BM;
@@ -1010,7 +1075,7 @@ fg_status fp8_cast_per_block_ue8m0(const float* w, int64_t ldw, uint8_t* q, int3
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
+  const int64_t blocks = (int64_t)(ceil128(N)) * (ceil128(K));
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<true, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
                      ldw, q, (void*)sb, N, K);
@@ -1043,7 +1108,7 @@ fg_status fp8_cast_per_block_ue8m0_bf16(const uint16_t* w, int64_t ldw, uint8_t*
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
+  const int64_t blocks = (int64_t)(ceil128(N)) * (ceil128(K));
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<true, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)stream, w, ldw, q, (void*)sb, N, K);
@@ -1076,7 +1141,7 @@ fg_status fp8_cast_per_block_bf16(const uint16_t* w, int64_t ldw, uint8_t* q, fl
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
+  const int64_t blocks = (int64_t)(ceil128(N)) * (ceil128(K));
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<false, uint16_t>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)stream, w, ldw, q, (void*)sb, N, K);
@@ -1094,7 +1159,7 @@ fg_status fp8_cast_per_block(const float* w, int64_t ldw, uint8_t* q, float* sb,
   FG_TRY(check_ptr(q, 4, "q"));
   FG_TRY(check_ptr(sb, 4, "sb"));
   FG_TRY(check_ld(ldw, K, 4, "ldw"));
-  const int64_t blocks = (int64_t)((N + 127) / 128) * ((K + 127) / 128);
+  const int64_t blocks = (int64_t)(ceil128(N)) * (ceil128(K));
   if (blocks > 0x7fffffff) return fail(FG_EUNSUPPORTED, "input too large");
   hipLaunchKernelGGL((fg::cast_per_block_kernel<false, float>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, ldw, q,
                      sb, N, K);

@@ -62,10 +62,10 @@ struct GemmParams {
   int num_tiles;         // tile slots walked by the persistent grid
   int group_m;           // raster band height in tiles
   int kb_factor;         // K extent of one group's factor arrays: 0 = Kb (fp32 factors), ceil(Kb/4) (packed UE8M0)
-  // stream-K (dense only): fp32 partial tiles, one slot per workgroup, and
-  // one arrival counter per tile (zero between launches)
-  float* sk_partials;
-  int* sk_flags;
+  // few-row split-K: fp32 partial slots and one arrival counter per output
+  // unit, in the caller's workspace (counters zero between launches)
+  float* ws_partials;
+  int* ws_counters;
 };
 
 // Group stride, in K groups (fp32 factors) or packed words (UE8M0), of the
@@ -234,6 +234,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // the instruction's scalar offset (at most a 4 MiB row) added, and without
 // 32-bit wrap-around: such a load returns zeros and touches no memory.
 constexpr int kOobOffset = 0x7fffffff;
+
+// Cache policy bits of a buffer access (sc0 | sc1): system-coherent, so the
+// data neither stays in nor is served from a non-coherent cache.  Used for
+// the fp32 partials that workgroups exchange.
+constexpr int kSysCoherent = 1 | 16;
 
 // K tails (K % 128 != 0, K % 16 == 0): the last slice holds K % 128 columns.
 // A 16-byte chunk that starts at or past column K of its row is read as
@@ -1142,262 +1147,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_ue8m0_kernel(GemmParam
     }
     cur = nxt;
     it = it_n;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-#undef FG_STAGE
-#undef FG_SA
-}
-
-// ===========================================================================
-// Stream-K variant of the large-tile kernel (dense).  When the tile count is
-// not a multiple of the workgroup count, whole-tile scheduling leaves CUs idle
-// in the last round; here the K slices of all tiles are divided evenly.
-//
-//  * Each XCD (workgroups b with b % 8 == x) owns a contiguous block of whole
-//    tiles; its workgroups split that block's (tile, K slice) iterations into
-//    equal contiguous ranges.  Workgroups that share a tile therefore share an
-//    L2.
-//  * A workgroup walks its range from the highest iteration down.  For a tile
-//    covered by several workgroups, the highest one (which reaches that tile
-//    last) finalizes it: it waits until the lower ones -- which computed their
-//    part of the tile first -- have published fp32 partials, adds them and
-//    stores.  Waits only ever target lower block ids, which the dispatcher has
-//    already started, so the waits end whatever the residency.
-// ===========================================================================
-
-// All stream-K bookkeeping is 32-bit: the host only selects stream-K when an
-// XCD block's iteration count times the workgroups per XCD fits in int32.
-// Cache policy bits of a buffer access (sc0 | sc1): system-coherent.
-constexpr int kSysCoherent = 1 | 16;
-
-struct SkRange {
-  int s, e;    // this workgroup's iterations, relative to its XCD block
-  int t0;      // first tile of the XCD block
-  int iters;   // iterations of the XCD block
-  int nx, j;   // workgroups per XCD, this workgroup's index in it
-};
-
-struct SkSeg {
-  int t;            // tile id (global linear), -1 = none
-  int k0, k1;       // K slices [k0, k1)
-  int role;         // 0 whole tile, 1 contributor, 2 finalizer
-  int j_first;      // finalizer: lowest contributing workgroup index in the XCD
-};
-
-__device__ __forceinline__ int sk_start(const SkRange& r, int j) { return r.iters * j / r.nx; }
-
-// Segment just below iteration `hi` (exclusive) of this workgroup's range.
-__device__ __forceinline__ SkSeg sk_segment(const SkRange& r, int Kb, int hi) {
-  SkSeg g;
-  if (hi <= r.s) {
-    g.t = -1;
-    g.k0 = g.k1 = 0;
-    g.role = 0;
-    g.j_first = 0;
-    return g;
-  }
-  const int tl = (hi - 1) / Kb;  // tile within the block
-  const int tstart = tl * Kb, tend = tstart + Kb;
-  const int lo = max(r.s, tstart);
-  g.t = r.t0 + tl;
-  g.k0 = lo - tstart;
-  g.k1 = hi - tstart;
-  const bool has_first = lo == tstart, has_last = hi == tend;
-  g.role = (has_first && has_last) ? 0 : (has_last ? 2 : 1);
-  // lowest workgroup whose range holds the tile's first iteration
-  int jf = tstart * r.nx / r.iters;
-  while (jf > 0 && sk_start(r, jf) > tstart) --jf;
-  while (jf + 1 < r.nx && sk_start(r, jf + 1) <= tstart) ++jf;
-  g.j_first = jf;
-  return g;
-}
-
-template <class C>
-__device__ __forceinline__ void sk_tile_work(const GemmParams& p, int t, Work& w) {
-  int tm, tn;
-  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  w.A = p.A;
-  w.sa = p.sa;
-  w.B = p.B;
-  w.sb = p.sb;
-  w.D = p.D;
-  w.m0 = tm * C::BM;
-  w.n0 = tn * C::BN;
-  w.rows_alloc = p.rows;
-  w.rows_valid = p.rows;
-  w.seg = 0;
-  w.nseg = 1;
-  w.half_mask = 3;
-  w.e_lo = w.e_hi = 0;
-  w.w = t;
-}
-
-template <class C>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_sk_kernel(GemmParams p) {
-  constexpr int BM = C::BM, WM = C::WM, WN = C::WN;
-  constexpr int SM = C::SM, SN = C::SN;
-  constexpr int NACC = SM * SN * 4;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
-#define FG_STAGE(i) (lds + (i) * C::STAGE)
-#define FG_SA(i) (lds + C::SA_OFF + (i) * 1024)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N;
-  const int wn = wave % C::WAVES_N;
-  const int l16 = lane & 15;
-  const int kq = lane >> 4;
-
-  int a_off[2], b_off[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int ra = wm * WM + l16;
-    const int rb = BM + wn * WN + l16;
-    a_off[h] = ra * 128 + (((2 * kq + h) ^ swz16(ra)) << 4);
-    b_off[h] = rb * 128 + (((2 * kq + h) ^ swz16(rb)) << 4);
-  }
-
-  const int Kb = p.Kb;
-  const int b = blockIdx.x;
-  SkRange rg;
-  {
-    const int x = b & 7;
-    rg.nx = gridDim.x >> 3;  // the host launches a multiple of 8 workgroups
-    rg.j = b >> 3;
-    rg.t0 = p.num_tiles * x / 8;
-    const int t1 = p.num_tiles * (x + 1) / 8;
-    rg.iters = (t1 - rg.t0) * Kb;
-    rg.s = sk_start(rg, rg.j);
-    rg.e = sk_start(rg, rg.j + 1);
-  }
-  SkSeg cur = sk_segment(rg, Kb, rg.e);
-  if (cur.t < 0) return;
-  Work cw;
-  sk_tile_work<C>(p, cur.t, cw);
-
-  float sb_c[2];
-  load_sb<C>(p, cw, cur.k0, wn, sb_c);
-  issue_slice_loads<C>(p, cw, cur.k0, FG_STAGE(0), FG_SA(0), wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  float acc[SM][SN][4];
-#pragma unroll
-  for (int ms = 0; ms < SM; ++ms)
-#pragma unroll
-    for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
-
-  int stage = 0;
-  int hi = rg.e;
-  while (cur.t >= 0) {
-    const int lo = hi - (cur.k1 - cur.k0);
-    const SkSeg nxt = sk_segment(rg, Kb, lo);
-    Work nw = cw;
-    if (nxt.t >= 0) sk_tile_work<C>(p, nxt.t, nw);
-
-    for (int kb = cur.k0; kb < cur.k1; ++kb) {
-      const bool last = kb + 1 == cur.k1;
-      float sb_n[2] = {0.f, 0.f};
-      if (!last) {
-        load_sb<C>(p, cw, kb + 1, wn, sb_n);
-        issue_slice_loads<C>(p, cw, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
-      } else if (nxt.t >= 0) {
-        load_sb<C>(p, nw, nxt.k0, wn, sb_n);
-        issue_slice_loads<C>(p, nw, nxt.k0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
-      }
-      if (cw.m0 + wm * WM < cw.rows_valid) {
-        float sc[SM][2];
-        slice_scales<C>(FG_SA(stage), wm, l16, sb_c, sc);
-        slice_mma<C>(FG_STAGE(stage), a_off, b_off, sc, second_block_subtile<C>(cw, wn), acc);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      stage ^= 1;
-      sb_c[0] = sb_n[0];
-      sb_c[1] = sb_n[1];
-    }
-
-    // Partial exchange without whole-cache maintenance: partials are written
-    // and read with system-coherent buffer operations (sc0 sc1: they do not
-    // stay in, or get served from, a non-coherent cache) and the arrival
-    // counter is a system-scope atomic.  A contributor's waves wait for their
-    // stores to be acknowledged before the workgroup counts in; the finalizer
-    // reads the partials only after it has seen every arrival.
-    const __amdgpu_buffer_rsrc_t prs =
-        make_rsrc(p.sk_partials, (int64_t)gridDim.x * C::NWAVES * NACC * 64 * (int64_t)sizeof(float));
-    if (cur.role == 1) {
-      // contributor: publish the partial tile, then count in
-      const int base = ((b * C::NWAVES + wave) * NACC * 64 + lane) * 4;
-#pragma unroll
-      for (int ms = 0; ms < SM; ++ms)
-#pragma unroll
-        for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc[ms][tt][r]), prs, base,
-                                                  ((ms * SN + tt) * 4 + r) * 256, kSysCoherent);
-      // each wave's system-coherent stores are acknowledged at the point of
-      // coherence before the workgroup counts in
-      __builtin_amdgcn_s_waitcnt(0);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (tid == 0) __hip_atomic_fetch_add(p.sk_flags + cur.t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    } else {
-      if (cur.role == 2) {
-        // finalizer: wait for the lower workgroups' partials and add them.
-        // The wait is bounded: past the bound the tile is finished without
-        // the missing partials (a wrong result, never a hang).
-        const int need = rg.j - cur.j_first;
-        if (tid == 0) {
-          for (int spin = 0; spin < (1 << 22); ++spin) {
-            if (__hip_atomic_load(p.sk_flags + cur.t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= need) break;
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        for (int jj = cur.j_first; jj < rg.j; ++jj) {
-          const int bb = (jj << 3) | (b & 7);
-          const int base = ((bb * C::NWAVES + wave) * NACC * 64 + lane) * 4;
-          // one fragment row (SN*4 values) at a time keeps the loads' registers bounded
-#pragma unroll
-          for (int ms = 0; ms < SM; ++ms) {
-            __builtin_amdgcn_sched_barrier(0);
-            float v[SN][4];
-#pragma unroll
-            for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                v[tt][r] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(prs, base, ((ms * SN + tt) * 4 + r) * 256, kSysCoherent));
-#pragma unroll
-            for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[ms][tt][r] += v[tt][r];
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        if (tid == 0) __hip_atomic_store(p.sk_flags + cur.t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
-      store_tile<C, kDense>(p, cw, acc, FG_STAGE(stage ^ 1), wave, lane);
-    }
-#pragma unroll
-    for (int ms = 0; ms < SM; ++ms)
-#pragma unroll
-      for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
-    cur = nxt;
-    cw = nw;
-    hi = lo;
   }
   __builtin_amdgcn_s_waitcnt(0);
 #undef FG_STAGE

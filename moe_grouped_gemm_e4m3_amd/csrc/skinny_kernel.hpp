@@ -272,7 +272,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   // partial of (unit, split): [GROUPS][64 lanes] float4, 1 KiB per block
   const int64_t slot_floats = (int64_t)C::GROUPS * 64 * 4;
   const __amdgpu_buffer_rsrc_t prs =
-      make_rsrc(p.sk_partials + (int64_t)unit * splits * slot_floats,
+      make_rsrc(p.ws_partials + (int64_t)unit * splits * slot_floats,
                 (int64_t)splits * slot_floats * (int64_t)sizeof(float));
 #pragma unroll
   for (int y = 0; y < C::GPW; ++y) {
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   __syncthreads();
   int* last_flag = (int*)(lds + C::LDS - 16);
   if (tid == 0) {
-    const int before = __hip_atomic_fetch_add(p.sk_flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int before = __hip_atomic_fetch_add(p.ws_counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     *last_flag = before == splits - 1;
   }
   __syncthreads();
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
 #pragma unroll
   for (int y = 0; y < C::GPW; ++y) skinny_store<C, ADD_C>(p, r0, n0, wave * C::GPW + y, t[y], lane);
   // every workgroup of the unit has counted in: reset for the next launch
-  if (tid == 0) __hip_atomic_store(p.sk_flags + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (tid == 0) __hip_atomic_store(p.ws_counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace fg

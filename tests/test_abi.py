@@ -85,6 +85,41 @@ def test_dense_argument_errors(lib, kw, status, needle):
     assert needle in lib.fg_last_error().decode()
 
 
+def dense_ws(lib, ws=P16 * 16, ws_bytes=1 << 20, **kw):
+    a = dict(A=P16, lda=512, sa=P16, ld_sa=64, B=P16, ldb=512, sb=P16, D=P16, ldd=256, M=64, N=256, K=512)
+    a.update(kw)
+    return lib.gemm_fp8_nt_ws(a["A"], a["lda"], a["sa"], a["ld_sa"], a["B"], a["ldb"], a["sb"], a["D"], a["ldd"],
+                              a["M"], a["N"], a["K"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(ws_bytes=-1), FG_EINVAL, "negative"),
+        (dict(ws=None, ws_bytes=4096), FG_EINVAL, "workspace is NULL"),
+        (dict(ws=P16 * 16 + 16), FG_EALIGN, "256-byte aligned"),
+        (dict(K=100), FG_EALIGN, "K=100"),
+        (dict(A=None), FG_EINVAL, "A is NULL"),
+        (dict(M=-2), FG_EINVAL, "negative"),
+    ],
+)
+def test_dense_workspace_argument_errors(lib, kw, status, needle):
+    """gemm_fp8_nt_ws checks its workspace arguments on the host before any
+    device query (the too-small case needs the device's plan: a GPU test)."""
+    assert dense_ws(lib, **kw) == status
+    assert needle in lib.fg_last_error().decode()
+
+
+def test_workspace_queries_on_the_host(lib):
+    assert lib.fg_nt_workspace_max_bytes() == (8 << 20) + (64 << 10)
+    assert lib.fg_nt_workspace_bytes(-1, 64, 128) == -1
+    assert lib.fg_nt_workspace_bytes(64, -1, 128) == -1
+    # sizes the calls reject have no workspace size (and no overflow)
+    assert lib.fg_layout_workspace_bytes(b"tn", 64, 64, (1 << 22) + 16) == -1
+    assert lib.fg_k_grouped_workspace_bytes((1 << 30) + 1, 64, 128) == -1
+    assert lib.fg_layout_workspace_bytes(b"tn", 3, 5, 256) == 768 + 1280  # each copy rounded to 256 bytes
+
+
 def test_empty_problems_are_noops(lib):
     # no pointers at all: nothing may be touched or launched
     assert lib.gemm_fp8_nt(None, 0, None, 0, None, 0, None, None, 0, 0, 128, 256, None) == FG_OK

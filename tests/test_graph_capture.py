@@ -1,10 +1,12 @@
 """HIP graph capture and concurrent streams.
 
-The header promises that every call may be captured into a HIP graph (a call
-made while its stream is capturing never allocates) and that calls on
-different streams use different split-K workspaces.  The graph is replayed
-several times with eager work in between, and every replay is compared bit
-for bit with the eager result of the same call."""
+The header promises that no call allocates or synchronises, so every call may
+be captured into a HIP graph, and that a call's plan (and so its bits)
+depends only on its arguments: the few-row split-K takes its exchange buffers
+from a workspace (the binding keeps a zero-filled one per stream, made by
+torch's allocator; on a fresh stream it is made inside the capture).  The
+graph is replayed several times with eager work in between, and every replay
+is compared bit for bit with the eager result of the same call."""
 
 from __future__ import annotations
 
@@ -39,8 +41,9 @@ def _masked_operands(G, Mc, N, K, seed):
 @pytest.mark.parametrize("fresh_stream", [False, True], ids=["warm-stream", "fresh-stream"])
 def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
     """Dense few-row (split K), dense large-tile and masked calls, and the
-    power-of-two-factor dense, masked and contiguous calls, captured together.  On the fresh stream nothing has run before the capture, so the
-    split-K path must fall back to no split rather than allocate."""
+    power-of-two-factor dense, masked and contiguous calls, captured together.
+    On the fresh stream nothing has run before the capture; the captured
+    few-row GEMM still takes the split plan of the eager call."""
     monkeypatch.delenv("FG_FORCE_CONFIG", raising=False)
     monkeypatch.delenv("FG_SKINNY", raising=False)
     announce(f"graph capture ({'fresh' if fresh_stream else 'warm'} stream)")
@@ -96,16 +99,11 @@ def test_graph_replays_match_eager(gpu_lib, monkeypatch, fresh_stream):
         run_all(s)
     torch.cuda.synchronize()
 
-    # eager reference on the default stream (its own workspace), with the
-    # plan the capture took: on a fresh stream the few-row GEMM was captured
-    # without a K split (32-column tiles, one split)
+    # eager reference on the default stream (its own workspace), default plan
     for o in outs:
         o.fill_(0)
-    if fresh_stream:
-        monkeypatch.setenv("FG_SKINNY", "2,1")
     run_all()
     torch.cuda.synchronize()
-    monkeypatch.delenv("FG_SKINNY", raising=False)
     ref = [bf16_bits(o) for o in outs]
     valid = np.arange(256)[None, :] < masked[4].cpu().numpy()[:, None]
     mapped = idx.cpu().numpy() >= 0
@@ -152,3 +150,43 @@ def test_concurrent_streams_split_k(gpu_lib, monkeypatch):
         torch.cuda.synchronize()
         for D, ref in zip(outs, seq):
             assert np.array_equal(bf16_bits(D), ref)
+
+
+def test_split_plan_does_not_depend_on_capture(gpu_lib, monkeypatch):
+    """The decode shape's split plan needs a workspace; the same call made
+    eagerly, captured on a fresh stream, and through the C entry point with
+    an explicit workspace gives the same bits.  The captured graph is then
+    replayed on another stream while eager calls with a different workspace
+    run on the capturing one."""
+    monkeypatch.delenv("FG_FORCE_CONFIG", raising=False)
+    monkeypatch.delenv("FG_SKINNY", raising=False)
+    announce("split plan vs capture 64x2112x7168")
+    M, N, K = 64, 2112, 7168
+    op = _dense_operands(M, N, K, seed=12)
+    assert gpu_lib.nt_workspace_bytes(M, N, K) > 0  # the plan splits K
+    eager = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.gemm_fp8_nt(*op, eager)
+    torch.cuda.synchronize()
+    ref = bf16_bits(eager)
+    own = torch.zeros(gpu_lib.nt_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    explicit = torch.empty_like(eager)
+    gpu_lib.gemm_fp8_nt(*op, explicit, workspace=own)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(explicit), ref)
+    s_cap, s_other = torch.cuda.Stream(), torch.cuda.Stream()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s_cap):
+        gpu_lib.gemm_fp8_nt(*op, out, stream=s_cap)
+    torch.cuda.synchronize()
+    side = torch.empty_like(eager)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s_other):
+            g.replay()
+        with torch.cuda.stream(s_cap):
+            gpu_lib.gemm_fp8_nt(*op, side, stream=s_cap, workspace=own)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(out), ref), rep
+        assert np.array_equal(bf16_bits(side), ref), rep

@@ -1,8 +1,8 @@
 """D = C + A . B^T (an fp32 addend C) on the GPU against the CPU oracle.
 
 Every kernel that serves the dense call is forced in turn: the few-row
-kernel with and without a K split (the addend is applied once, by the
-workgroup that finishes the sum), the 128x128 kernel and the large kernel
+kernel at each column width and activation height (the addend call never
+splits K: it takes no workspace), the 128x128 kernel and the large kernel
 at each tile width.  In the exact regime (integer codes, power-of-two
 scales, C on a 1/4 grid) the result is compared bit for bit; random inputs
 use the oracle's per-element bound with |C| in the magnitude.  With C = 0 the
@@ -27,14 +27,13 @@ KERNELS = {
     "skinny-1x1": {"FG_SKINNY": "1,1"},
     "skinny-2x1": {"FG_SKINNY": "2,1"},
     "skinny-4x1": {"FG_SKINNY": "4,1"},
-    "skinny-2x4": {"FG_SKINNY": "2,4"},
     "skinny-2x2-128rows": {"FG_SKINNY": "2,2,8"},
     "small": {"FG_FORCE_CONFIG": "small"},
     "big-256": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "256"},
     "big-224": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "224"},
     "big-160": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "160"},
 }
-ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN", "FG_STREAM_K")
+ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN")
 
 
 @pytest.fixture(params=list(KERNELS))
@@ -99,14 +98,15 @@ def test_random(gpu_lib, kernel, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(64, 2112, 1024), (300, 700, 512)])
 def test_zero_addend_gives_gemm_bits(gpu_lib, kernel, M, N, K):
-    """Same kernels, same summation order: C = 0 reproduces gemm_fp8_nt."""
+    """Same kernels, same summation order: C = 0 reproduces the bits of the
+    C entry point gemm_fp8_nt (neither splits K)."""
     if not _applies(kernel, M, K):
         pytest.skip("plan does not apply to this shape")
     announce(f"addend {kernel} zero C {M}x{N}x{K}")
     A32, B32 = synth.dense_problem(M, N, K, seed=17)
     qa, sa, qb, sb = quantize_dense(A32, B32)
     D0 = sentinel_like((M, N))
-    gpu_lib.gemm_fp8_nt(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), D0)
+    gpu_lib.gemm_fp8_nt_unsplit(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), D0)
     D1 = run_c(gpu_lib, qa, sa, qb, sb, np.zeros((M, N), np.float32))
     assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
 

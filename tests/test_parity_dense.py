@@ -116,9 +116,7 @@ def test_power_of_two_equivariance(gpu_lib, tile_config):
 
 def test_determinism_and_grid_invariance(gpu_lib, tile_config, monkeypatch):
     """Whole-tile scheduling: the CU cap changes which workgroup computes a
-    tile, never how, so the bits are identical.  (Stream-K splits K by the
-    workgroup count; it is covered by test_stream_k_deterministic.)"""
-    monkeypatch.setenv("FG_STREAM_K", "0")
+    tile, never how, so the bits are identical."""
     announce(f"dense grid invariance 640x1000x1024 {tile_config}")
     M, N, K = 640, 1000, 1024
     A32, B32 = synth.dense_problem(M, N, K, seed=21)
@@ -177,50 +175,3 @@ def test_m4096_full_size_sampled(gpu_lib, shape):
         assert np.array_equal(sb_d[nb].cpu().numpy(), sb[0])
         X, S = ogemm.gemm_nt(qa, sa, qb, sb, with_magnitude=True)
         assert_close(bf16_to_f64(Dh[:, cols]), X, S, K // 128, f"{shape} block {nb}")
-
-
-@pytest.mark.parametrize("cus", [0, 64, 8])
-@pytest.mark.parametrize("M,N,K", [(1024, 1000, 2048), (2048, 2112, 1024), (600, 1300, 3072)])
-def test_stream_k_matches_oracle(gpu_lib, monkeypatch, cus, M, N, K):
-    """Stream-K forced on: a tile's K slices are split over several
-    workgroups whose fp32 partials are added by the tile's finalizer."""
-    announce(f"dense stream-K {M}x{N}x{K} cus={cus}")
-    monkeypatch.setenv("FG_STREAM_K", "1")
-    monkeypatch.setenv("FG_FORCE_CONFIG", "big")
-    A32, B32 = synth.dense_problem(M, N, K, seed=M + 3 * N + K)
-    qa, sa, qb, sb = quantize_dense(A32, B32)
-    X, S = oracle_dense(qa, sa, qb, sb)
-    try:
-        gpu_lib.set_num_cus(cus)
-        for rep in range(2):  # a second launch reuses the arrival counters
-            D = run_dense(gpu_lib, qa, sa, qb, sb)
-            assert_close(bf16_to_f64(D), X, S, K // 128, f"stream-K {M}x{N}x{K} cus={cus} rep={rep}")
-    finally:
-        gpu_lib.set_num_cus(0)
-
-
-def test_stream_k_exact_regime_bitwise(gpu_lib, monkeypatch):
-    announce("dense stream-K exact regime 1024x1000x2048")
-    monkeypatch.setenv("FG_STREAM_K", "1")
-    monkeypatch.setenv("FG_FORCE_CONFIG", "big")
-    rng = np.random.default_rng(99)
-    qa, sa, qb, sb = exact_regime(rng, 1024, 1000, 2048)
-    D = run_dense(gpu_lib, qa, sa, qb, sb)
-    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_nt(qa, sa, qb, sb)))
-
-
-def test_stream_k_deterministic(gpu_lib, monkeypatch):
-    """Same CU cap, same split, same bits -- run after run."""
-    announce("dense stream-K determinism 2048x2112x1024")
-    monkeypatch.setenv("FG_STREAM_K", "1")
-    monkeypatch.setenv("FG_FORCE_CONFIG", "big")
-    A32, B32 = synth.dense_problem(2048, 2112, 1024, seed=31)
-    qa, sa, qb, sb = quantize_dense(A32, B32)
-    for cus in (0, 64):
-        try:
-            gpu_lib.set_num_cus(cus)
-            ref = bf16_bits(run_dense(gpu_lib, qa, sa, qb, sb))
-            for _ in range(3):
-                assert np.array_equal(ref, bf16_bits(run_dense(gpu_lib, qa, sa, qb, sb))), cus
-        finally:
-            gpu_lib.set_num_cus(0)

@@ -216,3 +216,61 @@ def test_masked_decode_full_size(gpu_lib, shape):
             X, S = ogemm.gemm_nt(qa, sa, qb, sb, with_magnitude=True)
             y = bf16_to_f64(D[g, torch.from_numpy(rows).cuda(), cols])
             assert_close(y, X, S, K // 128, f"group {g} block {nb}")
+
+
+def test_device_check_mode(gpu_lib, monkeypatch):
+    """FG_CHECK_DEVICE=1: valid metadata runs as usual; an expert index
+    outside [-1, G), a block holding two experts, and a count outside
+    [0, M_cap] are reported as FG_EINVAL naming the position, and the GEMM is
+    not launched (D keeps its sentinel).  B is allocated with one expert more
+    than G, so even the out-of-range index would stay inside it."""
+    monkeypatch.setenv("FG_CHECK_DEVICE", "1")
+    announce("device check mode")
+    G, N, K = 3, 256, 256
+    A32, B32, idx = synth.contiguous_problem([128, 200, 60], N, K, seed=40)
+    qa, sa = quant.quantize_per_token(A32.numpy())
+    qb, sb = quantize_grouped_B(B32.numpy())
+    qb_x = np.concatenate([qb, qb[:1]])  # G + 1 experts of storage
+    sb_x = np.concatenate([sb, sb[:1]])
+    a, s_a, b, s_b = dev_u8(qa), dev_sa(sa), dev_u8(qb_x), dev_f32(sb_x)
+    ok = run_contig(gpu_lib, qa, sa, qb, sb, idx)
+    for bad, needle in [((5, G), "m_indices\\[5\\] = 3"), ((130, -5), "m_indices\\[130\\] = -5"),
+                        ((257, 0), "m_indices\\[257\\] = 0")]:
+        row, val = bad
+        idx_bad = idx.copy()
+        idx_bad[row] = val
+        D = sentinel_like((idx.shape[0], N))
+        with pytest.raises(gpu_lib.FP8GemmError, match=needle):
+            gpu_lib.gemm_fp8_grouped_contiguous(a, s_a, b[:G], s_b[:G], torch.from_numpy(idx_bad).cuda(), D)
+        torch.cuda.synchronize()
+        assert (bf16_bits(D) == SENTINEL_BF16).all()
+    # the valid call in check mode equals the unchecked one
+    D = sentinel_like((idx.shape[0], N))
+    gpu_lib.gemm_fp8_grouped_contiguous(a, s_a, b[:G], s_b[:G], torch.from_numpy(idx).cuda(), D)
+    torch.cuda.synchronize()
+    mapped = idx >= 0
+    assert np.array_equal(bf16_bits(D)[mapped], bf16_bits(ok)[mapped])
+    # masked counts
+    Gm, Mc = 4, 128
+    rng = np.random.default_rng(41)
+    qa_m, sa_m, qb_m, sb_m = exact_regime(rng, Mc, N, K, groups=(Gm, Gm))
+    for mask, needle in [([5, 0, 129, 3], "masked_m\\[2\\] = 129"), ([5, -1, 7, 3], "masked_m\\[1\\] = -1")]:
+        D = sentinel_like((Gm, Mc, N))
+        with pytest.raises(gpu_lib.FP8GemmError, match=needle):
+            gpu_lib.gemm_fp8_grouped_masked(dev_u8(qa_m), dev_sa(sa_m, groups=True), dev_u8(qb_m), dev_f32(sb_m),
+                                            torch.tensor(mask, dtype=torch.int32, device="cuda"), D)
+        torch.cuda.synchronize()
+        assert (bf16_bits(D) == SENTINEL_BF16).all()
+    Dm = run_masked(gpu_lib, qa_m, sa_m, qb_m, sb_m, [5, 0, 128, 3])
+    Xm, valid = ogemm.gemm_grouped_masked(qa_m, sa_m, qb_m, sb_m, [5, 0, 128, 3])
+    assert np.array_equal(bf16_bits(Dm)[valid], ogemm.to_bf16(Xm[valid]))
+    # the check reads a result back, so it refuses a capturing stream
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    D = sentinel_like((idx.shape[0], N))
+    idx_d = torch.from_numpy(idx).cuda()
+    torch.cuda.synchronize()
+    with pytest.raises(gpu_lib.FP8GemmError, match="captured"):
+        with torch.cuda.graph(g, stream=s):
+            gpu_lib.gemm_fp8_grouped_contiguous(a, s_a, b[:G], s_b[:G], idx_d, D, stream=s)
+    torch.cuda.synchronize()

@@ -21,10 +21,10 @@ from tests.helpers import (
 
 pytestmark = pytest.mark.gpu
 
-ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN", "FG_STREAM_K")
+ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN")
 KERNELS = {
     "default": {},
-    "skinny-2x2": {"FG_SKINNY": "2,2"},
+    "skinny-2x1": {"FG_SKINNY": "2,1"},
     "small": {"FG_FORCE_CONFIG": "small"},
     "big-224": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "224"},
 }

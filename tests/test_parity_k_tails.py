@@ -25,7 +25,7 @@ from tests.helpers import (
 
 pytestmark = pytest.mark.gpu
 
-ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN", "FG_STREAM_K")
+ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN")
 TAIL_KS = [16, 48, 176, 304, 1040]
 
 

@@ -24,7 +24,7 @@ from tests.helpers import (
 pytestmark = pytest.mark.gpu
 
 LAYOUTS = ["nn", "tn", "tt"]
-ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN", "FG_STREAM_K")
+ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN")
 
 
 @pytest.fixture(autouse=True)
@@ -109,13 +109,14 @@ def test_random_inputs(gpu_lib, layout):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_same_bits_as_nt(gpu_lib, layout):
-    """The layouts run the NT kernels on a transposed copy: same bits as NT."""
+    """The layouts run the NT kernels on a transposed copy: same bits as the
+    NT entry point (neither splits K)."""
     M, N, K = 64, 2112, 1024
     announce(f"layout {layout} equals nt")
     A32, B32 = synth.dense_problem(M, N, K, seed=29)
     qa, sa, qb, sb = quantize_dense(A32, B32)
     D0 = sentinel_like((M, N))
-    gpu_lib.gemm_fp8_nt(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), D0)
+    gpu_lib.gemm_fp8_nt_unsplit(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), D0)
     As, Bs = stored(layout, qa, qb)
     D1 = call(gpu_lib, layout, As, sa, Bs, sb)
     assert np.array_equal(bf16_bits(D1), bf16_bits(D0))

@@ -119,3 +119,49 @@ def test_small_m_decode_full_size(gpu_lib, monkeypatch, shape):
     D = run_dense(gpu_lib, qa, sa, qb, sb)
     X, S = oracle_dense(qa, sa, qb, sb)
     assert_close(bf16_to_f64(D), X, S, K // 128, f"decode {M}x{N}x{K}")
+
+
+def test_workspace_rules(gpu_lib, monkeypatch):
+    """gemm_fp8_nt_ws: a workspace below fg_nt_workspace_bytes is rejected
+    before anything runs; NULL selects gemm_fp8_nt's unsplit plan (same bits
+    as the C entry point gemm_fp8_nt); a workspace that already served other
+    shapes gives the same bits as a fresh zero-filled one."""
+    monkeypatch.delenv("FG_FORCE_CONFIG", raising=False)
+    monkeypatch.delenv("FG_SKINNY", raising=False)
+    M, N, K = 64, 2112, 2048
+    announce(f"skinny workspace rules {M}x{N}x{K}")
+    A32, B32 = synth.dense_problem(M, N, K, seed=13)
+    qa, sa, qb, sb = quantize_dense(A32, B32)
+    a, s_a, b, s_b = dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb)
+    need = gpu_lib.nt_workspace_bytes(M, N, K)
+    assert need > 64 * 1024  # the decode plan splits K
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+    D = sentinel_like((M, N))
+    with pytest.raises(gpu_lib.FP8GemmError, match="workspace of"):
+        gpu_lib.gemm_fp8_nt(a, s_a, b, s_b, D, workspace=small)
+    torch.cuda.synchronize()
+    assert (bf16_bits(D) == SENTINEL_BF16).all()  # nothing was launched
+    unsplit = sentinel_like((M, N))
+    gpu_lib.gemm_fp8_nt_unsplit(a, s_a, b, s_b, unsplit)
+    lib = gpu_lib.load_library()
+    null_ws = sentinel_like((M, N))
+    st = lib.gemm_fp8_nt_ws(a.data_ptr(), K, s_a.data_ptr(), s_a.stride(0), b.data_ptr(), K, s_b.data_ptr(),
+                            null_ws.data_ptr(), N, M, N, K, None, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.fg_last_error()
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(null_ws), bf16_bits(unsplit))
+    X, S = oracle_dense(qa, sa, qb, sb)
+    assert_close(bf16_to_f64(unsplit), X, S, K // 128, "unsplit plan")
+    # a workspace reused across shapes keeps its counters at zero
+    ws = torch.zeros(gpu_lib.load_library().fg_nt_workspace_max_bytes(), dtype=torch.uint8, device="cuda")
+    fresh = bf16_bits(run_dense(gpu_lib, qa, sa, qb, sb))
+    for (m2, n2, k2) in [(32, 4096, 7168), (128, 300, 4096), (M, N, K)]:
+        A2, B2 = synth.dense_problem(m2, n2, k2, seed=m2 + n2)
+        q2 = quantize_dense(A2, B2)
+        D2 = torch.empty(m2, n2, dtype=torch.bfloat16, device="cuda")
+        gpu_lib.gemm_fp8_nt(dev_u8(q2[0]), dev_sa(q2[1]), dev_u8(q2[2]), dev_f32(q2[3]), D2, workspace=ws)
+    Dw = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.gemm_fp8_nt(a, s_a, b, s_b, Dw, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(Dw), fresh)
+    assert (ws[:64 * 1024] == 0).all()  # counters left at zero
