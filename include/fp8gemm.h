@@ -112,6 +112,25 @@ fg_status gemm_fp8_nt_ws(const uint8_t* A, int64_t lda, const float* sa, int64_t
                          uint16_t* D, int64_t ldd, int M, int N, int K,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * gemm_fp8_nt_ws for callers that cannot allocate device memory at all (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same plan and the same results, bit for bit, as
+ * gemm_fp8_nt_ws with a large enough workspace, with the split-K buffers in
+ * a scratch array of the library instead: 8 MiB + 64 KiB per GPU, a static
+ * device array that each GPU the library runs on holds until the process
+ * ends.  Each split call clears the arrival counters it uses (a small fill
+ * kernel, no memset) before its GEMM.  Every call on one GPU shares that
+ * GPU's scratch, so calls that overlap in time on one GPU (other streams,
+ * graphs replayed concurrently) race; serialise them.  The plan never needs
+ * more scratch than the array holds (the split is bounded by it); a plan that
+ * did would return FG_EUNSUPPORTED.  Nothing is allocated; everything else as
+ * gemm_fp8_nt.
+ */
+fg_status gemm_fp8_nt_noalloc(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
+                              const uint8_t* B, int64_t ldb, const float* sb,
+                              uint16_t* D, int64_t ldd, int M, int N, int K, void* stream);
+
 /* Workspace bytes gemm_fp8_nt_ws needs for (M, N, K) on the current device:
  * 0 when its plan does not split K, else 64 KiB of counters plus the
  * partials.  -1 for a negative size or when the device cannot be queried. */

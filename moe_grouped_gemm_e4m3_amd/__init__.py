@@ -65,6 +65,7 @@ _I = ctypes.c_int
 _SIGNATURES = {
     "gemm_fp8_nt": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
     "gemm_fp8_nt_ws": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P, _I64, _P]),
+    "gemm_fp8_nt_noalloc": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I, _I, _I, _P]),
     "fg_nt_workspace_bytes": (_I64, [_I, _I, _I]),
     "fg_nt_workspace_max_bytes": (_I64, []),
     "gemm_fp8_nt_c": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I, _I, _I, _P]),

@@ -65,6 +65,7 @@ struct DeviceInfo {
   int cus = 0;
   bool ok = false;
   int* check_word = nullptr;  // device address of this device's g_check_word
+  void* scratch = nullptr;    // device address of this device's scratch array
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
@@ -270,7 +271,32 @@ constexpr int64_t kSplitPartialMax = (int64_t)8 << 20;                // 8 MiB
 struct SplitWs {
   void* base = nullptr;  // counters, then partials
   int64_t bytes = 0;
+  bool scratch = false;  // use this device's scratch array (base is looked up)
 };
+
+// Scratch of gemm_fp8_nt_noalloc: the split-K workspace of the largest plan
+// (64 KiB of counters + 8 MiB of partials), one copy per device, for callers
+// that cannot allocate.  Host code never uses the name itself (on the host it
+// is a stand-in, not a device address): each device's address is looked up
+// once with hipGetSymbolAddress and kept in g_dev.
+constexpr int64_t kScratchBytes = kSplitCounterBytes + kSplitPartialMax;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+fg_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FG_EHIP, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev[dev].scratch) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(FG_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_dev[dev].scratch = ptr;
+  }
+  *out = g_dev[dev].scratch;
+  return FG_OK;
+}
 
 // Width of the large kernel's 256-row tile.  The persistent grid runs whole
 // tiles in rounds and a tile's time grows with its width, so the width with
@@ -490,11 +516,25 @@ fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, const SplitWs* 
     // the plan only splits when the call brought a workspace
     const int64_t need = kSplitCounterBytes + pl.partial_bytes();
     if (!ws || pl.units > kSkinnyMaxUnits) return fail(FG_EINVAL, "%s: the K split needs a workspace", what);
-    if (ws->bytes < need)
+    void* base = ws->base;
+    if (ws->scratch) {
+      if (need > kScratchBytes)
+        return fail(FG_EUNSUPPORTED, "%s: the plan needs %lld bytes of scratch, above the %lld this entry point has",
+                    what, (long long)need, (long long)kScratchBytes);
+      FG_TRY(scratch_ptr(&base));
+    } else if (ws->bytes < need) {
       return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
                   (long long)ws->bytes, (long long)need);
-    p.ws_counters = (int*)ws->base;
-    p.ws_partials = (float*)((uint8_t*)ws->base + kSplitCounterBytes);
+    }
+    p.ws_counters = (int*)base;
+    p.ws_partials = (float*)((uint8_t*)base + kSplitCounterBytes);
+    if (ws->scratch) {
+      // a shared scratch keeps whatever an earlier call left: start from zero
+      hipLaunchKernelGGL(fg::zero_ints_kernel, dim3((unsigned)((pl.units + 255) / 256)), dim3(256), 0, stream,
+                         p.ws_counters, (int)pl.units);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(FG_EHIP, "%s counter clear launch: %s", what, hipGetErrorString(e));
+    }
   }
 #define FG_SKINNY_CASE(MF, CF) \
   if (pl.mf == MF && pl.cf == CF) return launch_skinny_cfg<MF, CF, ADD_C>(p, pl.splits, pl.parts, stream, what);
@@ -836,6 +876,17 @@ fg_status gemm_fp8_nt_ws(const uint8_t* A, int64_t lda, const float* sa, int64_t
   fg::GemmParams p{};
   return dense_nt<fg::kDense>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, workspace ? &ws : nullptr, stream,
                               what);
+}
+
+fg_status gemm_fp8_nt_noalloc(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B,
+                              int64_t ldb, const float* sb, uint16_t* D, int64_t ldd, int M, int N, int K,
+                              void* stream) {
+  const char* what = "gemm_fp8_nt_noalloc";
+  g_err.clear();
+  SplitWs ws;
+  ws.scratch = true;
+  fg::GemmParams p{};
+  return dense_nt<fg::kDense>(p, A, lda, sa, ld_sa, B, ldb, sb, D, ldd, M, N, K, &ws, stream, what);
 }
 
 fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B,

@@ -330,4 +330,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   if (tid == 0) __hip_atomic_store(p.ws_counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Zero n ints (the split-K arrival counters of a shared scratch), without a
+// memset node, so that the launch can be captured into a graph.
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace fg

@@ -63,6 +63,8 @@ int main() {
   EXPECT(gemm_fp8_nt_ws(A, 512, S, 64, A, 512, S, D, 256, 64, 256, 512, (void*)0x10010, 4096, nullptr), FG_EALIGN);
   EXPECT(gemm_fp8_nt_ws(A, 512, S, 64, A, 512, S, D, 256, 64, 256, 512, WS, big, nullptr), DEV);
   EXPECT(gemm_fp8_nt_ws(A, 512, S, 64, A, 512, S, D, 256, 64, 256, 512, nullptr, 0, nullptr), DEV);
+  EXPECT(gemm_fp8_nt_noalloc(A, 512, S, 64, A, 512, S, D, 256, 64, 256, 100, nullptr), FG_EALIGN);
+  EXPECT(gemm_fp8_nt_noalloc(A, 512, S, 64, A, 512, S, D, 256, 64, 256, 512, nullptr), DEV);
   if (fg_nt_workspace_bytes(-1, 1, 1) != -1) ++g_fail;
   if (fg_nt_workspace_max_bytes() != (int64_t)(8 << 20) + (64 << 10)) ++g_fail;
   (void)fg_nt_workspace_bytes(64, 2112, 7168);  // -1 without a device
