@@ -84,8 +84,9 @@ def gemm_blockwise(A, sa, B, sb, with_magnitude: bool = False):
     return (X, S) if with_magnitude else X
 
 
-def gemm_dequant(A, sa, B, sb):
-    """Form (ii): dequantise both operands exactly, then one float64 matmul."""
+def gemm_dequant(A, sa, B, sb, with_magnitude: bool = False):
+    """Form (ii): dequantise both operands exactly, then one float64 matmul
+    (and, with ``with_magnitude``, S = |a| @ |b|.T of the same operands)."""
     A = np.asarray(A, np.uint8)
     B = np.asarray(B, np.uint8)
     sa = np.asarray(sa, np.float32)
@@ -95,7 +96,10 @@ def gemm_dequant(A, sa, B, sb):
     nblk = np.arange(N) // GROUP
     a = decode(A) * sa[kblk, :M].T.astype(np.float64)
     b = decode(B) * sb[nblk][:, kblk].astype(np.float64)
-    return a @ b.T
+    X = a @ b.T
+    if with_magnitude:
+        return X, np.abs(a) @ np.abs(b).T
+    return X
 
 
 def gemm_nt(A, sa, B, sb, with_magnitude: bool = False):

@@ -325,6 +325,10 @@ def test_k_tail_gemm_matches_bruteforce(M, N, K):
         assert abs(Fraction(float(X[m, n])) - Xe[m, n]) <= Fraction(2) ** -50 * Se[m, n]
         assert abs(Fraction(float(S[m, n])) - Se[m, n]) <= Fraction(2) ** -50 * Se[m, n]
     assert np.allclose(X, gemm.gemm_dequant(A, sa, B, sb), rtol=0, atol=1e-12 * S.max())
+    # the dequantised form's magnitude against the exact sums as well
+    _, S2 = gemm.gemm_dequant(A, sa, B, sb, with_magnitude=True)
+    for m, n in itertools.product(range(M), range(N)):
+        assert abs(Fraction(float(S2[m, n])) - Se[m, n]) <= Fraction(2) ** -50 * Se[m, n]
 
 
 def test_k_tail_quantisers_match_torch_on_their_own_columns():
@@ -357,6 +361,9 @@ def test_two_oracle_forms_agree():
     X1, S = gemm.gemm_blockwise(A, sa, B, sb, with_magnitude=True)
     X2 = gemm.gemm_dequant(A, sa, B, sb)
     assert (np.abs(X1 - X2) <= 1e-12 * S).all()
+    X3, S3 = gemm.gemm_dequant(A, sa, B, sb, with_magnitude=True)
+    assert np.array_equal(X3, X2)
+    assert (np.abs(S3 - S) <= 1e-12 * S).all()
 
 
 def test_gemm_closed_form_constant_codes():
