@@ -9,17 +9,24 @@ accumulation is imprecise and is compensated by promotion (GeekNews topic
 19444, opening bullets).
 
 Reading of "per-element relative error <= 1e-2": taken literally it cannot
-hold where X cancels to ~0, since any fp32 accumulation in any order is off
-by up to the rounding bound below.  The per-element test is therefore
+hold where X cancels to ~0, since any accumulation in any order is off by up
+to the rounding bound below.  The per-element test is therefore
 
-    |y - X| <= 1e-2 * |X| + eps,   eps = 2^-24 * (128 + Kb + 2) * S
+    |y - X| <= 1e-2 * |X| + eps,   eps = (2^-14 + 2^-24 * (Kb + 3)) * S
 
-eps is the first-order worst case of fp32 accumulation: up to 127 roundings
-inside a 128-term slice sum, one for the scale product sa*sb, one per slice
-promotion FMA (Kb of them), and one more of slack; each rounding is bounded
-by 2^-24 times a partial sum of magnitudes <= S.  The final bf16 rounding
-(relative 2^-8) sits inside the 1e-2 term.  The literal count is reported
-too, for information.
+The first term is the matrix core's own sum of a 128-term slice.  The pages
+say only that FP8 accumulation inside the matrix core is imprecise and that
+promotion at every 128 elements compensates; they give no figure.  Reading:
+each slice's partial is within 2^-14 of the slice's magnitude sum(|a*b|)
+(the slice magnitudes, times their scales, add up to S).  gfx950's FP8 MFMA
+is not a sequence of IEEE fp32 additions: on a one-slice problem it was
+measured up to 162 * 2^-24 of S away from the exact sum, beyond the 127
+fp32 roundings of a sequential sum; 2^-14 leaves a factor of about 6.  The
+second term is fp32 outside the matrix core: one rounding for the scale
+product sa*sb, one per slice promotion FMA (Kb of them), one for an addend
+and one of slack, each bounded by 2^-24 times a partial sum of magnitudes
+<= S.  The final bf16 rounding (relative 2^-8) sits inside the 1e-2 term.
+The literal count is reported too, for information.
 """
 
 from __future__ import annotations
@@ -27,11 +34,12 @@ from __future__ import annotations
 import numpy as np
 
 U32 = 2.0 ** -24
+SLICE_SUM = 2.0 ** -14  # matrix-core error of one slice, relative to its magnitude
 
 
 def accumulation_bound(S: np.ndarray, Kb: int) -> np.ndarray:
     """eps per element for a K of Kb 128-slices."""
-    return U32 * (128 + Kb + 2) * np.asarray(S, np.float64)
+    return (SLICE_SUM + U32 * (Kb + 3)) * np.asarray(S, np.float64)
 
 
 def similarity_defect(y, x) -> float:

@@ -511,6 +511,33 @@ def test_metrics_accept_fp32_promotion_and_reject_dropped_slice():
     assert not metrics.check_result(-y, X, S, Kb)["ok"]
 
 
+@pytest.mark.parametrize("bits,ok", [(16, True), (12, False)])
+def test_metrics_level_of_the_matrix_core_term(bits, ok):
+    """A slice sum that aligns its 128 products to the largest one's exponent
+    and truncates each to `bits` bits below it: with 16 bits (coarser than
+    any error measured on the device) it stays inside the bound, with 12 the
+    cancelling sums, where the 1e-2 term gives no room, fall outside."""
+    rng = np.random.default_rng(31)
+    M, N, K = 48, 64, 384
+    A = rng.integers(0, 0x7F, (M, K), dtype=np.uint8)
+    B = rng.integers(0, 0x7F, (N, K), dtype=np.uint8)
+    A[:, ::2] |= 0x80  # half the products negative: sums cancel
+    sa = np.ones((K // 128, M), np.float32)
+    sb = np.ones((1, K // 128), np.float32)
+    X, S = gemm.gemm_nt(A, sa, B, sb, with_magnitude=True)
+    da, db = torch_decode(A).astype(np.float64), torch_decode(B).astype(np.float64)
+    acc = np.zeros((M, N), np.float32)
+    for kb in range(K // 128):
+        ks = slice(kb * 128, kb * 128 + 128)
+        prod = da[:, None, ks] * db[None, :, ks]  # exact
+        top = np.floor(np.log2(np.maximum(np.abs(prod).max(axis=2, keepdims=True), 2.0 ** -40)))
+        q = 2.0 ** (top - bits)
+        P = (np.trunc(prod / q) * q).sum(axis=2).astype(np.float32)
+        acc = (acc + P).astype(np.float32)
+    y = e4m3.bf16_bits_to_f64(e4m3.bf16_rne_bits(acc.astype(np.float64)))
+    assert metrics.check_result(y, X, S, K // 128)["ok"] == ok
+
+
 def test_planted_decode_mistake_is_caught(monkeypatch):
     """Mutate the oracle's decode table (flip the sign of one code) and show
     the brute-force pin no longer passes."""

@@ -2,7 +2,7 @@
 
 Tolerances: bit-exact in the exactly representable regime (integer codes,
 power-of-two scales), otherwise the oracle's per-element bound
-|y - X| <= 1e-2 |X| + 2^-24 (128 + Kb + 2) S plus a similarity defect below
+|y - X| <= 1e-2 |X| + (2^-14 + 2^-24 (Kb + 3)) S plus a similarity defect below
 1e-3 (``oracle.metrics``)."""
 
 from __future__ import annotations
