@@ -168,14 +168,22 @@ fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t 
  * fp32 [Kb][ld_sa] (1x128 along K for each of the M rows), sb fp32 [Nb][Kb]
  * (128x128 blocks of the [N, K] operand).  C: fp32 [M, N] addend (row stride
  * ldc >= N) or NULL for none.  D: as in gemm_fp8_nt.  An operand stored MN-major
- * has no alignment requirement.
- * Each MN-major operand is first transposed, K-major, into the caller's
- * device workspace (a byte copy bound by HBM), then the NT kernels run on the
- * copy.  workspace must be 16-byte aligned and hold at least
- * fg_layout_workspace_bytes(layout, M, N, K) bytes (FG_EINVAL otherwise); it is
- * in use until the call's work on `stream` has finished.  Transposed rows must
- * fit 4 MiB (K <= 2^22) and the stored [K, .] operands at most 65535*128 rows
- * (FG_EUNSUPPORTED).  K % 16 == 0.  Nothing is allocated.
+ * has no alignment requirement on the copying path.
+ * The workspace selects one of two paths:
+ *  - workspace_bytes > 0: each MN-major operand is first transposed, K-major,
+ *    into the caller's device workspace (a byte copy bound by HBM), then the
+ *    NT kernels run on the copy.  workspace must be 16-byte aligned and hold
+ *    at least fg_layout_workspace_bytes(layout, M, N, K) bytes (FG_EINVAL
+ *    otherwise).  It is in use until the call's work on `stream` has
+ *    finished.  The stored [K, .] operands have at most 65535*128 rows
+ *    (FG_EUNSUPPORTED).  The faster path.
+ *  - workspace_bytes == 0 (workspace ignored): no copy; the large-tile
+ *    kernel stages each MN-major operand as stored.  Each such operand must
+ *    be 16-byte aligned with a row stride and a column count (M for A, N for
+ *    B) that are multiples of 16 (FG_EALIGN otherwise).  Measured 25-45 %
+ *    slower than the copies on MI355X; for callers without device memory
+ *    to spare.
+ * K <= 2^22 (FG_EUNSUPPORTED).  K % 16 == 0.  Nothing is allocated.
  */
 fg_status gemm_fp8_nn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                       const uint8_t* B, int64_t ldb, const float* sb, const float* C, int64_t ldc,
@@ -208,11 +216,19 @@ int64_t fg_layout_workspace_bytes(const char* layout, int M, int N, int K);
  *   C   device fp32 [G, M, N] addend, contiguous, or NULL
  *   D   device bf16 [G, M, N], contiguous; written
  * Group g uses the factors of its own K groups (columns k_g/128 .. of sa
- * and sb).  Both operands are transposed K-major into the caller's device
- * workspace (16-byte aligned, at least fg_k_grouped_workspace_bytes(M, N,
- * K_total) bytes; FG_EINVAL otherwise), then one NT GEMM per group runs on
- * its K columns of the copies, all on `stream`.  K_total <= 2^22 and at most
- * 65535*128 (FG_EUNSUPPORTED).  Nothing is allocated.
+ * and sb).  Groups with ks[g] = 0 get D[g] = C[g] (or 0) from a fill
+ * kernel; the groups with K rows run as one persistent launch (one per run
+ * of 256 such groups), all on `stream`.  The workspace selects how the
+ * operands are read:
+ *  - workspace_bytes > 0: both are transposed K-major into the caller's
+ *    device workspace (16-byte aligned, at least
+ *    fg_k_grouped_workspace_bytes(M, N, K_total) bytes; FG_EINVAL
+ *    otherwise), which is in use until the call's work on `stream` has
+ *    finished.  The faster path.
+ *  - workspace_bytes == 0 (workspace ignored): no copy; the kernel stages A
+ *    and B as stored.  They must be 16-byte aligned, with lda, ldb, M and N
+ *    multiples of 16 (FG_EALIGN otherwise).
+ * K_total <= 2^22 (FG_EUNSUPPORTED).  Nothing is allocated.
  */
 fg_status gemm_fp8_k_grouped_tn_contiguous(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,
                                            const uint8_t* B, int64_t ldb, const float* sb,

@@ -330,7 +330,9 @@ def _gemm_layout(layout, A, sa, B, sb, D, C, stream, workspace):
 def gemm_fp8_nn(A, sa, B, sb, D, C=None, stream=None, workspace=None):
     """D[M,N] = bf16(C + A . B), A [M, K], B stored [K, N].  Scales as for
     gemm_fp8_nt (sb: 128x128 blocks of the logical [N, K] operand).  The
-    workspace (layout_workspace_bytes) comes from torch's allocator if not given."""
+    workspace (layout_workspace_bytes) comes from torch's allocator if not
+    given; an empty one (0 bytes) runs without copies, on the operands as
+    stored (MN-major ones then need 16-byte rows and M, N multiples of 16)."""
     return _gemm_layout("nn", A, sa, B, sb, D, C, stream, workspace)
 
 
@@ -358,7 +360,9 @@ def gemm_fp8_k_grouped_tn_contiguous(A, sa, B, sb, ks, D, C=None, stream=None, w
     A [K_total, M] and B [K_total, N] (uint8 / e4m3, row-contiguous); sa fp32
     [K_total/128, M] view; sb fp32 [Nb, K_total/128]; ks: host sequence of
     group sizes (multiples of 128); D bf16 [G, M, N] and C fp32 [G, M, N]
-    contiguous.  The workspace comes from torch's allocator if not given."""
+    contiguous.  The workspace comes from torch's allocator if not given; an
+    empty one (0 bytes) runs without copies, on A and B as stored (they then
+    need 16-byte rows and M, N multiples of 16)."""
     A, B = _fp8(A, "A"), _fp8(B, "B")
     sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
     if C is not None:

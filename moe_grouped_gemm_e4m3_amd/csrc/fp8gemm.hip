@@ -233,19 +233,24 @@ fg_status launch_gemm(fg::GemmParams& p, hipStream_t stream, const char* what) {
 // long K a band's A and B stream through L2 for a long time, and a taller
 // band reuses each B column block across more row blocks: measured on the
 // M=4096 shapes, 16 rows is 3 % faster at K=16384 and 4-5 % slower at K=1536.
-int raster_band(int K) { return K >= 8192 ? 16 : 8; }
+int raster_band(int K) {
+  const char* f = getenv("FG_RASTER_BAND");  // tuning
+  if (f && atoi(f) > 0) return atoi(f);
+  return K >= 8192 ? 16 : 8;
+}
 
 // K % 128 != 0 runs a build of the kernel whose last slice clips its loads
 // at column K; whole-slice problems keep the build without that code.
-template <class C, int L, bool KTAIL>
+template <class C, int L, bool KTAIL, bool TA = false, bool TB = false>
 fg_status launch_big_k(fg::GemmParams& p, hipStream_t stream, const char* what) {
   static int occ_cache = 0;
-  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L, KTAIL>, C::THREADS, &occ_cache);
+  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L, KTAIL, TA, TB>, C::THREADS, &occ_cache);
   p.group_m = raster_band(p.K);
   int64_t grid = 0;
   FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
   print_config(what, p, C::BM, C::BN, C::THREADS, grid, occ);
-  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L, KTAIL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L, KTAIL, TA, TB>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
@@ -481,11 +486,21 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
   }
   // 32-column tiles for one row part; with two parts, 64-column ones (each
   // workgroup then reads as many weight bytes per activation byte as a
-  // one-part 32-column tile, and the parts double the workgroups)
+  // one-part 32-column tile, and the parts double the workgroups).  A long
+  // K range (32 slices or more) with one row part and a workspace takes
+  // 64-column tiles split four ways instead: a CU then fetches half the
+  // activation bytes per weight byte, which is what these launches are bound
+  // by (measured at M = 64, K = 7168: 7-8 % faster at N = 2112 and 4096).
   pl.cf = pl.parts > 1 ? 4 : 2;
+  const bool wide = split_ok && pl.parts == 1 && Kb >= 32;
+  if (wide) pl.cf = 4;
   pl.units = units_of(pl.cf);
   int sp = 1;
-  if (split_ok && pl.units * 4 < (int64_t)cus * 3) sp = pl.units * 4 >= cus ? 2 : 4;
+  if (wide) {
+    sp = 4;
+  } else if (split_ok && pl.units * 4 < (int64_t)cus * 3) {
+    sp = pl.units * 4 >= cus ? 2 : 4;
+  }
   while (sp > 1 && (Kb < 4 * sp || !fits(pl.cf, sp))) sp /= 2;
   pl.splits = sp;
   *out = pl;
@@ -658,6 +673,31 @@ fg_status launch_transpose(const uint8_t* in, int64_t ld_in, uint8_t* out, int64
   return FG_OK;
 }
 
+// An MN-major operand ([K, M] or [K, N]) of `ext` columns can be staged by
+// the large kernel as stored when its rows start on 16-byte boundaries and
+// end on one (the kernel reads whole 16-byte chunks up to column ext).
+bool mn_direct(const void* x, int64_t ld, int ext) {
+  return x && aligned(x, 16) && ld % 16 == 0 && ld <= kMaxLd && ext % 16 == 0;
+}
+
+// The large kernel on the operands as stored (TA / TB: MN-major), 256x256 tiles.
+template <bool TA, bool TB>
+fg_status launch_layout_direct(fg::GemmParams& p, hipStream_t stream, const char* what) {
+  using Cfg = CfgBig;
+  p.tiles_m = (p.rows + Cfg::BM - 1) / Cfg::BM;
+  p.tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t slots = (int64_t)p.tiles_m * p.tiles_n;
+  if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
+  p.num_tiles = (int)slots;
+  // K tails matter only to a K-major operand (an MN-major one reads rows past K as zeros)
+  const bool ktail = !(TA && TB) && (p.K & 127) != 0;
+  if (p.Cin)
+    return ktail ? launch_big_k<Cfg, fg::kDenseC, true, TA, TB>(p, stream, what)
+                 : launch_big_k<Cfg, fg::kDenseC, false, TA, TB>(p, stream, what);
+  return ktail ? launch_big_k<Cfg, fg::kDense, true, TA, TB>(p, stream, what)
+               : launch_big_k<Cfg, fg::kDense, false, TA, TB>(p, stream, what);
+}
+
 template <bool TA, bool TB>
 fg_status gemm_layout(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa, const uint8_t* B, int64_t ldb,
                       const float* sb, const float* C, int64_t ldc, uint16_t* D, int64_t ldd, int M, int N, int K,
@@ -671,6 +711,37 @@ fg_status gemm_layout(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
   if (C) FG_TRY(check_ld(ldc, N, 1, "ldc"));
   const uint8_t* a = A;
   const uint8_t* b = B;
+  // Without a workspace the large kernel stages the MN-major operands as
+  // stored and the transposing LDS reads turn them into MFMA fragments.
+  if (K > 0 && (TA || TB) && workspace_bytes == 0) {
+    if ((TA && !mn_direct(A, lda, M)) || (TB && !mn_direct(B, ldb, N)))
+      return fail(FG_EALIGN,
+                  "%s without a workspace: an MN-major operand needs 16-byte aligned rows, a row stride and a column "
+                  "count that are multiples of 16",
+                  what);
+    if (TA) FG_TRY(check_ld(lda, M, 1, "lda"));
+    if (TB) FG_TRY(check_ld(ldb, N, 1, "ldb"));
+    if (K > kMaxLd) return fail(FG_EUNSUPPORTED, "K=%d above 4 Mi rows", K);
+    FG_TRY(check_ptr(D, 2, "D"));
+    FG_TRY(check_ld(ldd, N, 1, "ldd"));
+    FG_TRY(check_ptr(sa, 4, "sa"));
+    FG_TRY(check_ptr(sb, 4, "sb"));
+    FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
+    if (!TA) {
+      FG_TRY(check_ptr(A, 16, "A"));
+      FG_TRY(check_ld(lda, K, 16, "lda"));
+    }
+    if (!TB) {
+      FG_TRY(check_ptr(B, 16, "B"));
+      FG_TRY(check_ld(ldb, K, 16, "ldb"));
+    }
+    FG_TRY(check_row_bytes(lda, ldb));
+    fg::GemmParams p{};
+    p.A = A; p.lda = lda; p.sa = sa; p.ld_sa = ld_sa; p.B = B; p.ldb = ldb; p.sb = sb; p.D = D; p.ldd = ldd;
+    p.Cin = C; p.ldc = ldc;
+    p.rows = M; p.N = N; p.K = K; p.G = 1; p.Kb = ceil128(K); p.Nb = ceil128(N); p.ld_sb = p.Kb;
+    return launch_layout_direct<TA, TB>(p, (hipStream_t)stream, what);
+  }
   if (K > 0 && (TA || TB)) {
     if (TA) {
       FG_TRY(check_ptr(A, 1, "A"));
@@ -796,52 +867,98 @@ fg_status gemm_fp8_k_grouped_tn_contiguous(const uint8_t* A, int64_t lda, const 
   FG_TRY(check_ptr(D, 2, "D"));
   if (C) FG_TRY(check_ptr(C, 4, "C"));
   const int Kbt = (int)(K_total / 128);
-  const uint8_t* at = nullptr;
-  const uint8_t* bt = nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  // With a workspace both operands are transposed K-major into it (the
+  // faster path: the K-major staging streams at the NT kernel's rate);
+  // without one the kernel stages them as stored.
+  const bool mn = workspace_bytes == 0;
   if (K_total > 0) {
-    FG_TRY(check_ptr(A, 1, "A"));
-    FG_TRY(check_ptr(B, 1, "B"));
     FG_TRY(check_ptr(sa, 4, "sa"));
     FG_TRY(check_ptr(sb, 4, "sb"));
     FG_TRY(check_ld(lda, M, 1, "lda"));
     FG_TRY(check_ld(ldb, N, 1, "ldb"));
     FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
-    const int64_t need = fg_k_grouped_workspace_bytes(M, N, K_total);
-    if (workspace_bytes < need)
-      return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
-                  (long long)workspace_bytes, (long long)need);
-    FG_TRY(check_ptr(workspace, 16, "workspace"));
-    uint8_t* ws = (uint8_t*)workspace;
-    FG_TRY(launch_transpose(A, lda, ws, K_total, (int)K_total, M, (hipStream_t)stream, what));
-    FG_TRY(launch_transpose(B, ldb, ws + ws_round((int64_t)M * K_total), K_total, (int)K_total, N,
-                            (hipStream_t)stream, what));
-    at = ws;
-    bt = ws + ws_round((int64_t)M * K_total);
-  }
-  // one dense NT GEMM per group on its K columns of the transposed copies;
-  // sb keeps its full row stride (Kb_total)
-  int64_t k0 = 0;
-  for (int g = 0; g < G; ++g) {
-    const int kg = ks[g];
-    const int64_t kb0 = k0 / 128;
-    fg::GemmParams p{};
-    p.ld_sb = Kbt > 0 ? Kbt : 1;
-    uint16_t* Dg = D + (int64_t)g * M * N;
-    const uint8_t* ag = at ? at + k0 : nullptr;
-    const uint8_t* bg = bt ? bt + k0 : nullptr;
-    const float* sag = kg ? sa + kb0 * ld_sa : sa;
-    const float* sbg = kg ? sb + kb0 : sb;
-    const int64_t ldt = K_total > 0 ? K_total : 16;
-    fg_status st;
-    if (C) {
-      p.Cin = C + (int64_t)g * M * N;
-      p.ldc = N;
-      st = dense_nt<fg::kDenseC>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, nullptr, stream, what);
+    if (mn) {
+      if (!mn_direct(A, lda, M) || !mn_direct(B, ldb, N))
+        return fail(FG_EALIGN,
+                    "%s without a workspace: A and B need 16-byte aligned rows, row strides and M, N that are "
+                    "multiples of 16",
+                    what);
     } else {
-      st = dense_nt<fg::kDense>(p, ag, ldt, sag, ld_sa, bg, ldt, sbg, Dg, N, M, N, kg, nullptr, stream, what);
+      FG_TRY(check_ptr(A, 1, "A"));
+      FG_TRY(check_ptr(B, 1, "B"));
+      const int64_t need = fg_k_grouped_workspace_bytes(M, N, K_total);
+      if (workspace_bytes < need)
+        return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
+                    (long long)workspace_bytes, (long long)need);
+      FG_TRY(check_ptr(workspace, 16, "workspace"));
     }
-    if (st != FG_OK) return st;
-    k0 += kg;
+  }
+  // groups without K rows: D[g] = C[g] (or 0)
+  for (int g = 0; g < G; ++g) {
+    if (ks[g] > 0) continue;
+    const int64_t n = (int64_t)M * N;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL(fg::fill_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, D + (int64_t)g * M * N,
+                       C ? C + (int64_t)g * M * N : nullptr, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FG_EHIP, "%s fill launch: %s", what, hipGetErrorString(e));
+  }
+  if (K_total == 0) return FG_OK;
+  fg::GemmParams p{};
+  fg::KGroups kg{};
+  if (mn) {
+    p.A = A; p.lda = lda; p.B = B; p.ldb = ldb;
+    kg.a_step = 128 * lda;
+    kg.b_step = 128 * ldb;
+  } else {
+    uint8_t* ws = (uint8_t*)workspace;
+    FG_TRY(launch_transpose(A, lda, ws, K_total, (int)K_total, M, st, what));
+    FG_TRY(launch_transpose(B, ldb, ws + ws_round((int64_t)M * K_total), K_total, (int)K_total, N, st, what));
+    p.A = ws; p.lda = K_total; p.B = ws + ws_round((int64_t)M * K_total); p.ldb = K_total;
+    kg.a_step = 128;
+    kg.b_step = 128;
+  }
+  using Cfg = CfgBig;
+  p.sa = sa; p.ld_sa = ld_sa; p.sb = sb; p.ld_sb = Kbt;
+  p.D = D; p.ldd = N; p.Cin = C; p.ldc = N;
+  p.rows = M; p.N = N; p.K = (int)K_total; p.G = G; p.Kb = Kbt; p.Nb = ceil128(N);
+  p.tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+  p.tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+  static int occ_mn = 0, occ_k = 0;
+  const int occ = mn ? occupancy_of(fg::gemm_fp8_k_grouped_kernel<Cfg, true>, Cfg::THREADS, &occ_mn)
+                     : occupancy_of(fg::gemm_fp8_k_grouped_kernel<Cfg, false>, Cfg::THREADS, &occ_k);
+  // one persistent launch per run of at most kMaxKGroups groups with K rows
+  int64_t kb = 0;
+  for (int g0 = 0; g0 < G;) {
+    kg.n = 0;
+    int g = g0;
+    for (; g < G && kg.n < fg::kMaxKGroups; ++g) {
+      if (ks[g] > 0) {
+        kg.g[kg.n] = g;
+        kg.kb0[kg.n] = (int)kb;
+        ++kg.n;
+      }
+      kb += ks[g] / 128;
+    }
+    kg.kb0[kg.n] = (int)kb;
+    g0 = g;
+    if (kg.n == 0) continue;
+    const int64_t slots = (int64_t)kg.n * p.tiles_m * p.tiles_n;
+    if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
+    p.num_tiles = (int)slots;
+    p.group_m = raster_band((int)((kg.kb0[kg.n] - kg.kb0[0]) * 128 / kg.n));
+    int64_t grid = 0;
+    FG_TRY(launch_grid(occ, p.num_tiles, &grid));
+    print_config(what, p, Cfg::BM, Cfg::BN, Cfg::THREADS, grid, occ);
+    if (mn)
+      hipLaunchKernelGGL((fg::gemm_fp8_k_grouped_kernel<Cfg, true>), dim3((unsigned)grid), dim3(Cfg::THREADS), 0, st,
+                         p, kg);
+    else
+      hipLaunchKernelGGL((fg::gemm_fp8_k_grouped_kernel<Cfg, false>), dim3((unsigned)grid), dim3(Cfg::THREADS), 0,
+                         st, p, kg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   }
   return FG_OK;
 }

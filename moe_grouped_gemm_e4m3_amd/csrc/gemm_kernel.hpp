@@ -38,7 +38,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // kDenseC is the dense GEMM with an fp32 addend, D = C + A B^T: it runs
 // exactly as kDense except that the epilogue adds C before the BF16 rounding.
-enum LayoutKind { kDense = 0, kContiguous = 1, kMasked = 2, kDenseC = 3 };
+// kKGrouped is the K-grouped GEMM of weight gradients, D[g] = C[g] + A_g^T B_g,
+// on its operands as stored ([K, M] / [K, N]) or on K-major copies (see KGroups).
+enum LayoutKind { kDense = 0, kContiguous = 1, kMasked = 2, kDenseC = 3, kKGrouped = 4 };
+
+// The K-grouped GEMM's groups with work, in order: the output index of each
+// and its first 128-deep K slice (kb0[n] is the end), and how far one slice
+// moves each operand (128 rows of an MN-major operand, 128 bytes of a
+// K-major one).  A kernel argument.
+constexpr int kMaxKGroups = 256;
+struct KGroups {
+  int n;
+  int g[kMaxKGroups];
+  int kb0[kMaxKGroups + 1];
+  int64_t a_step, b_step;
+};
 
 struct GemmParams {
   const uint8_t* A;  // dense/contiguous: [rows, K] (lda); masked: [G, M_cap, K] packed
@@ -101,19 +115,23 @@ __device__ __forceinline__ void raster(int w, int tiles_m, int tiles_n, int grou
 // !valid and at columns >= N), added to the accumulator before the single BF16
 // rounding.  Callers issue every load of an epilogue pass before the first
 // use, so the pass waits for memory once.
-__device__ __forceinline__ f32x4 load_addend4(const GemmParams& p, int m, int n, bool valid) {
+__device__ __forceinline__ f32x4 load_addend4(const float* cbase, int64_t ldc, int N, int m, int n, bool valid) {
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
   if (valid) {
-    const float* c = p.Cin + (int64_t)m * p.ldc + n;
-    if (n + 4 <= p.N && (p.ldc & 3) == 0 && ((uintptr_t)p.Cin & 15) == 0) {
+    const float* c = cbase + (int64_t)m * ldc + n;
+    if (n + 4 <= N && (ldc & 3) == 0 && ((uintptr_t)cbase & 15) == 0) {
       x = *(const f32x4*)c;
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (n + r < p.N) x[r] = c[r];
+        if (n + r < N) x[r] = c[r];
     }
   }
   return x;
+}
+
+__device__ __forceinline__ f32x4 load_addend4(const GemmParams& p, int m, int n, bool valid) {
+  return load_addend4(p.Cin, p.ldc, p.N, m, n, valid);
 }
 
 __device__ __forceinline__ void add_addend4(const GemmParams& p, int m, int n, float (&v)[4]) {
@@ -494,6 +512,9 @@ struct Work {
   int half_mask;      // contiguous: 128-row halves computed in this segment
   int e_lo, e_hi;     // contiguous: expert of each half (-1 = padding only)
   int w;              // tile id (< 0: no more work)
+  int kbn;            // 128-deep K slices of the tile
+  int krows;          // K rows readable from A / B (rows past them load as zeros)
+  const float* C;     // K-grouped: the group's fp32 addend, or NULL
 };
 
 __device__ __forceinline__ int block_max_index(const int32_t* idx, int from, int count, int rows) {
@@ -509,14 +530,34 @@ __device__ __forceinline__ int block_max_index(const int32_t* idx, int from, int
 
 // Resolve tile id w into its first segment; false if the tile has no work.
 template <int L, int BM, int BN>
-__device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t) {
+__device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t, const KGroups* kg = nullptr) {
   int tm, tn;
   t.w = w;
   t.seg = 0;
   t.nseg = 1;
   t.half_mask = 3;
   t.e_lo = t.e_hi = 0;
-  if (L == kMasked) {
+  t.kbn = p.Kb;
+  t.krows = p.K;
+  t.C = nullptr;
+  if (L == kKGrouped) {
+    // group idx owns the K range [128 kb0, 128 kb1) of A and B and writes
+    // D[g] (packed [G, M, N])
+    const int per = p.tiles_m * p.tiles_n;
+    const int idx = w / per;
+    raster(w - idx * per, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int g = kg->g[idx];
+    const int kb0 = kg->kb0[idx];
+    t.kbn = kg->kb0[idx + 1] - kb0;
+    t.krows = t.kbn * 128;
+    t.A = p.A + kb0 * kg->a_step;
+    t.sa = p.sa + (int64_t)kb0 * p.ld_sa;
+    t.B = p.B + kb0 * kg->b_step;
+    t.sb = p.sb + kb0;
+    t.D = p.D + (int64_t)g * p.rows * p.N;
+    t.C = p.Cin ? p.Cin + (int64_t)g * p.rows * p.N : nullptr;
+    t.rows_valid = p.rows;
+  } else if (L == kMasked) {
     const int per_group = p.tiles_m * p.tiles_n;
     const int g = w / per_group;
     raster(w - g * per_group, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -565,7 +606,8 @@ __device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t)
 
 // Next segment of the same tile, or the next tile with work for this workgroup.
 template <int L, int BM, int BN>
-__device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& it, int local, int grid) {
+__device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& it, int local, int grid,
+                                            const KGroups* kg = nullptr) {
   if (L == kContiguous && t.seg + 1 < t.nseg) {
     t.seg += 1;
     t.half_mask = 2;
@@ -580,7 +622,7 @@ __device__ __forceinline__ void advance_big(const GemmParams& p, Work& t, int& i
       t.w = -1;
       return;
     }
-    if (resolve_big<L, BM, BN>(p, w, t)) return;
+    if (resolve_big<L, BM, BN>(p, w, t, kg)) return;
   }
 }
 
@@ -607,16 +649,53 @@ __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rs, int64_t ld
   }
 }
 
+// Operands stored MN-major ([K, M] or [K, N], the NN / TN / TT layouts and
+// the K-grouped GEMM) are staged as they are stored: the slice's 128 K rows
+// of the tile's 256 MN columns, K row r at byte 256 r of the operand's stage
+// area.  The 16-byte chunk c of row r sits at chunk c ^ kmn_swz(r): the
+// transposing fragment reads (lds_frag_mn) take 8 consecutive K rows at one
+// chunk per 16 lanes, and this puts those rows, and the rows 32 apart that
+// the neighbouring lanes take, in different banks.
+__device__ __forceinline__ int kmn_swz(int r) { return (r & 7) | (((r >> 5) & 1) << 3); }
+
+// This wave's N loads of 4 K rows (1 KiB) each into an MN-major stage area,
+// from 1 KiB load q0; chunks at or past column `cols` of the tile (a
+// multiple of 16) are not read and load as zeros.
+template <int N>
+__device__ __forceinline__ void issue_rows_mn(__amdgpu_buffer_rsrc_t rs, int64_t ld, int q0, uint8_t* area, int lane,
+                                              int cols) {
+  const int p_chunk = lane & 15;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int r = (q0 + j) * 4 + (lane >> 4);
+    const int c = p_chunk ^ kmn_swz(r);
+    const int voff = c * 16 < cols ? r * (int)ld + c * 16 : kOobOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(area + (q0 + j) * 1024), 16,
+                                             voff, 0, 0, 0);
+  }
+}
+
+// Buffer range over one slice of an MN-major operand of `ext` columns
+// (ext % 16 == 0): its K rows from slice kb on, from column mn0 to the last
+// K row's column ext.  K rows past `krows` read as zeros; columns past ext
+// are never requested (issue_rows_mn's `cols`).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mn_slice_rsrc(const uint8_t* base, int64_t ld, int kb, int krows,
+                                                                 int mn0, int ext) {
+  return make_rsrc(base + (int64_t)kb * 128 * ld + mn0, (int64_t)(krows - kb * 128 - 1) * ld + (ext - mn0));
+}
+
 // KTAIL: the kernel is built for K % 128 != 0 (launches with whole slices
 // only use the build without it, whose loads carry no clipping code at all).
-template <class C, bool KTAIL = false>
+// TA / TB: A / B stored MN-major.
+template <class C, bool KTAIL = false, bool TA = false, bool TB = false>
 __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Work& t, int kb, uint8_t* stage,
                                                   uint8_t* sa_area, int wave, int lane, int sa_k = -1) {
   constexpr int BM = C::BM;
   constexpr int HALF = C::NWAVES / 2, LA = C::LOADS_A, LB = C::LOADS_B;
+  static_assert(!(TA || TB) || (BM == 256 && C::BN == 256 && HALF == 4), "MN-major operands: 256x256 tiles");
   const bool is_a = wave < HALF;  // wave-uniform: one wave of each SIMD loads
-  const int64_t bytes_a = (int64_t)(t.rows_alloc - t.m0 - 1) * p.lda + p.K;
-  const int64_t bytes_b = (int64_t)(p.N - t.n0 - 1) * p.ldb + p.K;
+  const int64_t bytes_a = (int64_t)(t.rows_alloc - t.m0 - 1) * p.lda + t.krows;
+  const int64_t bytes_b = (int64_t)(p.N - t.n0 - 1) * p.ldb + t.krows;
   // A whole slice loads as is; only the partial last slice of a K tail
   // (wave-uniform branch) clips its chunks at column K.
   const int kleft = p.K - kb * 128;
@@ -627,15 +706,26 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
   // memory pipe (measured: 1-4 % faster than splitting A and B loads over the
   // two halves).
   if (is_a) {
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.A + (int64_t)t.m0 * p.lda, bytes_a);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.B + (int64_t)t.n0 * p.ldb, bytes_b);
     const int qa = wave * LA, qb = BM / 8 + wave * LB;  // first 8-row load of each operand
-    if (clip) {
-      issue_rows<LA, true>(ra, p.lda, qa, qa * 8, stage, lane, kb, kleft);
-      issue_rows<LB, true>(rb, p.ldb, qb, qb * 8 - BM, stage, lane, kb, kleft);
+    if (TA) {
+      issue_rows_mn<8>(mn_slice_rsrc(t.A, p.lda, kb, t.krows, t.m0, t.rows_alloc), p.lda, wave * 8, stage, lane,
+                       t.rows_alloc - t.m0);
     } else {
-      issue_rows<LA, false>(ra, p.lda, qa, qa * 8, stage, lane, kb, kleft);
-      issue_rows<LB, false>(rb, p.ldb, qb, qb * 8 - BM, stage, lane, kb, kleft);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.A + (int64_t)t.m0 * p.lda, bytes_a);
+      if (clip)
+        issue_rows<LA, true>(ra, p.lda, qa, qa * 8, stage, lane, kb, kleft);
+      else
+        issue_rows<LA, false>(ra, p.lda, qa, qa * 8, stage, lane, kb, kleft);
+    }
+    if (TB) {
+      issue_rows_mn<8>(mn_slice_rsrc(t.B, p.ldb, kb, t.krows, t.n0, p.N), p.ldb, wave * 8, stage + BM * 128, lane,
+                       p.N - t.n0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.B + (int64_t)t.n0 * p.ldb, bytes_b);
+      if (clip)
+        issue_rows<LB, true>(rb, p.ldb, qb, qb * 8 - BM, stage, lane, kb, kleft);
+      else
+        issue_rows<LB, false>(rb, p.ldb, qb, qb * 8 - BM, stage, lane, kb, kleft);
     }
     // sa[kb][m0 + 64 wave + lane] into the stage's scale area; rows past
     // rows_alloc read as 0 (their outputs are never stored)
@@ -692,6 +782,32 @@ __device__ __forceinline__ i32x8 lds_frag(const uint8_t* st, int off0, int off1)
   return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Per-lane geometry of the MN-major fragment reads: within each 16-lane group
+// q = lane / 16, lane 2j + h addresses K row 32q + j (and 8t further for read
+// t) at byte 8h of the fragment's chunk; the transposing read then hands lane
+// i of the group the 8 K bytes of MN row i.  Returns {row offset, swizzle}.
+__device__ __forceinline__ void mn_frag_geom(int lane, int area, int (&g)[2]) {
+  const int q = lane >> 4, i = lane & 15;
+  const int r = 32 * q + (i >> 1);
+  g[0] = area + r * 256 + 8 * (i & 1);
+  g[1] = kmn_swz(r) << 4;  // the same for r + 8t (t < 4)
+}
+
+// The 16 x 128 fragment of MN rows [16 s, 16 s + 16) of an MN-major stage
+// area, in MFMA operand layout (lane: row lane % 16, K bytes [32 (lane / 16),
+// +32)), by four transposing 8-byte reads of 8 K rows each.
+__device__ __forceinline__ i32x8 lds_frag_mn(const uint8_t* st, const int (&g)[2], int s) {
+  const uint8_t* a = st + g[0] + ((s << 4) ^ g[1]);
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(a));
+  const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(a + 2048));
+  const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(a + 4096));
+  const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(a + 6144));
+  return (i32x8){r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+}
+
 // One 128-deep K slice of the wave tile: SM x SN MFMAs, each a fresh partial
 // P, promoted into acc with s = sa * sb.  Software-pipelined by weight subtile:
 // step (tt, ms) issues the MFMA of (tt, ms) and the four promotion FMAs of
@@ -701,23 +817,32 @@ __device__ __forceinline__ i32x8 lds_frag(const uint8_t* st, int off0, int off1)
 // compiler from pulling each MFMA down next to its consumers.  s[ms][0]
 // applies to subtiles before `tb`, s[ms][1] from `tb` on (the wave's columns
 // may cross one 128-column weight-scale block boundary).
-template <class C>
+// TA / TB: the operand is staged MN-major; its offsets are then mn_frag_geom's
+// and a_s0 / b_s0 the chunk of the wave's first fragment row.
+template <class C, bool TA = false, bool TB = false>
 __device__ __forceinline__ void slice_mma(const uint8_t* st, const int (&a_off)[2], const int (&b_off)[2],
-                                          const float (&s)[C::SM][2], int tb, float (&acc)[C::SM][C::SN][4]) {
+                                          const float (&s)[C::SM][2], int tb, float (&acc)[C::SM][C::SN][4],
+                                          int a_s0 = 0, int b_s0 = 0) {
   constexpr int SM = C::SM, SN = C::SN;
+  auto frag_a = [&](int ms) {
+    return TA ? lds_frag_mn(st, a_off, a_s0 + ms) : lds_frag(st, a_off[0] + ms * 2048, a_off[1] + ms * 2048);
+  };
+  auto frag_b = [&](int tt) {
+    return TB ? lds_frag_mn(st, b_off, b_s0 + tt) : lds_frag(st, b_off[0] + tt * 2048, b_off[1] + tt * 2048);
+  };
   // the first weight fragment, then the activation fragments in the order
   // the first subtile's MFMAs use them: LDS reads return in order, so the
   // first MFMA waits for two fragments instead of all SM + 1
-  i32x8 bf = lds_frag(st, b_off[0], b_off[1]);
+  i32x8 bf = frag_b(0);
   i32x8 af[SM];
 #pragma unroll
-  for (int ms = 0; ms < SM; ++ms) af[ms] = lds_frag(st, a_off[0] + ms * 2048, a_off[1] + ms * 2048);
+  for (int ms = 0; ms < SM; ++ms) af[ms] = frag_a(ms);
   __builtin_amdgcn_sched_barrier(0);
   f32x4 prev[SM];
 #pragma unroll
   for (int tt = 0; tt < SN; ++tt) {
     i32x8 bn = bf;
-    if (tt + 1 < SN) bn = lds_frag(st, b_off[0] + (tt + 1) * 2048, b_off[1] + (tt + 1) * 2048);
+    if (tt + 1 < SN) bn = frag_b(tt + 1);
     f32x4 cur[SM];
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) {
@@ -783,18 +908,23 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int l16 = lane & 15, kq = lane >> 4;
   const bool vec = (p.ldd & 7) == 0 && ((uintptr_t)p.D & 15) == 0;
+  // fp32 addend: C of the dense call, or the K-grouped tile's group slice
+  constexpr bool ADDEND = L == kDenseC || L == kKGrouped;
+  const float* cbase = L == kDenseC ? p.Cin : t.C;
+  const int64_t ldc = L == kDenseC ? p.ldc : (int64_t)p.N;
+  const bool add_c = ADDEND && cbase != nullptr;
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     // the addend of this pass's fragments, all loads in flight together
-    f32x4 cv[L == kDenseC ? G::MS_PER_PASS : 1][SN];
-    if (L == kDenseC) {
+    f32x4 cv[ADDEND ? G::MS_PER_PASS : 1][SN];
+    if (add_c) {
 #pragma unroll
       for (int j = 0; j < G::MS_PER_PASS; ++j) {
         const int m = t.m0 + wm * WM + (pass * G::MS_PER_PASS + j) * 16 + l16;
 #pragma unroll
         for (int tt = 0; tt < SN; ++tt) {
           const int n = t.n0 + wn * WN + tt * 16 + 4 * kq;
-          cv[j][tt] = load_addend4(p, m, n, m < t.rows_valid && n < p.N);
+          cv[j][tt] = load_addend4(cbase, ldc, p.N, m, n, m < t.rows_valid && n < p.N);
         }
       }
     }
@@ -809,7 +939,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
         const int c = byte >> 4;
         const int off = srow * ROWB + ((c ^ (srow & 15)) << 4) + (byte & 15);
         float v[4] = {acc[ms][tt][0], acc[ms][tt][1], acc[ms][tt][2], acc[ms][tt][3]};
-        if (L == kDenseC)
+        if (ADDEND && add_c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] += cv[j][tt][r];
         *(uint2*)(stg + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -850,8 +980,10 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Work& t, c
   }
 }
 
-template <class C, int L, bool KTAIL>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
+// The large-tile kernel's body.  TA / TB: A / B stored MN-major (K rows of
+// M / N bytes); kg: the K-grouped GEMM's groups (kKGrouped only).
+template <class C, int L, bool KTAIL, bool TA, bool TB>
+__device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGroups* kg) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
 
@@ -869,7 +1001,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   const int kq = lane >> 4;
   const int half = (wm * WM) / 128;  // 128-row half of the tile this wave's rows lie in
 
-  // fragment read offsets (the swizzle depends only on the row's low 4 bits)
+  // fragment read offsets (the swizzle depends only on the row's low 4 bits);
+  // MN-major operands: the transposing reads' geometry and the chunk of the
+  // wave's first fragment row
   int a_off[2], b_off[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -878,20 +1012,23 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
     a_off[h] = ra * 128 + (((2 * kq + h) ^ swz16(ra)) << 4);
     b_off[h] = rb * 128 + (((2 * kq + h) ^ swz16(rb)) << 4);
   }
+  if (TA) mn_frag_geom(lane, 0, a_off);
+  if (TB) mn_frag_geom(lane, BM * 128, b_off);
+  const int a_s0 = (wm * WM) >> 4, b_s0 = (wn * WN) >> 4;
 
   const int grid = gridDim.x;
   const int local = xcd_local_id(blockIdx.x, grid);
-  const int Kb = p.Kb;
 
   Work cur;
   int it = 0;
   cur.w = -1;
-  if (!(local < p.num_tiles && resolve_big<L, BM, BN>(p, local, cur))) advance_big<L, BM, BN>(p, cur, it, local, grid);
+  if (!(local < p.num_tiles && resolve_big<L, BM, BN>(p, local, cur, kg)))
+    advance_big<L, BM, BN>(p, cur, it, local, grid, kg);
   if (cur.w < 0) return;
 
   float sb_c[2];
   load_sb<C>(p, cur, 0, wn, sb_c);
-  issue_slice_loads<C, KTAIL>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane);
+  issue_slice_loads<C, KTAIL, TA, TB>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -908,23 +1045,24 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   while (cur.w >= 0) {
     Work nxt = cur;
     int it_n = it;
-    advance_big<L, BM, BN>(p, nxt, it_n, local, grid);
+    advance_big<L, BM, BN>(p, nxt, it_n, local, grid, kg);
     const bool active = (L == kContiguous) ? (((cur.half_mask >> half) & 1) != 0)
                                            : (cur.m0 + wm * WM < cur.rows_valid);
     const int tb = second_block_subtile<C>(cur, wn);
+    const int Kb = cur.kbn;
 
     for (int kb = 0; kb < Kb; ++kb) {
       // prefetch the following slice: this tile's next one, or the first of the next work item
       const bool last = kb + 1 == Kb;
       if (!last)
-        issue_slice_loads<C, KTAIL>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
+        issue_slice_loads<C, KTAIL, TA, TB>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
       else if (nxt.w >= 0)
-        issue_slice_loads<C, KTAIL>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
+        issue_slice_loads<C, KTAIL, TA, TB>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
 
       if (active) {
         float s[SM][2];
         slice_scales<C>(FG_SA(stage), wm, l16, sb_c, s);
-        slice_mma<C>(FG_STAGE(stage), a_off, b_off, s, tb, acc);
+        slice_mma<C, TA, TB>(FG_STAGE(stage), a_off, b_off, s, tb, acc, a_s0, b_s0);
       }
 
       // The next slice's weight scales are scalar loads, issued only now:
@@ -965,6 +1103,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams 
   __builtin_amdgcn_s_waitcnt(0);
 #undef FG_STAGE
 #undef FG_SA
+}
+
+template <class C, int L, bool KTAIL, bool TA = false, bool TB = false>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
+  big_kernel_body<C, L, KTAIL, TA, TB>(p, nullptr);
+}
+
+// K-grouped GEMM, D[g] = C[g] + A_g^T B_g: one persistent launch over the
+// tiles of every group with work.  MN: A [K, M] and B [K, N] as stored;
+// otherwise K-major copies A^T [M, K] and B^T [N, K].
+template <class C, bool MN>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_k_grouped_kernel(GemmParams p, KGroups kg) {
+  big_kernel_body<C, kKGrouped, false, MN, MN>(p, &kg);
+}
+
+// D[g] = bf16(C[g]) or 0 for the K-grouped GEMM's groups without K rows:
+// n elements from c (NULL: zeros) into d.
+static __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* d, const float* c, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    d[i] = (uint16_t)(pack_bf16x2(c ? c[i] : 0.f, 0.f) & 0xffff);
 }
 
 

@@ -81,6 +81,9 @@ int main() {
   EXPECT(gemm_fp8_tt(A, 64, S, 64, A, 512, S, nullptr, 0, D, 256, 64, 256, 100, WS, big, nullptr), FG_EALIGN);
   EXPECT(gemm_fp8_tn(A, 64, S, 64, A, 256, S, nullptr, 0, D, 256, 64, 256, (1 << 22) + 16, WS, big, nullptr),
          FG_EUNSUPPORTED);
+  // no workspace: MN-major operands need 16-byte rows and M, N multiples of 16
+  EXPECT(gemm_fp8_tn(A, 72, S, 64, A, 256, S, nullptr, 0, D, 256, 64, 256, 512, nullptr, 0, nullptr), FG_EALIGN);
+  EXPECT(gemm_fp8_nn(A, 512, S, 64, A, 250, S, nullptr, 0, D, 250, 64, 250, 512, nullptr, 0, nullptr), FG_EALIGN);
 
   // K-grouped TN
   int ks[3] = {128, 0, 256};
@@ -95,8 +98,10 @@ int main() {
          FG_EALIGN);
   EXPECT(gemm_fp8_k_grouped_tn_contiguous(A, 64, S, 64, A, 256, S, ks_neg, 2, nullptr, D, 64, 256, WS, big, nullptr),
          FG_EINVAL);
-  EXPECT(gemm_fp8_k_grouped_tn_contiguous(A, 64, S, 64, A, 256, S, ks, 3, nullptr, D, 64, 256, WS, 16, nullptr),
+  EXPECT(gemm_fp8_k_grouped_tn_contiguous(A, 72, S, 64, A, 256, S, ks, 3, nullptr, D, 64, 256, WS, 16, nullptr),
          FG_EINVAL);
+  EXPECT(gemm_fp8_k_grouped_tn_contiguous(A, 64, S, 64, A, 256, S, ks, 3, nullptr, D, 60, 256, nullptr, 0, nullptr),
+         FG_EALIGN);
   if (fg_k_grouped_workspace_bytes(-1, 1, 1) != -1) ++g_fail;
   (void)fg_k_grouped_workspace_bytes(0x7fffffff, 0x7fffffff, big);
 

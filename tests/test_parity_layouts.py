@@ -1,12 +1,15 @@
 """The NN, TN and TT storage layouts on the GPU against the CPU oracle.
 
-An operand stored MN-major is transposed into the workspace by a byte
-transpose and the NT kernels run on the copy, so a wrong byte anywhere in
-the transpose changes the GEMM result: in the exact regime (integer codes,
-power-of-two scales, an addend on a 1/4 grid) every layout is compared bit
-for bit, for the few-row, 128x128 and large-tile kernels, with ragged shapes
-that leave partial transpose tiles and with row strides that force the
-transpose's byte-wise paths."""
+Two paths serve an operand stored MN-major: with a workspace, a byte
+transpose into it followed by the NT kernels on the copy; without one, the
+large-tile kernel staging it as stored (the transposing LDS reads build the
+MFMA fragments).  A wrong
+byte anywhere in either changes the GEMM result: in the exact regime (integer
+codes, power-of-two scales, an addend on a 1/4 grid) every layout is compared
+bit for bit on both paths, for the few-row, 128x128 and large-tile kernels,
+with ragged shapes that leave partial tiles and K tails, and with row strides
+that force the transpose's byte-wise paths or pad the direct path's rows with
+NaN bytes it must never read."""
 
 from __future__ import annotations
 
@@ -25,12 +28,31 @@ pytestmark = pytest.mark.gpu
 
 LAYOUTS = ["nn", "tn", "tt"]
 ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN")
+# "copy": a workspace from torch's allocator (transposed copies);
+# "direct": an empty workspace (operands staged as stored)
+PATHS = ["copy", "direct"]
 
 
 @pytest.fixture(autouse=True)
 def default_plan(monkeypatch):
     for k in ENV_KEYS:
         monkeypatch.delenv(k, raising=False)
+
+
+@pytest.fixture(params=PATHS)
+def path(request):
+    return request.param
+
+
+def direct_ok(layout, M, N, lda=None, ldb=None):
+    """The direct path's rule: each MN-major operand has a row stride and a
+    column count that are multiples of 16."""
+    ok = True
+    if layout[0] == "t":
+        ok &= M % 16 == 0 and (lda or M) % 16 == 0
+    if layout[1] == "n":
+        ok &= N % 16 == 0 and (ldb or N) % 16 == 0
+    return ok
 
 
 def stored(layout, A, B):
@@ -48,39 +70,59 @@ def dev_padded(a: np.ndarray, pad: int) -> torch.Tensor:
     return buf[:, : a.shape[1]]
 
 
-def call(fg, layout, As, sa, Bs, sb, C=None, out=None, pad=(0, 0)):
+def call(fg, layout, As, sa, Bs, sb, C=None, out=None, pad=(0, 0), path="copy"):
     M = sa.shape[1]
     N = Bs.shape[1] if layout[1] == "n" else Bs.shape[0]
     D = out if out is not None else sentinel_like((M, N))
     Ad = dev_padded(As, pad[0]) if pad[0] else dev_u8(As)
     Bd = dev_padded(Bs, pad[1]) if pad[1] else dev_u8(Bs)
-    getattr(fg, "gemm_fp8_" + layout)(Ad, dev_sa(sa), Bd, dev_f32(sb), D, C=None if C is None else dev_f32(C))
+    ws = torch.empty(0, dtype=torch.uint8, device="cuda") if path == "direct" else None
+    getattr(fg, "gemm_fp8_" + layout)(Ad, dev_sa(sa), Bd, dev_f32(sb), D, C=None if C is None else dev_f32(C),
+                                      workspace=ws)
     torch.cuda.synchronize()
     return D
 
 
+def call_or_reject(fg, layout, As, sa, Bs, sb, path, ok, **kw):
+    """call(); on the direct path with operands it does not take, check the
+    FG_EALIGN error and that D is untouched, and return None."""
+    if path == "direct" and not ok:
+        M = sa.shape[1]
+        N = Bs.shape[1] if layout[1] == "n" else Bs.shape[0]
+        D = kw.pop("out", None)
+        D = D if D is not None else sentinel_like((M, N))
+        with pytest.raises(fg.FP8GemmError, match="without a workspace"):
+            call(fg, layout, As, sa, Bs, sb, out=D, path=path, **kw)
+        assert (bf16_bits(D) == SENTINEL_BF16).all()
+        return None
+    return call(fg, layout, As, sa, Bs, sb, path=path, **kw)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (37, 200, 512), (128, 130, 256), (300, 1000, 640),
-                                   (513, 2112, 256), (1100, 1300, 384)])
+                                   (513, 2112, 256), (1100, 1300, 384), (144, 272, 384), (528, 1040, 640),
+                                   (400, 2064, 272), (784, 16, 128)])
 @pytest.mark.parametrize("with_c", [False, True], ids=["no-C", "C"])
-def test_exact_regime_bitwise(gpu_lib, layout, M, N, K, with_c):
-    announce(f"layout {layout} exact regime {M}x{N}x{K} C={with_c}")
+def test_exact_regime_bitwise(gpu_lib, path, layout, M, N, K, with_c):
+    announce(f"layout {layout} {path} exact regime {M}x{N}x{K} C={with_c}")
     rng = np.random.default_rng(M + 7 * N + K + len(layout))
     A, sa, B, sb = exact_regime(rng, M, N, K)
     As, Bs = stored(layout, A, B)
     C = (rng.integers(-1024, 1025, (M, N)) / 4.0).astype(np.float32) if with_c else None
-    D = call(gpu_lib, layout, As, sa, Bs, sb, C)
-    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C)))
+    D = call_or_reject(gpu_lib, layout, As, sa, Bs, sb, path, direct_ok(layout, M, N), C=C)
+    if D is not None:
+        assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C)))
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("pad", [(1, 3), (5, 16), (16, 7)])
-def test_strided_operands(gpu_lib, layout, pad):
+@pytest.mark.parametrize("M,N,pad", [(150, 290, (1, 3)), (150, 290, (5, 16)), (150, 290, (16, 7)),
+                                     (160, 288, (16, 32)), (160, 288, (48, 16))])
+def test_strided_operands(gpu_lib, path, layout, M, N, pad):
     """Row strides that are not multiples of 16 on the stored operands (byte-wise
-    transpose loads), NaN bytes in the padding, and an output view with a
-    sentinel border."""
-    M, N, K = 150, 290, 384
-    announce(f"layout {layout} strided pad={pad}")
+    transpose loads), padded 16-byte rows on the direct path, NaN bytes in the
+    padding, and an output view with a sentinel border."""
+    K = 384
+    announce(f"layout {layout} {path} strided {M}x{N} pad={pad}")
     rng = np.random.default_rng(sum(pad))
     A, sa, B, sb = exact_regime(rng, M, N, K)
     As, Bs = stored(layout, A, B)
@@ -88,21 +130,26 @@ def test_strided_operands(gpu_lib, layout, pad):
     pa = pad[0] if layout[0] == "t" else 16
     pb = pad[1] if layout[1] == "n" else 16
     Dbuf = sentinel_like((M + 2, N + 5))
-    call(gpu_lib, layout, As, sa, Bs, sb, out=Dbuf[:M, :N], pad=(pa, pb))
+    ok = direct_ok(layout, M, N, M + pa, N + pb)
+    if call_or_reject(gpu_lib, layout, As, sa, Bs, sb, path, ok, out=Dbuf[:M, :N], pad=(pa, pb)) is None:
+        return
     assert np.array_equal(bf16_bits(Dbuf[:M, :N]), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb)))
     bits = bf16_bits(Dbuf)
     assert (bits[M:, :] == SENTINEL_BF16).all() and (bits[:, N:] == SENTINEL_BF16).all()
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_random_inputs(gpu_lib, layout):
-    M, N, K = 257, 1030, 1024
-    announce(f"layout {layout} random {M}x{N}x{K}")
+@pytest.mark.parametrize("M,N", [(257, 1030), (272, 1040)])
+def test_random_inputs(gpu_lib, path, layout, M, N):
+    K = 1024
+    announce(f"layout {layout} {path} random {M}x{N}x{K}")
     A32, B32 = synth.dense_problem(M, N, K, seed=23)
     qa, sa, qb, sb = quantize_dense(A32, B32)
     As, Bs = stored(layout, qa, qb)
     C = np.random.default_rng(2).standard_normal((M, N)).astype(np.float32)
-    D = call(gpu_lib, layout, As, sa, Bs, sb, C)
+    D = call_or_reject(gpu_lib, layout, As, sa, Bs, sb, path, direct_ok(layout, M, N), C=C)
+    if D is None:
+        return
     X, S = ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C, with_magnitude=True)
     assert_close(bf16_to_f64(D), X, S, K // 128 + 1, f"layout {layout} random")
 
@@ -122,6 +169,42 @@ def test_same_bits_as_nt(gpu_lib, layout):
     assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_direct_same_bits_as_transposed(gpu_lib, monkeypatch, layout):
+    """Staging an MN-major operand as stored and transposing it first feed the
+    same bytes to the same MFMAs in the same order: identical bits."""
+    M, N, K = 1040, 2064, 1280
+    announce(f"layout {layout} direct equals transposed")
+    A32, B32 = synth.dense_problem(M, N, K, seed=31)
+    qa, sa, qb, sb = quantize_dense(A32, B32)
+    As, Bs = stored(layout, qa, qb)
+    C = np.random.default_rng(3).standard_normal((M, N)).astype(np.float32)
+    monkeypatch.setenv("FG_FORCE_CONFIG", "big")
+    D1 = call(gpu_lib, layout, As, sa, Bs, sb, C, path="direct")
+    D0 = call(gpu_lib, layout, As, sa, Bs, sb, C, path="copy")
+    assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
+    X, S = ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C, with_magnitude=True)
+    assert_close(bf16_to_f64(D1), X, S, K // 128 + 1, f"layout {layout} direct")
+
+
+def test_direct_path_needs_no_workspace(gpu_lib):
+    """Through the C ABI: a NULL workspace of 0 bytes runs the direct path."""
+    import ctypes
+
+    M, N, K = 2048, 4096, 256
+    rng = np.random.default_rng(12)
+    A, sa, B, sb = exact_regime(rng, M, N, K)
+    As, Bs = stored("tn", A, B)
+    Ad, Bd, sad, sbd = dev_u8(As), dev_u8(Bs), dev_sa(sa), dev_f32(sb)
+    D = sentinel_like((M, N))
+    lib = gpu_lib.load_library()
+    st = lib.gemm_fp8_tn(Ad.data_ptr(), M, sad.data_ptr(), sad.stride(0), Bd.data_ptr(), N, sbd.data_ptr(), None, 0,
+                         D.data_ptr(), N, M, N, K, None, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(ogemm.gemm_layout("tn", As, sa, Bs, sb)))
+
+
 def test_workspace_too_small_is_rejected(gpu_lib):
     M, N, K = 64, 256, 256
     rng = np.random.default_rng(3)
@@ -137,15 +220,15 @@ def test_workspace_too_small_is_rejected(gpu_lib):
     assert (bf16_bits(D) == SENTINEL_BF16).all()
 
 
-def test_full_size_tn_sampled(gpu_lib):
+def test_full_size_tn_sampled(gpu_lib, path):
     """TN (both operands stored [K, .], the weight-gradient form) at the dense
-    4096 x 7168 x 2048 size; sampled rows x column blocks."""
+    4096 x 7168 x 2048 size, on both paths; sampled rows x column blocks."""
     M, N, K = synth.DENSE_M4096.shapes[4]
-    announce(f"layout tn full size {M}x{N}x{K}")
+    announce(f"layout tn {path} full size {M}x{N}x{K}")
     A32, B32 = synth.dense_problem(M, N, K, seed=0)
     qa, sa, qb, sb = quantize_dense(A32, B32)
     As, Bs = stored("tn", qa, qb)
-    D = call(gpu_lib, "tn", As, sa, Bs, sb)
+    D = call(gpu_lib, "tn", As, sa, Bs, sb, path=path)
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False)]))
     for nb in np.unique(np.concatenate([[0, N // 128 - 1], rng.choice(N // 128, 2, replace=False)])):
