@@ -251,8 +251,10 @@ int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total);
  * M_total % 128 == 0, K % 16 == 0, G >= 1.
  * Device-side precondition (not checked): within each aligned 128-row block
  * every non-negative index is the same value e < G.  The block is computed
- * against B[e], where e is the largest index in the block; rows whose index
- * is not e (padding) are left untouched; a block of padding only is skipped.
+ * against B[e], where e is the largest index in the block below G; rows whose
+ * index is not e (padding) are left untouched; a block of padding only is
+ * skipped.  An index >= G counts as padding, so no weight outside B is ever
+ * addressed.
  * Debug mode: with the environment variable FG_CHECK_DEVICE=1 a check kernel
  * validates m_indices first and the host reads its result back (this
  * synchronises the stream, and the call returns FG_EINVAL while the stream

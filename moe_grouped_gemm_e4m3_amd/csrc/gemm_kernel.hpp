@@ -219,7 +219,8 @@ __device__ __forceinline__ bool resolve_tile(const GemmParams& p, int w, int BM,
       int e = -1;
       for (int r = lane; r < BM; r += 64) {
         const int m = min(tm * BM + r, p.rows - 1);
-        e = max(e, p.m_indices[m]);
+        const int v = p.m_indices[m];
+        if (v < p.G) e = max(e, v);  // an index past the experts is padding
       }
       e = wave_max(e);
       e = __builtin_amdgcn_readfirstlane(e);
@@ -517,12 +518,15 @@ struct Work {
   const float* C;     // K-grouped: the group's fp32 addend, or NULL
 };
 
-__device__ __forceinline__ int block_max_index(const int32_t* idx, int from, int count, int rows) {
+__device__ __forceinline__ int block_max_index(const int32_t* idx, int from, int count, int rows, int G) {
   const int lane = threadIdx.x & 63;
   int e = -1;
   for (int r = lane; r < count; r += 64) {
     const int m = from + r;
-    if (m < rows) e = max(e, idx[m]);
+    if (m < rows) {
+      const int v = idx[m];
+      if (v < G) e = max(e, v);  // an index past the experts is padding: no weight is addressed with it
+    }
   }
   e = wave_max(e);
   return __builtin_amdgcn_readfirstlane(e);
@@ -581,8 +585,8 @@ __device__ __forceinline__ bool resolve_big(const GemmParams& p, int w, Work& t,
     if (L == kContiguous) {
       const int m0 = tm * BM;
       const int half = BM >= 256 ? BM / 2 : BM;
-      const int lo = block_max_index(p.m_indices, m0, half, p.rows);
-      const int hi = BM >= 256 ? block_max_index(p.m_indices, m0 + half, half, p.rows) : -1;
+      const int lo = block_max_index(p.m_indices, m0, half, p.rows, p.G);
+      const int hi = BM >= 256 ? block_max_index(p.m_indices, m0 + half, half, p.rows, p.G) : -1;
       if (lo < 0 && hi < 0) return false;
       t.e_lo = lo;
       t.e_hi = hi;

@@ -73,6 +73,38 @@ def test_contiguous_exact_regime_bitwise(gpu_lib):
     assert (bits[~valid] == SENTINEL_BF16).all()
 
 
+@pytest.mark.parametrize("K", [512, 0])
+def test_contiguous_index_past_experts_is_padding(gpu_lib, K):
+    """Blocks whose index is G or larger are padding: their rows stay
+    untouched and no weight past B is addressed; the other rows are exact.
+    Block layout (128 rows each): G, 0, 1000, 1, (two blocks in one 256-row
+    tile), then a tile of two blocks past the experts."""
+    announce(f"contiguous indices past the experts K={K}")
+    rng = np.random.default_rng(17)
+    G, N = 2, 264
+    blocks = [G, 0, 1000, 1, G + 1, 1 << 30]
+    idx = np.repeat(np.asarray(blocks, np.int32), 128)
+    idx[130:140] = -1  # padding rows inside a valid block
+    M = idx.shape[0]
+    qa, sa, _, _ = exact_regime(rng, M, N, max(K, 128))
+    _, _, qb, sb = exact_regime(rng, 1, N, max(K, 128), groups=(1, G))
+    qa, sa, qb, sb = qa[:, :K], sa[:K // 128], qb[:, :, :K], sb[:, :, :K // 128]
+    if K:
+        D = run_contig(gpu_lib, qa, sa, qb, sb, idx)
+    else:  # empty operands as plain device tensors
+        D = sentinel_like((M, N))
+        gpu_lib.gemm_fp8_grouped_contiguous(
+            torch.zeros(M, 0, dtype=torch.uint8, device="cuda"), torch.zeros(0, M, device="cuda"),
+            torch.zeros(G, N, 0, dtype=torch.uint8, device="cuda"), torch.zeros(G, -(-N // 128), 0, device="cuda"),
+            torch.from_numpy(idx).cuda(), D)
+        torch.cuda.synchronize()
+    ref_idx = np.where(idx >= G, -1, idx)
+    X, valid = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, ref_idx)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
 def test_contiguous_equals_dense_per_group(gpu_lib, monkeypatch):
     """Bit for bit against the large-tile dense kernel, which adds the slices
     in the same order (the few-row dense kernel adds per-wave K partials)."""

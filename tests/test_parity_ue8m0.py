@@ -326,6 +326,22 @@ def quantize_experts_ue8m0(B32):
     return np.stack([q for q, _ in ws]), np.stack([e for _, e in ws])
 
 
+def test_contig_index_past_experts_is_padding(gpu_lib):
+    """As for the fp32-factor kernel: blocks indexed G or above are padding."""
+    announce("ue8m0 contiguous indices past the experts")
+    rng = np.random.default_rng(19)
+    G, N, K = 2, 264, 640
+    idx = np.repeat(np.asarray([G, 0, 1000, 1, G + 1, 1 << 30], np.int32), 128)
+    M = idx.shape[0]
+    qa, sa, _, _ = exact_regime(rng, M, N, K)
+    _, _, qb, sb = exact_regime(rng, 1, N, K, groups=(1, G))
+    D = run_contig(gpu_lib, qa, to_bytes(sa), qb, to_bytes(sb), idx)
+    X, valid = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, np.where(idx >= G, -1, idx))
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
 def test_contig_exact_regime_bitwise(gpu_lib, width):
     """Expert blocks of 256, 128, 0, 128 and 128 rows (the 256-row tile over
     rows 256..511 holds two experts and runs as two segments; the last tile is
