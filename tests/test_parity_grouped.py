@@ -180,6 +180,33 @@ def test_masked_edges(gpu_lib, mask, Mc, N, K):
         assert_close(y[valid], X[valid], S[valid], K // 128, "masked")
 
 
+@pytest.mark.parametrize("G,Mc,N", [(16, 256, 1040), (12, 512, 520), (70, 256, 264)],
+                         ids=["16x256", "12x512", "70x256"])
+def test_masked_order_over_rounds(gpu_lib, G, Mc, N):
+    """Launches with more (group, tile) units than workgroups: under CU caps
+    that leave partial last rounds, every valid row is exact and every other
+    row untouched, with the same bits under every cap."""
+    K = 256
+    announce(f"masked order over rounds G={G} Mc={Mc} N={N}")
+    rng = np.random.default_rng(G + Mc)
+    mask = rng.integers(0, Mc + 1, G)
+    mask[:3] = [0, Mc, 1]
+    qa, sa, qb, sb = exact_regime(rng, Mc, N, K, groups=(G, G))
+    X, valid = ogemm.gemm_grouped_masked(qa, sa, qb, sb, mask)
+    ref = None
+    try:
+        for cus in (0, 1, 3, 7, 40):
+            gpu_lib.set_num_cus(cus)
+            bits = bf16_bits(run_masked(gpu_lib, qa, sa, qb, sb, mask))
+            assert (bits[~valid] == SENTINEL_BF16).all(), cus
+            assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid])), cus
+            if ref is None:
+                ref = bits
+            assert np.array_equal(bits, ref), cus
+    finally:
+        gpu_lib.set_num_cus(0)
+
+
 def test_masked_exact_regime_bitwise(gpu_lib):
     announce("masked exact regime")
     rng = np.random.default_rng(4)
