@@ -198,8 +198,10 @@ fg_status gemm_fp8_tt(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
                       uint16_t* D, int64_t ldd, int M, int N, int K,
                       void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes that gemm_fp8_<layout> needs for (M, N, K); layout is one
- * of "nt" (0), "nn", "tn", "tt".  -1 for an unknown layout or a negative size. */
+/* Workspace bytes the copying path of gemm_fp8_<layout> needs for (M, N, K)
+ * (a workspace of 0 bytes selects the copy-free path instead); layout is one
+ * of "nt" (0), "nn", "tn", "tt".  -1 for an unknown layout, a negative size
+ * or sizes the call rejects. */
 int64_t fg_layout_workspace_bytes(const char* layout, int M, int N, int K);
 
 /*
@@ -235,7 +237,9 @@ fg_status gemm_fp8_k_grouped_tn_contiguous(const uint8_t* A, int64_t lda, const 
                                            const int* ks, int G, const float* C, uint16_t* D, int M, int N,
                                            void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes of gemm_fp8_k_grouped_tn_contiguous; -1 for a negative size. */
+/* Workspace bytes the copying path of gemm_fp8_k_grouped_tn_contiguous needs
+ * (0 bytes selects the copy-free path); -1 for a negative size or sizes the
+ * call rejects. */
 int64_t fg_k_grouped_workspace_bytes(int M, int N, int64_t K_total);
 
 /*
