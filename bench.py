@@ -626,6 +626,9 @@ def _calibration(d):
     return out
 
 
+MAX_CLOCK_GHZ = 2.4  # MI355X peak shader clock
+
+
 def summarize(d: str, workload: str, steps: int):
     """Write profiles/<workload>_summary.md (and _traffic.json) from the
     rocprofv3 runs under d (PROFILE_COMMANDS, with -d d/<key>)."""
@@ -698,7 +701,11 @@ def summarize(d: str, workload: str, steps: int):
             busy = float(np.mean([r["SQ_VALU_MFMA_BUSY_CYCLES"] for r in ms_]))
             mops = float(np.mean([r["SQ_INSTS_VALU_MFMA_MOPS_F8"] for r in ms_]))
             clk = gui / 8 / (us * 1e-6) / 1e9
-            row += f" {clk:.2f} | {busy / (gui / 8 * 1024) * 100:.1f} % | {mops * 512 / fl:.3f} |"
+            # the counter run's busy window per dispatch includes its launch
+            # overhead: on launches of a few microseconds the ratio to the
+            # traced duration overstates the clock, shown then as n/a
+            clk_s = f"{clk:.2f}" if clk <= MAX_CLOCK_GHZ else "n/a"
+            row += f" {clk_s} | {busy / (gui / 8 * 1024) * 100:.1f} % | {mops * 512 / fl:.3f} |"
         lines.append(row)
         per_shape.append(entry)
         tot["us"] += us
@@ -713,7 +720,9 @@ def summarize(d: str, workload: str, steps: int):
     if "mfma" in ctr:
         lines += ["MFMA counters: `SQ_INSTS_VALU_MFMA_MOPS_F8` x 512 = FP8 flops executed; `GRBM_GUI_ACTIVE` / 8 "
                   "(XCDs) / duration = shader clock; `SQ_VALU_MFMA_BUSY_CYCLES` / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs) = "
-                  "the fraction of SIMD cycles the matrix core was busy, at the clock the chip ran.", ""]
+                  "the fraction of SIMD cycles the matrix core was busy, at the clock the chip ran.  The clock is "
+                  f"n/a where that ratio exceeds the chip's {MAX_CLOCK_GHZ} GHz: on short launches the counter run's "
+                  "busy window includes the dispatch overhead.", ""]
     stats = _csv(os.path.join(d, "trace", "**", "*kernel_stats.csv"))
     if stats:
         lines += ["All kernels of the traced run (rocprofv3 --stats):", "",
