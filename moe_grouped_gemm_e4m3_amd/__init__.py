@@ -171,6 +171,13 @@ def _unit_inner(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 
+def _ld(t: torch.Tensor) -> int:
+    """Row stride of a 2-D tensor in elements.  A single row's stride is
+    arbitrary in torch (a broadcast or sliced view can report 0), so one row
+    reports its own length."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def aligned_scale_ld(rows: int) -> int:
     """Leading dimension for activation scales: rows rounded up to 4 floats."""
     return max(4, (rows + 3) // 4 * 4)
@@ -238,8 +245,8 @@ def gemm_fp8_nt(A, sa, B, sb, D, stream=None, workspace=None):
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     _call(
         "gemm_fp8_nt_ws",
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
-        _ptr(D), D.stride(0), M, N, K, ws_ptr, ws_bytes, _stream(stream),
+        _ptr(A), _ld(A), _ptr(sa), _ld(sa), _ptr(B), _ld(B), _ptr(sb),
+        _ptr(D), _ld(D), M, N, K, ws_ptr, ws_bytes, _stream(stream),
     )
     return D
 
@@ -260,8 +267,8 @@ def gemm_fp8_nt_unsplit(A, sa, B, sb, D, stream=None):
         raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} D{tuple(D.shape)}")
     _call(
         "gemm_fp8_nt",
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
-        _ptr(D), D.stride(0), M, N, K, _stream(stream),
+        _ptr(A), _ld(A), _ptr(sa), _ld(sa), _ptr(B), _ld(B), _ptr(sb),
+        _ptr(D), _ld(D), M, N, K, _stream(stream),
     )
     return D
 
@@ -282,8 +289,8 @@ def gemm_fp8_nt_c(A, sa, B, sb, C, D, stream=None):
         raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)} D{tuple(D.shape)}")
     _call(
         "gemm_fp8_nt_c",
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
-        _ptr(C), C.stride(0), _ptr(D), D.stride(0), M, N, K, _stream(stream),
+        _ptr(A), _ld(A), _ptr(sa), _ld(sa), _ptr(B), _ld(B), _ptr(sb),
+        _ptr(C), _ld(C), _ptr(D), _ld(D), M, N, K, _stream(stream),
     )
     return D
 
@@ -320,8 +327,8 @@ def _gemm_layout(layout, A, sa, B, sb, D, C, stream, workspace):
         raise TypeError("workspace must be a contiguous uint8 CUDA tensor")
     _call(
         "gemm_fp8_" + layout,
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
-        _ptr(C), C.stride(0) if C is not None else 0, _ptr(D), D.stride(0), M, N, K,
+        _ptr(A), _ld(A), _ptr(sa), _ld(sa), _ptr(B), _ld(B), _ptr(sb),
+        _ptr(C), _ld(C) if C is not None else 0, _ptr(D), _ld(D), M, N, K,
         _ptr(workspace), workspace.numel(), _stream(stream),
     )
     return D
@@ -390,7 +397,7 @@ def gemm_fp8_k_grouped_tn_contiguous(A, sa, B, sb, ks, D, C=None, stream=None, w
     ks_host = (ctypes.c_int * G)(*ks)
     _call(
         "gemm_fp8_k_grouped_tn_contiguous",
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
+        _ptr(A), _ld(A), _ptr(sa), _ld(sa), _ptr(B), _ld(B), _ptr(sb),
         ctypes.cast(ks_host, ctypes.c_void_p), G, _ptr(C), _ptr(D), M, N,
         _ptr(workspace), workspace.numel(), _stream(stream),
     )
@@ -414,7 +421,7 @@ def gemm_fp8_grouped_contiguous(A, sa, B, sb, m_indices, D, stream=None):
         raise ValueError("shape mismatch")
     _call(
         "gemm_fp8_grouped_contiguous",
-        _ptr(A), _ptr(sa), sa.stride(0), _ptr(B), _ptr(sb), _ptr(m_indices), _ptr(D),
+        _ptr(A), _ptr(sa), _ld(sa), _ptr(B), _ptr(sb), _ptr(m_indices), _ptr(D),
         M, N, K, G, _stream(stream),
     )
     return D
@@ -464,7 +471,7 @@ def fp8_cast_per_token(x, q=None, sa=None, stream=None):
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     _unit_inner(sa, "sa")
-    _call("fp8_cast_per_token" + sfx, _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
+    _call("fp8_cast_per_token" + sfx, _ptr(x), _ld(x), _ptr(q), _ptr(sa), _ld(sa), M, K, _stream(stream))
     return q, sa
 
 
@@ -480,7 +487,7 @@ def fp8_cast_per_block(w, q=None, sb=None, stream=None):
     q = _fp8(q, "q")
     if not (q.is_contiguous() and sb.is_contiguous()):
         raise ValueError("q and sb must be contiguous")
-    _call("fp8_cast_per_block" + sfx, _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
+    _call("fp8_cast_per_block" + sfx, _ptr(w), _ld(w), _ptr(q), _ptr(sb), N, K, _stream(stream))
     return q, sb
 
 
@@ -516,8 +523,8 @@ def gemm_fp8_nt_ue8m0(A, sa, B, sb, D, stream=None):
         raise ValueError("factor shapes must be sa [ceil(Kb/4), M] and sb [Nb, ceil(Kb/4)]")
     _call(
         "gemm_fp8_nt_ue8m0",
-        _ptr(A), A.stride(0), _ptr(sa), sa.stride(0), _ptr(B), B.stride(0), _ptr(sb),
-        _ptr(D), D.stride(0), M, N, K, _stream(stream),
+        _ptr(A), _ld(A), _ptr(sa), _ld(sa), _ptr(B), _ld(B), _ptr(sb),
+        _ptr(D), _ld(D), M, N, K, _stream(stream),
     )
     return D
 
@@ -544,7 +551,7 @@ def gemm_fp8_grouped_contiguous_ue8m0(A, sa, B, sb, m_indices, D, stream=None):
         raise ValueError("factor shapes must be sa [ceil(Kb/4), M_total] and sb [G, Nb, ceil(Kb/4)]")
     _call(
         "gemm_fp8_grouped_contiguous_ue8m0",
-        _ptr(A), _ptr(sa), sa.stride(0), _ptr(B), _ptr(sb), _ptr(m_indices), _ptr(D),
+        _ptr(A), _ptr(sa), _ld(sa), _ptr(B), _ptr(sb), _ptr(m_indices), _ptr(D),
         M, N, K, G, _stream(stream),
     )
     return D
@@ -594,7 +601,7 @@ def fp8_cast_per_token_ue8m0(x, q=None, sa=None, stream=None):
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     _unit_inner(sa, "sa")
-    _call("fp8_cast_per_token_ue8m0" + sfx, _ptr(x), x.stride(0), _ptr(q), _ptr(sa), sa.stride(0), M, K, _stream(stream))
+    _call("fp8_cast_per_token_ue8m0" + sfx, _ptr(x), _ld(x), _ptr(q), _ptr(sa), _ld(sa), M, K, _stream(stream))
     return q, sa
 
 
@@ -612,7 +619,7 @@ def fp8_cast_per_block_ue8m0(w, q=None, sb=None, stream=None):
     sb = _i32(sb, "sb")
     if not (q.is_contiguous() and sb.is_contiguous()):
         raise ValueError("q and sb must be contiguous")
-    _call("fp8_cast_per_block_ue8m0" + sfx, _ptr(w), w.stride(0), _ptr(q), _ptr(sb), N, K, _stream(stream))
+    _call("fp8_cast_per_block_ue8m0" + sfx, _ptr(w), _ld(w), _ptr(q), _ptr(sb), N, K, _stream(stream))
     return q, sb
 
 
