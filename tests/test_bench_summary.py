@@ -81,3 +81,17 @@ def test_summary_rejects_a_log_that_does_not_match(tmp_path, monkeypatch):
     (d / "trace" / "launch_log.json").write_text(json.dumps([[0, "timed"]] * 2))
     with pytest.raises(SystemExit, match="logged GEMM calls"):
         bench.summarize(str(d), "masked_16x256", 20)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU only: --gpus 2, or a launcher's WORLD_SIZE of
+    2, ends with a message before any device work."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           timeout=300, env=dict(os.environ, **env), cwd=root)
+        assert r.returncode != 0
+        assert "one GPU" in r.stdout
