@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The loaded HIP library; skips off-GPU, fails loudly on a GPU machine without it."""
+    """The loaded HIP library; skips without a GPU, fails loudly with a GPU but without the library."""
     import torch
 
     if not torch.cuda.is_available():
