@@ -73,6 +73,27 @@ def test_contiguous_exact_regime_bitwise(gpu_lib):
     assert (bits[~valid] == SENTINEL_BF16).all()
 
 
+@pytest.mark.parametrize("G,seed", [(32, 1), (64, 2)])
+def test_contiguous_many_experts_bitwise(gpu_lib, G, seed):
+    """Many experts with random row counts (zeros included), each segment
+    padded to 128 rows: exact bits for every expert's rows, padding rows
+    untouched.  Two-expert 256-row tiles and padding-only blocks occur
+    throughout."""
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, 300, G)
+    rows[::7] = 0
+    idx = synth.contiguous_indices(rows, pad_to=128)
+    M, N, K = idx.shape[0], 392, 384
+    announce(f"contiguous {G} experts, {M} rows")
+    qa, sa, _, _ = exact_regime(rng, M, N, K)
+    _, _, qb, sb = exact_regime(rng, 1, N, K, groups=(1, G))
+    D = run_contig(gpu_lib, qa, sa, qb, sb, idx)
+    X, valid = ogemm.gemm_grouped_contiguous(qa, sa, qb, sb, idx)
+    bits = bf16_bits(D)
+    assert np.array_equal(bits[valid], ogemm.to_bf16(X[valid]))
+    assert (bits[~valid] == SENTINEL_BF16).all()
+
+
 @pytest.mark.parametrize("K", [512, 0])
 def test_contiguous_index_past_experts_is_padding(gpu_lib, K):
     """Blocks whose index is G or larger are padding: their rows stay
