@@ -6,15 +6,23 @@
 // the weights are read once and every activation row is reused across all of
 // them.  The work is the weight stream, so the kernel is built around it:
 //
-//  * No LDS staging and no barriers in the main loop.  Every wave loads its
-//    own operand fragments straight from memory into registers, already in
-//    MFMA operand layout, one K slice ahead of the slice it multiplies; the
-//    waves of a CU run independently and keep the memory pipe busy.
-//  * Inside a K slice both operands are read with the same byte permutation
-//    (lane group q holds bytes [16q, 16q+16) and [64+16q, 64+16q+16) of its
-//    row, where the MFMA expects [32q, 32q+32)); a dot product over the slice
-//    does not depend on the order of its terms' pairing, and each load
-//    instruction then covers 64 contiguous bytes of 16 rows.
+//  * No barriers in the main loop.  Every wave streams its own K slices,
+//    one slice ahead of the slice it multiplies; the waves of a CU run
+//    independently and keep the memory pipe busy.
+//  * The weights go straight from memory into registers, already in MFMA
+//    operand layout.  Inside a K slice both operands use the same byte
+//    permutation (lane group q holds bytes [16q, 16q+16) and [64+16q,
+//    64+16q+16) of its row, where the MFMA expects [32q, 32q+32)); a dot
+//    product over the slice does not depend on the order of its terms'
+//    pairing, and each weight load then covers 64 contiguous bytes of 16
+//    rows.
+//  * The activations are staged through a two-slot LDS ring of the wave's
+//    own with direct-to-LDS loads of whole 128-byte rows (8 rows per
+//    instruction), and the fragments are read from there.  The activation
+//    rows are cache hits (every column tile reads them), and on a cache hit
+//    a load of half rows moves less than half the bytes per unit of time of
+//    a whole-row load: staging them this way is what lets the weight
+//    stream run at the memory's rate.
 //  * A workgroup is four waves on one column tile (16 * CF weight rows) and
 //    one row part (16 * MF activation rows; more rows go to further parts),
 //    each wave on a quarter of the workgroup's K range.  The four fp32
@@ -39,10 +47,11 @@ namespace fg {
 constexpr int kSkinnyDepth = FG_SKINNY_DEPTH;
 
 // Workgroups per CU the registers allow: a wave holds DEPTH slices of
-// fragments and scales, the slice partials and the accumulators; two
-// workgroups per CU (two waves per SIMD) leave it 256 registers.
+// weight fragments, one slice of activation fragments, the slice partials of
+// one fragment row and the accumulators; two workgroups per CU (two waves per
+// SIMD) leave it 256 registers.
 constexpr __host__ __device__ int skinny_occupancy(int mf, int cf) {
-  return kSkinnyDepth * (8 * mf + 8 * cf + mf) + 8 * mf * cf <= 240 ? 2 : 1;
+  return kSkinnyDepth * 8 * cf + 8 * mf + 4 * cf + 4 * mf * cf <= 200 ? 2 : 1;
 }
 
 template <int MF_, int CF_>
@@ -53,50 +62,78 @@ struct SkinnyCfg {
   static constexpr int ROWS = 16 * MF, COLS = 16 * CF;
   static constexpr int GROUPS = MF * CF;  // 16x16 output blocks of the tile
   static constexpr int GPW = GROUPS / WAVES;
-  static constexpr int DEPTH = kSkinnyDepth;  // slices of fragments per wave in the ring
-  static constexpr int OCC = skinny_occupancy(MF, CF);
-  static constexpr int LDS = WAVES * GROUPS * 64 * 16 + 16;  // wave partials + flag
+  static constexpr int DEPTH = kSkinnyDepth;  // slices in flight per wave
+  // a wave's LDS ring slot: the slice's activation rows (128 B each), then
+  // their scales (4 B each)
+  static constexpr int SLOT = ROWS * 128 + ROWS * 4;
+  static constexpr int SA_OFF = ROWS * 128;
+  static constexpr int RING = DEPTH * SLOT;
+  // direct-to-LDS loads per slice: 8 activation rows each, then 64 scales each
+  static constexpr int A_LOADS = ROWS / 8, SA_LOADS = (ROWS + 63) / 64;
+  static constexpr int LDS = WAVES * RING + 16;  // rings (then wave partials) + flag
+  static constexpr int OCC = skinny_occupancy(MF, CF) == 2 && 2 * LDS <= 160 * 1024 ? 2 : 1;
   static_assert(GROUPS % WAVES == 0, "output blocks split over the waves");
   static_assert(128 % COLS == 0, "a column tile lies in one weight-scale block");
+  static_assert(GROUPS * 64 * 16 <= RING, "a wave's partials fit in its ring");
+  static_assert(DEPTH == 2, "the LDS waits count one slice of loads in flight");
 };
 
-// Fragments and scales of one K slice, as this wave needs them.
+// The weight fragments and weight scale of one K slice (the activations of
+// the slice are in the wave's ring slot).
 template <class C>
 struct SkinnySlice {
-  i32x8 a[C::MF];
   i32x8 b[C::CF];
-  float sa[C::MF];
   float sb;
 };
 
 // Per-lane load geometry of a wave (constant over the K loop).
 struct SkinnyLanes {
   __amdgpu_buffer_rsrc_t ra, rb, rsa;
-  int a_voff, b_voff;  // this lane's row (16 apart per fragment) and 16-byte column
-  int a_step, b_step;  // bytes between fragments (16 rows)
-  int sa_voff;         // this lane's activation row, bytes
+  int a_voff[2];       // activation row-load lane offsets for even / odd 8-row loads (load j adds 8 j rows)
+  int a_col[2];        // their chunks' first column inside a slice
+  int a_step8;         // bytes between 8-row loads
+  int b_voff, b_step;  // this lane's weight row and 16-byte column; bytes between fragments (16 rows)
+  int sa_voff;         // this lane's activation scale (row `lane` of the part), bytes
   int sa_kstep;        // bytes between K slices of sa
   const float* sb;     // sb[nb][.] of the tile's weight-scale block
-  int kq16;            // first column of this lane's 16-byte chunk inside a slice (16 * lane group)
+  int kq16;            // first column of this lane's 16-byte weight chunk inside a slice (16 * lane group)
   int K;
 };
 
+// Wait until at most N vector memory operations of this wave are outstanding
+// (they complete in issue order); direct-to-LDS loads count, and the
+// compiler does not track their LDS writes.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Issue the loads of slice kb: activations and their scales into ring slot
+// `slot` (A_LOADS + SA_LOADS direct-to-LDS loads), then the weight
+// fragments into f (2 CF loads), then the weight scale (a scalar load).
 template <class C>
-__device__ __forceinline__ void skinny_load(SkinnySlice<C>& f, const SkinnyLanes& g, int kb) {
+__device__ __forceinline__ void skinny_load(SkinnySlice<C>& f, uint8_t* slot, const SkinnyLanes& g, int kb,
+                                            int lane) {
   const int k0 = kb * 128;
-  // K tail: chunks at or past column K read as zeros (k_clip).  Always true
-  // for whole slices; the selects cost a few VALU ops in a kernel that waits
-  // on memory.
-  const bool lo_in = k0 + g.kq16 < g.K, hi_in = k0 + 64 + g.kq16 < g.K;
+  // K tail: chunks at or past column K read as zeros (k_clip).  Always in
+  // range for whole slices; the selects cost a few VALU ops in a kernel that
+  // waits on memory.
+  const bool a_in[2] = {k0 + g.a_col[0] < g.K, k0 + g.a_col[1] < g.K};
 #pragma unroll
-  for (int i = 0; i < C::MF; ++i) {
-    const int v = g.a_voff + i * g.a_step;
-    const i32x4 lo =
-        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.ra, lo_in ? v : kOobOffset, k0, 0));
-    const i32x4 hi =
-        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.ra, hi_in ? v : kOobOffset, k0 + 64, 0));
-    f.a[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int v = a_in[j & 1] ? g.a_voff[j & 1] + (j >> 1) * 2 * g.a_step8 : kOobOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.ra, (__attribute__((address_space(3))) void*)(slot + j * 1024), 16, v,
+                                             k0, 0, 0);
   }
+#pragma unroll
+  for (int j = 0; j < C::SA_LOADS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rsa, (__attribute__((address_space(3))) void*)(slot + C::SA_OFF + j * 256),
+                                             4, g.sa_voff + j * 256, kb * g.sa_kstep, 0, 0);
+  const bool lo_in = k0 + g.kq16 < g.K, hi_in = k0 + 64 + g.kq16 < g.K;
 #pragma unroll
   for (int j = 0; j < C::CF; ++j) {
     const int v = g.b_voff + j * g.b_step;
@@ -106,30 +143,35 @@ __device__ __forceinline__ void skinny_load(SkinnySlice<C>& f, const SkinnyLanes
         __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, hi_in ? v : kOobOffset, k0 + 64, 0));
     f.b[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-#pragma unroll
-  for (int i = 0; i < C::MF; ++i)
-    f.sa[i] = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(g.rsa, g.sa_voff + kb * g.sa_kstep + i * 64, 0, 0));
   f.sb = *(const __attribute__((address_space(4))) float*)(g.sb + kb);
 }
 
-// acc += P_kb * (sa * sb) for every output block of the wave.
-template <class C>
-__device__ __forceinline__ void skinny_compute(const SkinnySlice<C>& f, float (&acc)[C::GROUPS][4]) {
-  f32x4 P[C::MF][C::CF];
+// acc += P_kb * (sa * sb) for every output block of the wave, with the
+// slice's activations read from ring slot `slot`.  WAIT: vector memory
+// operations issued after this slice's weight loads that may stay
+// outstanding (the loads of the next slice; their weight loads are not
+// counted, so the wait holds whether or not they were issued).
+template <class C, int WAIT>
+__device__ __forceinline__ void skinny_compute(const SkinnySlice<C>& f, const uint8_t* slot, int lane,
+                                               float (&acc)[C::GROUPS][4]) {
+  wait_vm<WAIT + 2 * C::CF>();  // this slice's activation loads have landed in the ring
+  const int l16 = lane & 15, q = lane >> 4;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < C::MF; ++i)
-#pragma unroll
-    for (int j = 0; j < C::CF; ++j)
-      P[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
   for (int i = 0; i < C::MF; ++i) {
-    const float s = f.sa[i] * f.sb;
+    // row 16 i + l16, logical chunks q and 4 + q (the weights' permutation),
+    // at their swizzled places
+    const int r = 16 * i + l16;
+    const i32x8 a = lds_frag(slot, r * 128 + ((q ^ swz16(r)) << 4), r * 128 + (((4 + q) ^ swz16(r)) << 4));
+    const float s = *(const float*)(slot + C::SA_OFF + r * 4) * f.sb;
+    f32x4 P[C::CF];
+#pragma unroll
+    for (int j = 0; j < C::CF; ++j)
+      P[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], a, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < C::CF; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i * C::CF + j][r] = __builtin_fmaf(P[i][j][r], s, acc[i * C::CF + j][r]);
+      for (int r4 = 0; r4 < 4; ++r4) acc[i * C::CF + j][r4] = __builtin_fmaf(P[j][r4], s, acc[i * C::CF + j][r4]);
   }
 }
 
@@ -178,13 +220,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   SkinnyLanes g;
   const int l16 = lane & 15, q = lane >> 4;
   g.ra = make_rsrc(p.A + (int64_t)r0 * p.lda, (int64_t)(p.rows - r0 - 1) * p.lda + p.K);
-  g.a_voff = l16 * (int)p.lda + 16 * q;
-  g.a_step = 16 * (int)p.lda;
+  {
+    // 8-row activation load j: lane -> row 8 j + lane / 8, at the 16-byte
+    // place lane % 8 of its LDS row, which holds logical chunk
+    // (lane % 8) ^ swz16(row); swz16(8 j + r) = r ^ (j & 1).  The odd loads'
+    // offsets carry their extra 8 rows.
+    const int r8 = lane >> 3, c_even = (lane & 7) ^ r8, c_odd = c_even ^ 1;
+    g.a_voff[0] = r8 * (int)p.lda + 16 * c_even;
+    g.a_voff[1] = (8 + r8) * (int)p.lda + 16 * c_odd;
+    g.a_col[0] = 16 * c_even;
+    g.a_col[1] = 16 * c_odd;
+    g.a_step8 = 8 * (int)p.lda;
+  }
   g.rb = make_rsrc(p.B + (int64_t)n0 * p.ldb, (int64_t)(p.N - n0 - 1) * p.ldb + p.K);
   g.b_voff = l16 * (int)p.ldb + 16 * q;
   g.b_step = 16 * (int)p.ldb;
   g.rsa = make_rsrc(p.sa + r0, ((int64_t)(p.Kb - 1) * p.ld_sa + p.rows - r0) * 4);
-  g.sa_voff = l16 * 4;
+  g.sa_voff = lane * 4;
   g.sa_kstep = (int)p.ld_sa * 4;
   g.sb = p.sb + (int64_t)(n0 >> 7) * p.ld_sb;
   g.kq16 = 16 * q;
@@ -208,49 +260,56 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
       const int j = i + rot;
       return kw0 + (j >= n ? j - n : j);
     };
-    // A ring of DEPTH register slices: the loads of the next DEPTH - 1
-    // slices are in flight while one slice's MFMAs run.  The n % DEPTH
-    // leading slices go first on their own, so the pipelined loop has no
-    // conditional work (the compiler would otherwise sink a conditionally
-    // used load down to its use); its last iterations fetch the final slice
-    // again, unused.  The scheduling barriers keep each batch of loads ahead
-    // of the MFMAs that do not need it.
+    // A ring of DEPTH slices (weights in registers, activations in the
+    // wave's LDS slots): the loads of the next slice are in flight while one
+    // slice's MFMAs run.  The n % DEPTH leading slices go first on their
+    // own, so the pipelined loop has no conditional work (the compiler would
+    // otherwise sink a conditionally used load down to its use); its last
+    // iterations fetch the final slice again, unused.  The scheduling
+    // barriers keep each batch of loads ahead of the MFMAs that do not need
+    // it.
     constexpr int DEPTH = C::DEPTH;
+    constexpr int NA = C::A_LOADS + C::SA_LOADS;
+    uint8_t* ring = lds + wave * C::RING;
     SkinnySlice<C> f[DEPTH];
     int i = 0;
     for (const int lead = n % DEPTH; i < lead; ++i) {
-      skinny_load<C>(f[0], g, kat(i));
-      skinny_compute<C>(f[0], acc);
+      skinny_load<C>(f[0], ring, g, kat(i), lane);
+      skinny_compute<C, 0>(f[0], ring, lane, acc);
     }
     if (i < n) {
 #pragma unroll
-      for (int d = 0; d + 1 < DEPTH; ++d) skinny_load<C>(f[d], g, kat(min(i + d, n - 1)));
+      for (int d = 0; d + 1 < DEPTH; ++d) skinny_load<C>(f[d], ring + d * C::SLOT, g, kat(min(i + d, n - 1)), lane);
       for (; i < n; i += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
           __builtin_amdgcn_sched_barrier(0);
-          skinny_load<C>(f[(d + DEPTH - 1) % DEPTH], g, kat(min(i + d + DEPTH - 1, n - 1)));
+          skinny_load<C>(f[(d + DEPTH - 1) % DEPTH], ring + ((d + DEPTH - 1) % DEPTH) * C::SLOT, g,
+                         kat(min(i + d + DEPTH - 1, n - 1)), lane);
           __builtin_amdgcn_sched_barrier(0);
-          skinny_compute<C>(f[d], acc);
+          skinny_compute<C, NA>(f[d], ring + d * C::SLOT, lane, acc);
         }
       }
     }
+    // no direct-to-LDS load may still be writing the ring (the partials go there)
+    wait_vm<0>();
   }
 
   // ---- add the four wave partials in wave order; wave w keeps blocks
   // [w GPW, (w+1) GPW) ----
-  float4* red = (float4*)lds;
+  // (each wave's partials in its own ring, which no other wave uses)
+  auto red = [&](int w) { return (float4*)(lds + w * C::RING); };
 #pragma unroll
-  for (int x = 0; x < C::GROUPS; ++x) red[(wave * C::GROUPS + x) * 64 + lane] = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+  for (int x = 0; x < C::GROUPS; ++x) red(wave)[x * 64 + lane] = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
   __syncthreads();
   float sum[C::GPW][4];
 #pragma unroll
   for (int y = 0; y < C::GPW; ++y) {
     const int x = wave * C::GPW + y;
-    float4 t = red[x * 64 + lane];
+    float4 t = red(0)[x * 64 + lane];
 #pragma unroll
     for (int w = 1; w < C::WAVES; ++w) {
-      const float4 u = red[(w * C::GROUPS + x) * 64 + lane];
+      const float4 u = red(w)[x * 64 + lane];
       t.x += u.x;
       t.y += u.y;
       t.z += u.z;
