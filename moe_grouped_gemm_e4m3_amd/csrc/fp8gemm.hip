@@ -437,18 +437,21 @@ bool prefer_big(int64_t big_tiles) {
 // ---------------------------------------------------------------------------
 // Skinny kernel (dense, M <= 128).  The plan picks the activation fragments
 // per workgroup (64 rows; more rows go to a second row part), the column-tile
-// width (16 CF weight rows per workgroup) and the K split.  Measured on MI355X
-// on the decode shapes (M = 64, 128; N = 2112 .. 7168): with one row part
-// 32-column tiles are best (narrower tiles make every CU read the activations
-// again for fewer weights, wider ones leave CUs idle); with two row parts
-// 64-column tiles are, 13 % faster than one part of 128 rows with 32-column
-// tiles.  The K split only has to bring the workgroup count near the CU
-// count; each further split adds fp32 partial traffic and a reduction.
+// width (16 CF weight rows per workgroup) and the K split.  Every CU reads
+// the activations of its K range again, so wider tiles read fewer bytes per
+// weight byte; a K split brings the workgroup count up to the CU count but
+// adds an exchange of fp32 partials at the end, whose latency grows with the
+// number of splits.  Measured on MI355X on the decode shapes (M = 64, 128;
+// N = 2112, 4096, 7168; K = 7168, 2048), the best plans are: 32-column tiles
+// split at most three ways while that fills three quarters of the CUs in
+// one round, else 64-column tiles split at most three ways (when that gives
+// more workgroups), one round where possible.
 // The plan depends only on the shape, the device's CU count and whether the
 // call brings split-K buffers (`split_ok`), never on earlier calls or on
 // stream capture, so a call's summation order (and its bits) is fixed by its
 // arguments.  FG_SKINNY="CF,SPLITS[,MF]" overrides the choice (tuning and
-// tests; MF = 8 keeps 128 rows in one part).
+// tests; MF = 8 keeps 128 rows in one part, with CF = 1: the LDS ring of a
+// wider tile would not fit).
 
 struct SkinnyPlan {
   int mf = 0, cf = 0, splits = 1, parts = 1;
@@ -475,7 +478,7 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
     const int64_t units = units_of(cf);
     return sp == 1 || (units <= kSkinnyMaxUnits && (int64_t)sp * units * pl.mf * cf * 1024 <= kSplitPartialMax);
   };
-  if (nenv >= 2 && (cf_env == 1 || cf_env == 2 || cf_env == 4) && pl.mf * cf_env <= 16 && sp_env >= 1 &&
+  if (nenv >= 2 && (cf_env == 1 || cf_env == 2 || cf_env == 4) && (pl.mf == 4 || cf_env == 1) && sp_env >= 1 &&
       (sp_env == 1 || split_ok)) {
     if (!fits(cf_env, sp_env)) return false;
     pl.cf = cf_env;
@@ -484,24 +487,29 @@ bool plan_skinny(int M, int N, int K, int64_t lda, int64_t ld_sa, int cus, bool 
     *out = pl;
     return true;
   }
-  // 32-column tiles for one row part; with two parts, 64-column ones (each
-  // workgroup then reads as many weight bytes per activation byte as a
-  // one-part 32-column tile, and the parts double the workgroups).  A long
-  // K range (32 slices or more) with one row part and a workspace takes
-  // 64-column tiles split four ways instead: a CU then fetches half the
-  // activation bytes per weight byte, which is what these launches are bound
-  // by (measured at M = 64, K = 7168: 7-8 % faster at N = 2112 and 4096).
-  pl.cf = pl.parts > 1 ? 4 : 2;
-  const bool wide = split_ok && pl.parts == 1 && Kb >= 32;
-  if (wide) pl.cf = 4;
-  pl.units = units_of(pl.cf);
-  int sp = 1;
-  if (wide) {
-    sp = 4;
-  } else if (split_ok && pl.units * 4 < (int64_t)cus * 3) {
-    sp = pl.units * 4 >= cus ? 2 : 4;
+  // splits (up to three, with at least one K slice per wave) that keep the
+  // launch in one round of the CUs
+  const int smax = split_ok ? 3 : 1;
+  auto splits_for = [&](int cf) {
+    const int64_t u = units_of(cf);
+    int sp = 1;
+    while (sp < smax && u * (sp + 1) <= cus && Kb >= 4 * (sp + 1) && fits(cf, sp + 1)) ++sp;
+    return sp;
+  };
+  const int64_t u2 = units_of(2), u4 = units_of(4);
+  const int s2 = splits_for(2), s4 = splits_for(4);
+  int sp;
+  if (pl.mf == 8) {
+    pl.cf = 1;  // 128-row fragments (FG_SKINNY only): the one width whose LDS ring fits
+    sp = splits_for(1);
+  } else if (u2 <= cus && (u2 * s2 * 4 >= (int64_t)cus * 3 || u4 * s4 <= u2 * s2)) {
+    pl.cf = 2;
+    sp = s2;
+  } else {
+    pl.cf = 4;
+    sp = s4;
   }
-  while (sp > 1 && (Kb < 4 * sp || !fits(pl.cf, sp))) sp /= 2;
+  pl.units = units_of(pl.cf);
   pl.splits = sp;
   *out = pl;
   return pl.cf > 0;
@@ -554,7 +562,7 @@ fg_status launch_skinny(fg::GemmParams& p, const SkinnyPlan& pl, const SplitWs* 
 #define FG_SKINNY_CASE(MF, CF) \
   if (pl.mf == MF && pl.cf == CF) return launch_skinny_cfg<MF, CF, ADD_C>(p, pl.splits, pl.parts, stream, what);
   FG_SKINNY_CASE(4, 1) FG_SKINNY_CASE(4, 2) FG_SKINNY_CASE(4, 4)
-  FG_SKINNY_CASE(8, 1) FG_SKINNY_CASE(8, 2)
+  FG_SKINNY_CASE(8, 1)
 #undef FG_SKINNY_CASE
   return fail(FG_EUNSUPPORTED, "%s: no skinny configuration", what);
 }

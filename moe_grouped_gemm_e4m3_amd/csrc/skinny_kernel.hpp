@@ -6,23 +6,21 @@
 // the weights are read once and every activation row is reused across all of
 // them.  The work is the weight stream, so the kernel is built around it:
 //
-//  * No barriers in the main loop.  Every wave streams its own K slices,
-//    one slice ahead of the slice it multiplies; the waves of a CU run
-//    independently and keep the memory pipe busy.
-//  * The weights go straight from memory into registers, already in MFMA
-//    operand layout.  Inside a K slice both operands use the same byte
-//    permutation (lane group q holds bytes [16q, 16q+16) and [64+16q,
-//    64+16q+16) of its row, where the MFMA expects [32q, 32q+32)); a dot
-//    product over the slice does not depend on the order of its terms'
-//    pairing, and each weight load then covers 64 contiguous bytes of 16
-//    rows.
-//  * The activations are staged through a two-slot LDS ring of the wave's
-//    own with direct-to-LDS loads of whole 128-byte rows (8 rows per
-//    instruction), and the fragments are read from there.  The activation
-//    rows are cache hits (every column tile reads them), and on a cache hit
-//    a load of half rows moves less than half the bytes per unit of time of
-//    a whole-row load: staging them this way is what lets the weight
-//    stream run at the memory's rate.
+//  * No barriers in the main loop.  Every wave streams its own K slices
+//    through a two-slot LDS ring of its own, one slice ahead of the slice it
+//    multiplies; the waves of a CU run independently and keep the memory
+//    pipe busy.
+//  * Both operands reach the ring by direct-to-LDS loads of whole 128-byte
+//    rows (8 rows per instruction), and the MFMA fragments are read from
+//    there.  The fragment layout (16 rows per instruction, 32 bytes per lane)
+//    would make a register load touch 16 rows at 64 bytes each, and such
+//    half-row loads move 2-3x fewer bytes per unit of time than whole-row
+//    loads when they hit in the cache (as the activations do: every column
+//    tile reads them) and about 10 % fewer from HBM.
+//  * Both operands' fragments take, in lane group q, the 16-byte chunks q
+//    and 4 + q of their row (the MFMA expects chunks 2q and 2q + 1): one
+//    permutation of K applied to both sides of every dot product leaves the
+//    product unchanged.
 //  * A workgroup is four waves on one column tile (16 * CF weight rows) and
 //    one row part (16 * MF activation rows; more rows go to further parts),
 //    each wave on a quarter of the workgroup's K range.  The four fp32
@@ -46,12 +44,11 @@ namespace fg {
 #endif
 constexpr int kSkinnyDepth = FG_SKINNY_DEPTH;
 
-// Workgroups per CU the registers allow: a wave holds DEPTH slices of
-// weight fragments, one slice of activation fragments, the slice partials of
-// one fragment row and the accumulators; two workgroups per CU (two waves per
-// SIMD) leave it 256 registers.
+// Workgroups per CU the registers allow: a wave holds one slice of
+// fragments, the slice partials of one fragment row and the accumulators;
+// two workgroups per CU (two waves per SIMD) leave it 256 registers.
 constexpr __host__ __device__ int skinny_occupancy(int mf, int cf) {
-  return kSkinnyDepth * 8 * cf + 8 * mf + 4 * cf + 4 * mf * cf <= 200 ? 2 : 1;
+  return 8 * mf + 8 * cf + 4 * cf + 4 * mf * cf <= 200 ? 2 : 1;
 }
 
 template <int MF_, int CF_>
@@ -63,13 +60,15 @@ struct SkinnyCfg {
   static constexpr int GROUPS = MF * CF;  // 16x16 output blocks of the tile
   static constexpr int GPW = GROUPS / WAVES;
   static constexpr int DEPTH = kSkinnyDepth;  // slices in flight per wave
-  // a wave's LDS ring slot: the slice's activation rows (128 B each), then
-  // their scales (4 B each)
-  static constexpr int SLOT = ROWS * 128 + ROWS * 4;
-  static constexpr int SA_OFF = ROWS * 128;
+  // a wave's LDS ring slot: the slice's activation rows and weight rows
+  // (128 B each), then the activation scales (4 B each)
+  static constexpr int SLOT = ROWS * 128 + COLS * 128 + ROWS * 4;
+  static constexpr int B_OFF = ROWS * 128;
+  static constexpr int SA_OFF = (ROWS + COLS) * 128;
   static constexpr int RING = DEPTH * SLOT;
-  // direct-to-LDS loads per slice: 8 activation rows each, then 64 scales each
-  static constexpr int A_LOADS = ROWS / 8, SA_LOADS = (ROWS + 63) / 64;
+  // direct-to-LDS loads per slice: 8 activation or weight rows each, 64 scales each
+  static constexpr int A_LOADS = ROWS / 8, B_LOADS = COLS / 8, SA_LOADS = (ROWS + 63) / 64;
+  static constexpr int NLOADS = A_LOADS + B_LOADS + SA_LOADS;
   static constexpr int LDS = WAVES * RING + 16;  // rings (then wave partials) + flag
   static constexpr int OCC = skinny_occupancy(MF, CF) == 2 && 2 * LDS <= 160 * 1024 ? 2 : 1;
   static_assert(GROUPS % WAVES == 0, "output blocks split over the waves");
@@ -78,25 +77,25 @@ struct SkinnyCfg {
   static_assert(DEPTH == 2, "the LDS waits count one slice of loads in flight");
 };
 
-// The weight fragments and weight scale of one K slice (the activations of
-// the slice are in the wave's ring slot).
+// The weight scale of one K slice (its operands are in the wave's ring slot).
 template <class C>
 struct SkinnySlice {
-  i32x8 b[C::CF];
   float sb;
 };
 
 // Per-lane load geometry of a wave (constant over the K loop).
 struct SkinnyLanes {
   __amdgpu_buffer_rsrc_t ra, rb, rsa;
-  int a_voff[2];       // activation row-load lane offsets for even / odd 8-row loads (load j adds 8 j rows)
-  int a_col[2];        // their chunks' first column inside a slice
-  int a_step8;         // bytes between 8-row loads
-  int b_voff, b_step;  // this lane's weight row and 16-byte column; bytes between fragments (16 rows)
+  // 8-row load j puts lane l's 16 bytes at LDS place l % 8 of row 8 j + l / 8;
+  // the place holds logical chunk (l % 8) ^ swz16(row), and swz16(8 j + r) =
+  // r ^ (j & 1), so even and odd loads differ by one chunk
+  int a_voff[2];       // activation lane offsets of even / odd loads (the odd ones carry their extra 8 rows)
+  int b_voff[2];       // the same for the weights
+  int a_col[2];        // first column of the lane's chunk in even / odd loads
+  int a_step8, b_step8;  // bytes between 8-row loads
   int sa_voff;         // this lane's activation scale (row `lane` of the part), bytes
   int sa_kstep;        // bytes between K slices of sa
   const float* sb;     // sb[nb][.] of the tile's weight-scale block
-  int kq16;            // first column of this lane's 16-byte weight chunk inside a slice (16 * lane group)
   int K;
 };
 
@@ -112,9 +111,9 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Issue the loads of slice kb: activations and their scales into ring slot
-// `slot` (A_LOADS + SA_LOADS direct-to-LDS loads), then the weight
-// fragments into f (2 CF loads), then the weight scale (a scalar load).
+// Issue the loads of slice kb into ring slot `slot`: activation rows, weight
+// rows and activation scales (NLOADS direct-to-LDS loads), then the weight
+// scale (a scalar load) into f.
 template <class C>
 __device__ __forceinline__ void skinny_load(SkinnySlice<C>& f, uint8_t* slot, const SkinnyLanes& g, int kb,
                                             int lane) {
@@ -133,41 +132,38 @@ __device__ __forceinline__ void skinny_load(SkinnySlice<C>& f, uint8_t* slot, co
   for (int j = 0; j < C::SA_LOADS; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rsa, (__attribute__((address_space(3))) void*)(slot + C::SA_OFF + j * 256),
                                              4, g.sa_voff + j * 256, kb * g.sa_kstep, 0, 0);
-  const bool lo_in = k0 + g.kq16 < g.K, hi_in = k0 + 64 + g.kq16 < g.K;
 #pragma unroll
-  for (int j = 0; j < C::CF; ++j) {
-    const int v = g.b_voff + j * g.b_step;
-    const i32x4 lo =
-        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, lo_in ? v : kOobOffset, k0, 0));
-    const i32x4 hi =
-        __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, hi_in ? v : kOobOffset, k0 + 64, 0));
-    f.b[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const int v = a_in[j & 1] ? g.b_voff[j & 1] + (j >> 1) * 2 * g.b_step8 : kOobOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rb, (__attribute__((address_space(3))) void*)(slot + C::B_OFF + j * 1024),
+                                             16, v, k0, 0, 0);
   }
   f.sb = *(const __attribute__((address_space(4))) float*)(g.sb + kb);
 }
 
 // acc += P_kb * (sa * sb) for every output block of the wave, with the
-// slice's activations read from ring slot `slot`.  WAIT: vector memory
-// operations issued after this slice's weight loads that may stay
-// outstanding (the loads of the next slice; their weight loads are not
-// counted, so the wait holds whether or not they were issued).
+// slice's operands read from ring slot `slot`.  WAIT: the loads issued after
+// this slice's that may stay outstanding (those of the next slice, or none).
 template <class C, int WAIT>
 __device__ __forceinline__ void skinny_compute(const SkinnySlice<C>& f, const uint8_t* slot, int lane,
                                                float (&acc)[C::GROUPS][4]) {
-  wait_vm<WAIT + 2 * C::CF>();  // this slice's activation loads have landed in the ring
+  wait_vm<WAIT>();  // this slice's loads have landed in the ring
   const int l16 = lane & 15, q = lane >> 4;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < C::MF; ++i) {
-    // row 16 i + l16, logical chunks q and 4 + q (the weights' permutation),
+    // row 16 i + l16, logical chunks q and 4 + q,
     // at their swizzled places
     const int r = 16 * i + l16;
     const i32x8 a = lds_frag(slot, r * 128 + ((q ^ swz16(r)) << 4), r * 128 + (((4 + q) ^ swz16(r)) << 4));
     const float s = *(const float*)(slot + C::SA_OFF + r * 4) * f.sb;
     f32x4 P[C::CF];
 #pragma unroll
-    for (int j = 0; j < C::CF; ++j)
-      P[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], a, zero, 0, 0, 0, 0, 0, 0);
+    for (int j = 0; j < C::CF; ++j) {
+      const int rb = 16 * j + l16;
+      const i32x8 b = lds_frag(slot + C::B_OFF, rb * 128 + ((q ^ swz16(rb)) << 4), rb * 128 + (((4 + q) ^ swz16(rb)) << 4));
+      P[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, zero, 0, 0, 0, 0, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < C::CF; ++j)
 #pragma unroll
@@ -218,28 +214,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
   const int kw0 = kb0 + (kb1 - kb0) * wave / C::WAVES, kw1 = kb0 + (kb1 - kb0) * (wave + 1) / C::WAVES;
 
   SkinnyLanes g;
-  const int l16 = lane & 15, q = lane >> 4;
   g.ra = make_rsrc(p.A + (int64_t)r0 * p.lda, (int64_t)(p.rows - r0 - 1) * p.lda + p.K);
   {
-    // 8-row activation load j: lane -> row 8 j + lane / 8, at the 16-byte
-    // place lane % 8 of its LDS row, which holds logical chunk
-    // (lane % 8) ^ swz16(row); swz16(8 j + r) = r ^ (j & 1).  The odd loads'
-    // offsets carry their extra 8 rows.
     const int r8 = lane >> 3, c_even = (lane & 7) ^ r8, c_odd = c_even ^ 1;
     g.a_voff[0] = r8 * (int)p.lda + 16 * c_even;
     g.a_voff[1] = (8 + r8) * (int)p.lda + 16 * c_odd;
     g.a_col[0] = 16 * c_even;
     g.a_col[1] = 16 * c_odd;
     g.a_step8 = 8 * (int)p.lda;
+    g.b_voff[0] = r8 * (int)p.ldb + 16 * c_even;
+    g.b_voff[1] = (8 + r8) * (int)p.ldb + 16 * c_odd;
+    g.b_step8 = 8 * (int)p.ldb;
   }
   g.rb = make_rsrc(p.B + (int64_t)n0 * p.ldb, (int64_t)(p.N - n0 - 1) * p.ldb + p.K);
-  g.b_voff = l16 * (int)p.ldb + 16 * q;
-  g.b_step = 16 * (int)p.ldb;
   g.rsa = make_rsrc(p.sa + r0, ((int64_t)(p.Kb - 1) * p.ld_sa + p.rows - r0) * 4);
   g.sa_voff = lane * 4;
   g.sa_kstep = (int)p.ld_sa * 4;
   g.sb = p.sb + (int64_t)(n0 >> 7) * p.ld_sb;
-  g.kq16 = 16 * q;
   g.K = p.K;
 
   float acc[C::GROUPS][4];
@@ -269,7 +260,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_fp8_skinny_kernel(Gem
     // barriers keep each batch of loads ahead of the MFMAs that do not need
     // it.
     constexpr int DEPTH = C::DEPTH;
-    constexpr int NA = C::A_LOADS + C::SA_LOADS;
+    constexpr int NA = C::NLOADS;
     uint8_t* ring = lds + wave * C::RING;
     SkinnySlice<C> f[DEPTH];
     int i = 0;

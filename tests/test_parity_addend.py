@@ -27,7 +27,7 @@ KERNELS = {
     "skinny-1x1": {"FG_SKINNY": "1,1"},
     "skinny-2x1": {"FG_SKINNY": "2,1"},
     "skinny-4x1": {"FG_SKINNY": "4,1"},
-    "skinny-2x2-128rows": {"FG_SKINNY": "2,2,8"},
+    "skinny-1x2-128rows": {"FG_SKINNY": "1,2,8"},
     "small": {"FG_FORCE_CONFIG": "small"},
     "big-256": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "256"},
     "big-224": {"FG_FORCE_CONFIG": "big", "FG_FORCE_BN": "224"},

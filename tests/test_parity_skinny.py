@@ -24,8 +24,8 @@ pytestmark = pytest.mark.gpu
 
 # (column fragments, K splits[, activation fragments]): 64-row fragments by
 # default, rows beyond 64 in a second row part; the third field 8 selects
-# 128-row fragments in one part (M > 64 only, at most 2 column fragments)
-PLANS = ["1,1", "2,1", "4,1", "1,2", "2,4", "1,8", "2,3", "2,2,8", "1,3,8"]
+# 128-row fragments in one part (M > 64 only, one column fragment)
+PLANS = ["1,1", "2,1", "4,1", "1,2", "2,4", "1,8", "2,3", "4,3", "1,2,8", "1,3,8"]
 
 
 @pytest.fixture(params=PLANS)
@@ -38,7 +38,7 @@ def plan(request, monkeypatch):
 def _usable(plan: str, M: int, K: int) -> bool:
     cf, sp, *rest = map(int, plan.split(","))
     mf = rest[0] if rest else 4
-    if mf == 8 and (M <= 64 or cf > 2):
+    if mf == 8 and (M <= 64 or cf > 1):
         return False
     return -(-K // 128) >= sp
 
