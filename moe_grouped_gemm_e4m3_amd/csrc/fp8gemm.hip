@@ -241,24 +241,25 @@ int raster_band(int K) {
 
 // K % 128 != 0 runs a build of the kernel whose last slice clips its loads
 // at column K; whole-slice problems keep the build without that code.
-template <class C, int L, bool KTAIL, bool TA = false, bool TB = false>
+template <class C, int L, bool KTAIL, bool TA = false, bool TB = false, bool UE8 = false>
 fg_status launch_big_k(fg::GemmParams& p, hipStream_t stream, const char* what) {
   static int occ_cache = 0;
-  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L, KTAIL, TA, TB>, C::THREADS, &occ_cache);
+  const int occ = occupancy_of(fg::gemm_fp8_big_kernel<C, L, KTAIL, TA, TB, UE8>, C::THREADS, &occ_cache);
   p.group_m = raster_band(p.K);
   int64_t grid = 0;
   FG_TRY_ST(launch_grid(occ, p.num_tiles, &grid));
   print_config(what, p, C::BM, C::BN, C::THREADS, grid, occ);
-  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L, KTAIL, TA, TB>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fg::gemm_fp8_big_kernel<C, L, KTAIL, TA, TB, UE8>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                     stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   return FG_OK;
 }
 
-template <class C, int L>
+template <class C, int L, bool UE8 = false>
 fg_status launch_big(fg::GemmParams& p, hipStream_t stream, const char* what) {
-  return (p.K & 127) ? launch_big_k<C, L, true>(p, stream, what) : launch_big_k<C, L, false>(p, stream, what);
+  return (p.K & 127) ? launch_big_k<C, L, true, false, false, UE8>(p, stream, what)
+                     : launch_big_k<C, L, false, false, false, UE8>(p, stream, what);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,14 +342,14 @@ int pick_bn(int64_t row_tiles, int N, bool allow_256 = true) {
 
 // Large-kernel launch for `groups` independent [rows, N] outputs (1 for the
 // dense and contiguous forms, G for the masked one) with tile width BN.
-template <class C, int L>
+template <class C, int L, bool UE8 = false>
 fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream, const char* what) {
   p.tiles_m = (p.rows + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
   const int64_t slots = groups * p.tiles_m * p.tiles_n;
   if (slots >= ((int64_t)1 << 30)) return fail(FG_EUNSUPPORTED, "too many tiles");
   p.num_tiles = (int)slots;
-  return launch_big<C, L>(p, stream, what);
+  return launch_big<C, L, UE8>(p, stream, what);
 }
 
 // Dense GEMM with power-of-two factors: the large kernel's tiles (widths as
@@ -362,7 +363,7 @@ fg_status launch_big_tiled(fg::GemmParams& p, int64_t groups, hipStream_t stream
 // only (rows256_only), so that a group's weights stream once (measured on the
 // 16 x 256 decode shapes: the 128-row tile was 6-35 % slower than the best
 // 256-row one).  FG_UE8M0_TILE=256x224|256x160|128x256 forces a shape (tuning
-// and tests).
+// and tests; 256x256 is the promotion kernel's tile, below).
 int pick_ue8m0_tile(int M, int N, int64_t groups, bool rows256_only) {
   const char* ft = getenv("FG_UE8M0_TILE");
   if (ft && strcmp(ft, "128x256") == 0) return fg::kUe8m0Tile128x256;
@@ -391,6 +392,23 @@ int pick_ue8m0_tile(int M, int N, int64_t groups, bool rows256_only) {
 }
 
 // layout: fg::kDense, kContiguous or kMasked.
+// The 256x256 tile with power-of-two factors runs on the fp32-factor large
+// kernel, each UE8M0 byte decoded to its fp32 power of two (the scaled-MFMA
+// kernel has no 256-wide tile: its accumulators and fragments do not fit the
+// registers of two waves per SIMD).  The two give the same bits when both
+// run: a per-slice partial scaled by a power of two and added to the fp32
+// accumulator rounds once either way.  The masked GEMM takes it where the
+// plan's width is 256 (one weight stream per tile of 256 columns; measured at
+// 16 x 256 rows, N = 4096, K = 7168: 130 against 161 us); the MFMA-bound forms
+// keep the scaled MFMA, which needs no promotion (the promotion kernel was
+// level at N = 4096 and slower elsewhere).  FG_UE8M0_TILE=256x256 forces it,
+// another FG_UE8M0_TILE value forces the scaled-MFMA kernel.
+bool ue8m0_on_promotion_kernel(bool by_default) {
+  const char* ft = getenv("FG_UE8M0_TILE");
+  if (ft && *ft) return strcmp(ft, "256x256") == 0;
+  return by_default;
+}
+
 fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, int layout, hipStream_t stream,
                        const char* what) {
   static int occ_cache[2][4][3] = {};
@@ -412,13 +430,13 @@ fg_status launch_ue8m0(fg::GemmParams& p, int tile, int64_t groups, int layout, 
   return FG_OK;
 }
 
-template <int L>
+template <int L, bool UE8 = false>
 fg_status launch_big_width(fg::GemmParams& p, int64_t groups, hipStream_t stream, const char* what) {
   const int64_t row_tiles = groups * ((p.rows + CfgBig::BM - 1) / CfgBig::BM);
   switch (pick_bn(row_tiles, p.N)) {
-    case 224: return launch_big_tiled<CfgBig224, L>(p, groups, stream, what);
-    case 160: return launch_big_tiled<CfgBig160, L>(p, groups, stream, what);
-    default: return launch_big_tiled<CfgBig, L>(p, groups, stream, what);
+    case 224: return launch_big_tiled<CfgBig224, L, UE8>(p, groups, stream, what);
+    case 160: return launch_big_tiled<CfgBig160, L, UE8>(p, groups, stream, what);
+    default: return launch_big_tiled<CfgBig, L, UE8>(p, groups, stream, what);
   }
 }
 
@@ -1131,6 +1149,8 @@ fg_status gemm_fp8_nt_ue8m0(const uint8_t* A, int64_t lda, const int32_t* sa, in
   FG_TRY(check_ld(ldb, K, 16, "ldb"));
   FG_TRY(check_ld(ld_sa, M, 1, "ld_sa"));
   FG_TRY(check_row_bytes(lda, ldb));
+  if (ue8m0_on_promotion_kernel(false))
+    return launch_big_tiled<CfgBig, fg::kDense, true>(p, 1, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
   return launch_ue8m0(p, pick_ue8m0_tile(M, N, 1, false), 1, fg::kDense, (hipStream_t)stream, "gemm_fp8_nt_ue8m0");
 }
 
@@ -1171,6 +1191,9 @@ fg_status gemm_fp8_grouped_contiguous_ue8m0(const uint8_t* A, const int32_t* sa,
   // per-tile reuse outweighs the rounding of the last round (measured at
   // 8 x 4096 rows, N=4096, K=7168: 256x224 849-968 us, 256x160 935-974,
   // 128x256 1116-1127).  FG_UE8M0_TILE still forces a shape.
+  if (ue8m0_on_promotion_kernel(false))
+    return launch_big_tiled<CfgBig, fg::kContiguous, true>(p, 1, (hipStream_t)stream,
+                                                            "gemm_fp8_grouped_contiguous_ue8m0");
   const int tile = getenv("FG_UE8M0_TILE") ? pick_ue8m0_tile(M_total, N, 1, false) : fg::kUe8m0Tile256x224;
   return launch_ue8m0(p, tile, 1, fg::kContiguous, (hipStream_t)stream, "gemm_fp8_grouped_contiguous_ue8m0");
 }
@@ -1209,6 +1232,8 @@ fg_status gemm_fp8_grouped_masked_ue8m0(const uint8_t* A, const int32_t* sa, int
   FG_TRY(check_ld(ld_sa, M_cap, 1, "ld_sa"));
   FG_TRY(check_row_bytes(K, K));
   p.kb_factor = (p.Kb + 3) / 4;  // packed words per row of one group's factor arrays
+  if (ue8m0_on_promotion_kernel(pick_bn((int64_t)G * ((M_cap + 255) / 256), N) == 256))
+    return launch_big_tiled<CfgBig, fg::kMasked, true>(p, G, (hipStream_t)stream, "gemm_fp8_grouped_masked_ue8m0");
   return launch_ue8m0(p, pick_ue8m0_tile(M_cap, N, G, true), G, fg::kMasked, (hipStream_t)stream,
                       "gemm_fp8_grouped_masked_ue8m0");
 }

@@ -745,27 +745,43 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
 // wave's columns touch, for one K slice.  They are wave-uniform and never
 // written while a GEMM runs, so they are read through the scalar cache; the
 // activation scales of the slice arrive in LDS with its operands.
-template <class C>
+// UE8M0 byte -> the fp32 power of two 2^(e - 127) (e = 0 is the subnormal
+// 2^-127, e = 255 overflows to infinity).
+__device__ __forceinline__ float ue8m0_value(int e) {
+  return __builtin_bit_cast(float, e == 0 ? 0x00400000 : e << 23);
+}
+
+// UE8: the factors are UE8M0 bytes packed four K groups to an int32 (sb rows
+// of ceil(Kb / 4) words), decoded to fp32 here.
+template <class C, bool UE8 = false>
 __device__ __forceinline__ void load_sb(const GemmParams& p, const Work& t, int kb, int wn, float (&sb_r)[2]) {
   const int nw = t.n0 + wn * C::WN;
   const int nb0 = min(nw >> 7, p.Nb - 1);
-  const __attribute__((address_space(4))) float* sbk = (const __attribute__((address_space(4))) float*)(t.sb + kb);
-  sb_r[0] = sbk[(int64_t)nb0 * p.ld_sb];
-  if (!C::SCALE_PER_WAVE) {
-    const int nb1 = min(nb0 + 1, p.Nb - 1);
-    sb_r[1] = sbk[(int64_t)nb1 * p.ld_sb];
+  const int nb1 = C::SCALE_PER_WAVE ? nb0 : min(nb0 + 1, p.Nb - 1);
+  if (UE8) {
+    const int64_t kb4 = (p.Kb + 3) >> 2;
+    const __attribute__((address_space(4))) int* sbk =
+        (const __attribute__((address_space(4))) int*)((const int*)(const void*)t.sb + (kb >> 2));
+    const int sh = 8 * (kb & 3);
+    sb_r[0] = ue8m0_value((sbk[(int64_t)nb0 * kb4] >> sh) & 0xff);
+    sb_r[1] = C::SCALE_PER_WAVE ? sb_r[0] : ue8m0_value((sbk[(int64_t)nb1 * kb4] >> sh) & 0xff);
   } else {
-    sb_r[1] = sb_r[0];
+    const __attribute__((address_space(4))) float* sbk = (const __attribute__((address_space(4))) float*)(t.sb + kb);
+    sb_r[0] = sbk[(int64_t)nb0 * p.ld_sb];
+    sb_r[1] = C::SCALE_PER_WAVE ? sb_r[0] : sbk[(int64_t)nb1 * p.ld_sb];
   }
 }
 
-// s = sa * sb for this lane's SM rows, sa read from the stage's scale area.
-template <class C>
+// s = sa * sb for this lane's SM rows, sa read from the stage's scale area
+// (UE8: the packed word of the slice's four K groups; byte kb % 4 is the
+// slice's).
+template <class C, bool UE8 = false>
 __device__ __forceinline__ void slice_scales(const uint8_t* sa_area, int wm, int l16, const float (&sb)[2],
-                                             float (&s)[C::SM][2]) {
+                                             float (&s)[C::SM][2], int kb = 0) {
 #pragma unroll
   for (int ms = 0; ms < C::SM; ++ms) {
-    const float a = *(const float*)(sa_area + (wm * C::WM + ms * 16 + l16) * 4);
+    const int w = *(const int*)(sa_area + (wm * C::WM + ms * 16 + l16) * 4);
+    const float a = UE8 ? ue8m0_value((w >> (8 * (kb & 3))) & 0xff) : __builtin_bit_cast(float, w);
     s[ms][0] = a * sb[0];
     s[ms][1] = a * sb[1];
   }
@@ -1076,7 +1092,7 @@ __device__ __forceinline__ void store_direct(const GemmParams& p, const Work& t,
 
 // The large-tile kernel's body.  TA / TB: A / B stored MN-major (K rows of
 // M / N bytes); kg: the K-grouped GEMM's groups (kKGrouped only).
-template <class C, int L, bool KTAIL, bool TA, bool TB>
+template <class C, int L, bool KTAIL, bool TA, bool TB, bool UE8 = false>
 __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGroups* kg) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   constexpr int SM = C::SM, SN = C::SN;
@@ -1121,8 +1137,8 @@ __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGrou
   if (cur.w < 0) return;
 
   float sb_c[2];
-  load_sb<C>(p, cur, 0, wn, sb_c);
-  issue_slice_loads<C, KTAIL, TA, TB>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane);
+  load_sb<C, UE8>(p, cur, 0, wn, sb_c);
+  issue_slice_loads<C, KTAIL, TA, TB>(p, cur, 0, FG_STAGE(0), FG_SA(0), wave, lane, UE8 ? 0 : -1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -1149,13 +1165,15 @@ __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGrou
       // prefetch the following slice: this tile's next one, or the first of the next work item
       const bool last = kb + 1 == Kb;
       if (!last)
-        issue_slice_loads<C, KTAIL, TA, TB>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
+        issue_slice_loads<C, KTAIL, TA, TB>(p, cur, kb + 1, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane,
+                                            UE8 ? (kb + 1) >> 2 : -1);
       else if (nxt.w >= 0)
-        issue_slice_loads<C, KTAIL, TA, TB>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane);
+        issue_slice_loads<C, KTAIL, TA, TB>(p, nxt, 0, FG_STAGE(stage ^ 1), FG_SA(stage ^ 1), wave, lane,
+                                            UE8 ? 0 : -1);
 
       if (active) {
         float s[SM][2];
-        slice_scales<C>(FG_SA(stage), wm, l16, sb_c, s);
+        slice_scales<C, UE8>(FG_SA(stage), wm, l16, sb_c, s, kb);
         slice_mma<C, TA, TB>(FG_STAGE(stage), a_off, b_off, s, tb, acc, a_s0, b_s0);
       }
 
@@ -1165,9 +1183,9 @@ __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGrou
       // MFMAs could not start before all of the slice's fragment reads land.
       float sb_n[2] = {0.f, 0.f};
       if (!last)
-        load_sb<C>(p, cur, kb + 1, wn, sb_n);
+        load_sb<C, UE8>(p, cur, kb + 1, wn, sb_n);
       else if (nxt.w >= 0)
-        load_sb<C>(p, nxt, 0, wn, sb_n);
+        load_sb<C, UE8>(p, nxt, 0, wn, sb_n);
 
       // This wave's operand loads have landed in LDS; the barrier publishes
       // them to the other waves (and frees the stage just read).
@@ -1199,9 +1217,9 @@ __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGrou
 #undef FG_SA
 }
 
-template <class C, int L, bool KTAIL, bool TA = false, bool TB = false>
+template <class C, int L, bool KTAIL, bool TA = false, bool TB = false, bool UE8 = false>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_fp8_big_kernel(GemmParams p) {
-  big_kernel_body<C, L, KTAIL, TA, TB>(p, nullptr);
+  big_kernel_body<C, L, KTAIL, TA, TB, UE8>(p, nullptr);
 }
 
 // K-grouped GEMM, D[g] = C[g] + A_g^T B_g: one persistent launch over the

@@ -237,7 +237,7 @@ from tests.test_parity_ue8m0 import (  # noqa: E402
     run as run_ue8m0, run_contig as run_contig_ue8m0, run_masked as run_masked_ue8m0, to_bytes,
 )
 
-UE8M0_TILES = ["256x224", "256x160", "128x256"]
+UE8M0_TILES = ["256x224", "256x160", "128x256", "256x256"]
 
 
 @pytest.mark.parametrize("M,K", [(5, 48), (129, 176), (300, 7184), (512, 8208)])

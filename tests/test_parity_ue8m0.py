@@ -1,5 +1,6 @@
 """Power-of-two (UE8M0) factors on the GPU against the CPU oracle: the two
-casts, and the dense and masked grouped GEMMs on the scaled MFMA.
+casts, and the dense, contiguous and masked GEMMs, on the scaled MFMA and
+(256x256 tiles) on the fp32-factor kernel with the factor bytes decoded.
 
 The casts must match the oracle byte for byte (codes and factor bytes).  The
 GEMM is compared bit for bit in the exact regime -- its factors {1/2, 1, 2}
@@ -76,10 +77,11 @@ def test_cast_per_block_bytes(gpu_lib, N, K):
     assert np.array_equal(quant.unpack_ue8m0(sb.cpu().numpy(), K // 128, axis=1), e_ref)
 
 
-@pytest.fixture(params=["256x224", "256x160", "128x256"])
+@pytest.fixture(params=["256x224", "256x160", "128x256", "256x256"])
 def width(request, monkeypatch):
-    """The kernel's tile shapes, forced with FG_UE8M0_TILE; the value is the
-    tile width (used to vary the seeds)."""
+    """The tile shapes, forced with FG_UE8M0_TILE (256x256 runs on the
+    fp32-factor kernel with each factor byte decoded, the others on the
+    scaled MFMA); the value is the tile width (used to vary the seeds)."""
     monkeypatch.delenv("FG_FORCE_BN", raising=False)
     monkeypatch.setenv("FG_UE8M0_TILE", request.param)
     return int(request.param.split("x")[1])
@@ -132,7 +134,8 @@ def test_gemm_factor_equivariance(gpu_lib, width):
 
 
 def test_gemm_width_256_request_falls_back(gpu_lib, monkeypatch):
-    """This mode has no 256-wide tile; asking for one gives the 224-wide result."""
+    """The scaled-MFMA kernel has no 256-wide tile; asking it for one with
+    FG_FORCE_BN gives the 224-wide result."""
     M, N, K = 300, 700, 384
     rng = np.random.default_rng(7)
     qa, sa, qb, sb = exact_regime(rng, M, N, K)
@@ -259,6 +262,33 @@ def test_masked_full_equals_dense(gpu_lib, width):
     Dm = bf16_bits(run_masked(gpu_lib, qa, ea, qb, eb, [Mc] * G))
     for e in range(G):
         assert np.array_equal(Dm[e], bf16_bits(run(gpu_lib, qa[e], ea[e], qb[e], eb[e]))), e
+
+
+def test_promotion_and_scaled_mfma_kernels_agree(gpu_lib, monkeypatch):
+    """A slice's partial scaled by a power of two and added to the fp32
+    accumulator rounds once, whether the matrix core applies the factors or
+    a promotion FMA does: the two kernels give the same bits on the dense,
+    contiguous and masked forms (random operands, so every slice rounds)."""
+    M, N, K = 300, 520, 1024
+    A32, B32 = synth.dense_problem(M, N, K, seed=77)
+    qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
+    qb, eb = quant.quantize_per_block_ue8m0(B32.numpy())
+    G, Mc = 3, 200
+    g = torch.Generator().manual_seed(78)
+    A3 = torch.randn(G, Mc, K, generator=g).numpy()
+    B3 = torch.randn(G, N, K, generator=g).numpy()
+    qs = [quant.quantize_per_token_ue8m0(a) for a in A3]
+    ws = [quant.quantize_per_block_ue8m0(b) for b in B3]
+    qa3, ea3 = np.stack([q for q, _ in qs]), np.stack([e for _, e in qs])
+    qb3, eb3 = np.stack([q for q, _ in ws]), np.stack([e for _, e in ws])
+    mask = [200, 77, 0]
+    out = {}
+    for tile in ("256x224", "256x256"):
+        monkeypatch.setenv("FG_UE8M0_TILE", tile)
+        announce(f"ue8m0 kernels agree {tile}")
+        out[tile] = (bf16_bits(run(gpu_lib, qa, ea, qb, eb)), bf16_bits(run_masked(gpu_lib, qa3, ea3, qb3, eb3, mask)))
+    assert np.array_equal(out["256x224"][0], out["256x256"][0])
+    assert np.array_equal(out["256x224"][1], out["256x256"][1])
 
 
 @pytest.mark.parametrize("shape", synth.MASKED_16x256.shapes, ids=lambda s: "x".join(map(str, s)))
