@@ -118,3 +118,33 @@ def test_masked_random(gpu_lib, width):
     X, valid, S = ogemm.gemm_grouped_masked(qa, sa, qb, sb, mask, with_magnitude=True)
     assert_close(bf16_to_f64(D)[valid], X[valid], S[valid], K // 128, f"width {width} masked")
     assert (bf16_bits(D)[~valid] == SENTINEL_BF16).all()
+
+
+@pytest.mark.parametrize("with_c", [False, True])
+def test_unaligned_output_rows(gpu_lib, width, with_c):
+    """An output whose rows start 2 bytes past a 16-byte boundary and are an odd
+    number of elements apart, N not a multiple of 8: the epilogue's element-wise
+    stores (the vector ones need 16- or 8-byte alignment).  Exact regime, bit for
+    bit, with and without the fp32 addend; the padding around D is untouched."""
+    M, N, K = 300, 517, 384
+    announce(f"width {width}: unaligned output rows {M}x{N}x{K} C={with_c}")
+    rng = np.random.default_rng(width + 3 * with_c)
+    qa, sa, qb, sb = exact_regime(rng, M, N, K)
+    ldd = N + 3
+    buf = sentinel_like((M + 2, ldd))
+    flat = buf.view(-1)[1:1 + M * ldd]
+    D = flat.view(M, ldd)[:, :N]
+    X = ogemm.gemm_nt(qa, sa, qb, sb)
+    if with_c:
+        C = (rng.integers(-1024, 1025, (M, N)) / 4.0).astype(np.float32)
+        gpu_lib.gemm_fp8_nt_c(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), dev_f32(C), D)
+        X = X + C
+    else:
+        gpu_lib.gemm_fp8_nt(dev_u8(qa), dev_sa(sa), dev_u8(qb), dev_f32(sb), D)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(X))
+    bits = bf16_bits(buf).reshape(-1)
+    inside = np.zeros(bits.size, bool)
+    for m in range(M):
+        inside[1 + m * ldd: 1 + m * ldd + N] = True
+    assert (bits[~inside] == SENTINEL_BF16).all()
