@@ -747,7 +747,7 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
 // activation scales of the slice arrive in LDS with its operands.
 // UE8M0 byte -> the fp32 power of two 2^(e - 127) (e = 0 is the subnormal
 // 2^-127, e = 255 overflows to infinity).
-__device__ __forceinline__ float ue8m0_value(int e) {
+__device__ __forceinline__ float ue8m0_factor(int e) {
   return __builtin_bit_cast(float, e == 0 ? 0x00400000 : e << 23);
 }
 
@@ -763,8 +763,8 @@ __device__ __forceinline__ void load_sb(const GemmParams& p, const Work& t, int 
     const __attribute__((address_space(4))) int* sbk =
         (const __attribute__((address_space(4))) int*)((const int*)(const void*)t.sb + (kb >> 2));
     const int sh = 8 * (kb & 3);
-    sb_r[0] = ue8m0_value((sbk[(int64_t)nb0 * kb4] >> sh) & 0xff);
-    sb_r[1] = C::SCALE_PER_WAVE ? sb_r[0] : ue8m0_value((sbk[(int64_t)nb1 * kb4] >> sh) & 0xff);
+    sb_r[0] = ue8m0_factor((sbk[(int64_t)nb0 * kb4] >> sh) & 0xff);
+    sb_r[1] = C::SCALE_PER_WAVE ? sb_r[0] : ue8m0_factor((sbk[(int64_t)nb1 * kb4] >> sh) & 0xff);
   } else {
     const __attribute__((address_space(4))) float* sbk = (const __attribute__((address_space(4))) float*)(t.sb + kb);
     sb_r[0] = sbk[(int64_t)nb0 * p.ld_sb];
@@ -781,7 +781,7 @@ __device__ __forceinline__ void slice_scales(const uint8_t* sa_area, int wm, int
 #pragma unroll
   for (int ms = 0; ms < C::SM; ++ms) {
     const int w = *(const int*)(sa_area + (wm * C::WM + ms * 16 + l16) * 4);
-    const float a = UE8 ? ue8m0_value((w >> (8 * (kb & 3))) & 0xff) : __builtin_bit_cast(float, w);
+    const float a = UE8 ? ue8m0_factor((w >> (8 * (kb & 3))) & 0xff) : __builtin_bit_cast(float, w);
     s[ms][0] = a * sb[0];
     s[ms][1] = a * sb[1];
   }
