@@ -165,3 +165,21 @@ def test_workspace_rules(gpu_lib, monkeypatch):
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(Dw), fresh)
     assert (ws[:64 * 1024] == 0).all()  # counters left at zero
+
+
+# Row counts around the 16-row fragment and 64-row part boundaries, widths
+# around the 32- and 64-column tiles and one weight-scale block, K with a
+# partial last slice: the planner's own choice of tile width and K split.
+SWEEP = [(m, n, k) for m in (1, 15, 17, 63, 65, 127) for n, k in ((31, 144), (65, 1040), (130, 2320), (2112, 4112))]
+
+
+@pytest.mark.parametrize("M,N,K", SWEEP, ids=lambda v: str(v))
+def test_default_plan_sweep_bitwise(gpu_lib, monkeypatch, M, N, K):
+    monkeypatch.delenv("FG_FORCE_CONFIG", raising=False)
+    monkeypatch.delenv("FG_SKINNY", raising=False)
+    announce(f"skinny default plan {M}x{N}x{K}")
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    qa, sa, qb, sb = exact_regime(rng, M, N, K)
+    D = run_dense(gpu_lib, qa, sa, qb, sb)
+    X = ogemm.gemm_nt(qa, sa, qb, sb)
+    assert np.array_equal(bf16_bits(D), ogemm.to_bf16(X))
