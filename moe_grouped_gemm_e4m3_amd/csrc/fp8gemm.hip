@@ -395,9 +395,11 @@ int pick_ue8m0_tile(int M, int N, int64_t groups, bool rows256_only) {
 // The 256x256 tile with power-of-two factors runs on the fp32-factor large
 // kernel, each UE8M0 byte decoded to its fp32 power of two (the scaled-MFMA
 // kernel has no 256-wide tile: its accumulators and fragments do not fit the
-// registers of two waves per SIMD).  The two give the same bits when both
-// run: a per-slice partial scaled by a power of two and added to the fp32
-// accumulator rounds once either way.  The masked GEMM takes it where the
+// registers of two waves per SIMD).  The two agree bit for bit except where
+// a slice's dot product is not an fp32 number (more than 24 significant
+// bits): the scaled MFMA adds it to the accumulator unrounded, the promotion
+// FMA adds its fp32 rounding (1 element of 134 M, by 1 BF16 ulp, on the
+// contiguous MoE workload).  The masked GEMM takes it where the
 // plan's width is 256 (one weight stream per tile of 256 columns; measured at
 // 16 x 256 rows, N = 4096, K = 7168: 130 against 161 us); the MFMA-bound forms
 // keep the scaled MFMA, which needs no promotion (the promotion kernel was

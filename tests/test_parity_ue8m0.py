@@ -265,10 +265,12 @@ def test_masked_full_equals_dense(gpu_lib, width):
 
 
 def test_promotion_and_scaled_mfma_kernels_agree(gpu_lib, monkeypatch):
-    """A slice's partial scaled by a power of two and added to the fp32
-    accumulator rounds once, whether the matrix core applies the factors or
-    a promotion FMA does: the two kernels give the same bits on the dense,
-    contiguous and masked forms (random operands, so every slice rounds)."""
+    """The scaled MFMA adds a slice's exact dot product, times its power-of-two
+    factor, into the fp32 accumulator with one rounding; the promotion kernel
+    rounds the dot product to fp32 first.  The two differ only where that
+    dot product has more than 24 significant bits, which random e4m3 rows of
+    128 rarely give: on these dense and masked operands the bits are equal
+    (a regression to a wrong factor byte or block would change most of them)."""
     M, N, K = 300, 520, 1024
     A32, B32 = synth.dense_problem(M, N, K, seed=77)
     qa, ea = quant.quantize_per_token_ue8m0(A32.numpy())
