@@ -1020,11 +1020,6 @@ __device__ __forceinline__ void store_direct(const GemmParams& p, const Work& t,
   const bool odd = (kq & 1) != 0;
   const bool vec16 = (p.ldd & 7) == 0 && ((uintptr_t)p.D & 15) == 0;
   const bool vec8 = (p.ldd & 3) == 0 && ((uintptr_t)p.D & 7) == 0;
-  // fp32 addend: C of the dense call, or the K-grouped tile's group slice
-  constexpr bool ADDEND = L == kDenseC || L == kKGrouped;
-  const float* cbase = L == kDenseC ? p.Cin : t.C;
-  const int64_t ldc = L == kDenseC ? p.ldc : (int64_t)p.N;
-  const bool add_c = ADDEND && cbase != nullptr;
   const int nw = t.n0 + wn * C::WN;  // the wave's first column
 #pragma unroll
   for (int ms = 0; ms < C::SM; ++ms) {
@@ -1042,18 +1037,6 @@ __device__ __forceinline__ void store_direct(const GemmParams& p, const Work& t,
     for (int tt = 0; tt < SN; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[tt][r] = acc[ms][tt][r];
-    if (ADDEND && add_c) {
-      f32x4 cv[SN];
-#pragma unroll
-      for (int tt = 0; tt < SN; ++tt) {
-        const int n = nw + tt * 16 + 4 * kq;
-        cv[tt] = load_addend4(cbase, ldc, p.N, m, n, ok && n < p.N);
-      }
-#pragma unroll
-      for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[tt][r] += cv[tt][r];
-    }
     uint16_t* drow = t.D + (int64_t)m * p.ldd;
 #pragma unroll
     for (int tp = 0; tp + 1 < SN; tp += 2) {
@@ -1088,6 +1071,43 @@ __device__ __forceinline__ void store_direct(const GemmParams& p, const Work& t,
       }
     }
   }
+}
+
+// Accumulators at the start of a tile: zeros, or for D = C + A B^T the
+// tile's fp32 addend (C of the dense call, or the K-grouped tile's group
+// slice; t.w < 0, no tile, gives zeros), so that the epilogue adds nothing.
+// The loads go out right after
+// the previous tile's stores and nothing waits for them until the first
+// promotion of the tile's first slice: the addend's read overlaps the stores
+// and the first slice's loads and MFMAs instead of stalling the epilogue.
+template <class C, int L>
+__device__ __forceinline__ void init_acc(const GemmParams& p, const Work& t, float (&acc)[C::SM][C::SN][4],
+                                         int wave, int lane) {
+  constexpr bool ADDEND = L == kDenseC || L == kKGrouped;
+  const float* cbase = L == kDenseC ? p.Cin : t.C;
+  if (ADDEND && cbase != nullptr && t.w >= 0) {
+    const int64_t ldc = L == kDenseC ? p.ldc : (int64_t)p.N;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int l16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int ms = 0; ms < C::SM; ++ms) {
+      const int m = t.m0 + wm * C::WM + ms * 16 + l16;
+#pragma unroll
+      for (int tt = 0; tt < C::SN; ++tt) {
+        const int n = t.n0 + wn * C::WN + tt * 16 + 4 * kq;
+        const f32x4 x = load_addend4(cbase, ldc, p.N, m, n, m < t.rows_valid && n < p.N);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ms][tt][r] = x[r];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int ms = 0; ms < C::SM; ++ms)
+#pragma unroll
+    for (int tt = 0; tt < C::SN; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
 }
 
 // The large-tile kernel's body.  TA / TB: A / B stored MN-major (K rows of
@@ -1142,14 +1162,9 @@ __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGrou
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // accumulators live across the segments of a tile; zeroed after each store
+  // accumulators live across the segments of a tile; set up again after each store
   float acc[SM][SN][4];
-#pragma unroll
-  for (int ms = 0; ms < SM; ++ms)
-#pragma unroll
-    for (int tt = 0; tt < SN; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
+  init_acc<C, L>(p, cur, acc, wave, lane);
 
   int stage = 0;
   while (cur.w >= 0) {
@@ -1201,12 +1216,16 @@ __device__ __forceinline__ void big_kernel_body(const GemmParams& p, const KGrou
     // ---- last segment of the tile: store its rows ----
     if (cur.seg == cur.nseg - 1) {
       store_direct<C, L>(p, cur, acc, wave, lane);
+      if constexpr (L == kDenseC || L == kKGrouped || TA || TB) {
+        init_acc<C, L>(p, nxt, acc, wave, lane);
+      } else {
 #pragma unroll
-      for (int ms = 0; ms < SM; ++ms)
+        for (int ms = 0; ms < SM; ++ms)
 #pragma unroll
-        for (int tt = 0; tt < SN; ++tt)
+          for (int tt = 0; tt < SN; ++tt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
+            for (int r = 0; r < 4; ++r) acc[ms][tt][r] = 0.f;
+      }
     }
     cur = nxt;
     it = it_n;
