@@ -169,20 +169,24 @@ fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t 
  * (128x128 blocks of the [N, K] operand).  C: fp32 [M, N] addend (row stride
  * ldc >= N) or NULL for none.  D: as in gemm_fp8_nt.  An operand stored MN-major
  * has no alignment requirement on the copying path.
- * The workspace selects one of two paths:
- *  - workspace_bytes > 0: each MN-major operand is first transposed, K-major,
- *    into the caller's device workspace (a byte copy bound by HBM), then the
- *    NT kernels run on the copy.  workspace must be 16-byte aligned and hold
- *    at least fg_layout_workspace_bytes(layout, M, N, K) bytes (FG_EINVAL
- *    otherwise).  It is in use until the call's work on `stream` has
- *    finished.  The stored [K, .] operands have at most 65535*128 rows
- *    (FG_EUNSUPPORTED).  The faster path.
- *  - workspace_bytes == 0 (workspace ignored): no copy; the large-tile
- *    kernel stages each MN-major operand as stored.  Each such operand must
- *    be 16-byte aligned with a row stride and a column count (M for A, N for
- *    B) that are multiples of 16 (FG_EALIGN otherwise).  Measured 25-45 %
- *    slower than the copies on MI355X; for callers without device memory
- *    to spare.
+ * Two paths serve the MN-major operands:
+ *  - copies: each MN-major operand is first transposed, K-major, into the
+ *    caller's device workspace (a byte copy bound by HBM), then the NT
+ *    kernels run on the copy.  The stored [K, .] operands have at most
+ *    65535*128 rows (FG_EUNSUPPORTED).
+ *  - copy-free: the large-tile kernel stages each MN-major operand as
+ *    stored.  Each such operand must be 16-byte aligned with a row stride
+ *    and a column count (M for A, N for B) that are multiples of 16.
+ * workspace_bytes > 0: workspace must be 16-byte aligned and hold at least
+ *    fg_layout_workspace_bytes(layout, M, N, K) bytes (FG_EINVAL otherwise);
+ *    it is in use until the call's work on `stream` has finished.  The call
+ *    takes the copy-free path where the operands allow it and the large
+ *    kernel's 256 x 256 tiles keep the device's CUs at least three quarters
+ *    busy over their rounds (measured on MI355X at M = 4096: level with or
+ *    2-9 % faster than the copies there, 10-15 % slower than them at
+ *    N = 2112), and the copies otherwise.  Both paths give the same bits.
+ * workspace_bytes == 0 (workspace ignored): the copy-free path; operands it
+ *    cannot take give FG_EALIGN.  For callers without device memory to spare.
  * K <= 2^22 (FG_EUNSUPPORTED).  K % 16 == 0.  Nothing is allocated.
  */
 fg_status gemm_fp8_nn(const uint8_t* A, int64_t lda, const float* sa, int64_t ld_sa,

@@ -708,6 +708,25 @@ bool mn_direct(const void* x, int64_t ld, int ext) {
   return x && aligned(x, 16) && ld % 16 == 0 && ld <= kMaxLd && ext % 16 == 0;
 }
 
+// Given a workspace, whether to stage the MN-major operands as stored anyway
+// (their alignment permitting): where the large kernel's 256x256 tiles keep
+// the CUs at least three quarters busy over their rounds.  Measured on
+// MI355X at M = 4096, N = 4096, 7168 and 24576: level with or 2-9 % faster
+// than copying them first (the copies cost a pass over both operands); at
+// N = 2112 (144 such tiles on 256 CUs, against the NT plan's 224 tiles of
+// 256x160) the copies were 10-15 % faster.  FG_LAYOUT_COPY=1 keeps the
+// copies, =0 skips them wherever the operands allow (tests and tuning).
+bool layout_copy_free(int M, int N) {
+  const char* f = getenv("FG_LAYOUT_COPY");
+  if (f && *f) return strcmp(f, "0") == 0;
+  int cus = 0;
+  if (device_cus(&cus) != FG_OK) return false;
+  if (g_num_cus_cap > 0 && g_num_cus_cap < cus) cus = g_num_cus_cap;
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t rounds = (tiles + cus - 1) / cus;
+  return tiles * 4 >= rounds * cus * 3;
+}
+
 // The large kernel on the operands as stored (TA / TB: MN-major), 256x256 tiles.
 template <bool TA, bool TB>
 fg_status launch_layout_direct(fg::GemmParams& p, hipStream_t stream, const char* what) {
@@ -740,8 +759,21 @@ fg_status gemm_layout(const uint8_t* A, int64_t lda, const float* sa, int64_t ld
   const uint8_t* a = A;
   const uint8_t* b = B;
   // Without a workspace the large kernel stages the MN-major operands as
-  // stored and the transposing LDS reads turn them into MFMA fragments.
-  if (K > 0 && (TA || TB) && workspace_bytes == 0) {
+  // stored and the transposing LDS reads turn them into MFMA fragments; with
+  // one it does so where the plan prefers it (the workspace, checked as for
+  // the copies so that what a call accepts does not depend on the plan, is
+  // then left untouched).
+  bool direct = K > 0 && (TA || TB) && workspace_bytes == 0;
+  if (K > 0 && (TA || TB) && workspace_bytes > 0 && K <= kMaxLd && (!TA || mn_direct(A, lda, M)) &&
+      (!TB || mn_direct(B, ldb, N)) && layout_copy_free(M, N)) {
+    const int64_t need = layout_ws_bytes(TA, TB, M, N, K);
+    if (workspace_bytes < need)
+      return fail(FG_EINVAL, "%s: workspace of %lld bytes is below the %lld this call needs", what,
+                  (long long)workspace_bytes, (long long)need);
+    FG_TRY(check_ptr(workspace, 16, "workspace"));
+    direct = true;
+  }
+  if (direct) {
     if ((TA && !mn_direct(A, lda, M)) || (TB && !mn_direct(B, ldb, N)))
       return fail(FG_EALIGN,
                   "%s without a workspace: an MN-major operand needs 16-byte aligned rows, a row stride and a column "

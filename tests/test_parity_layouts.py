@@ -27,8 +27,9 @@ from tests.helpers import (
 pytestmark = pytest.mark.gpu
 
 LAYOUTS = ["nn", "tn", "tt"]
-ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN")
-# "copy": a workspace from torch's allocator (transposed copies);
+ENV_KEYS = ("FG_SKINNY", "FG_FORCE_CONFIG", "FG_FORCE_BN", "FG_LAYOUT_COPY")
+# "copy": a workspace from torch's allocator, copies forced (FG_LAYOUT_COPY=1;
+# by default the plan may skip them where the large tiles fill the device);
 # "direct": an empty workspace (operands staged as stored)
 PATHS = ["copy", "direct"]
 
@@ -40,7 +41,9 @@ def default_plan(monkeypatch):
 
 
 @pytest.fixture(params=PATHS)
-def path(request):
+def path(request, monkeypatch):
+    if request.param == "copy":
+        monkeypatch.setenv("FG_LAYOUT_COPY", "1")
     return request.param
 
 
@@ -185,6 +188,25 @@ def test_direct_same_bits_as_transposed(gpu_lib, monkeypatch, layout):
     assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
     X, S = ogemm.gemm_layout(layout, As, sa, Bs, sb, C=C, with_magnitude=True)
     assert_close(bf16_to_f64(D1), X, S, K // 128 + 1, f"layout {layout} direct")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_planned_path_with_workspace(gpu_lib, monkeypatch, layout):
+    """With a workspace and the default plan, at a size where the plan skips
+    the copies (16 x 28 tiles of 256 x 256 on the device) and at one where it
+    keeps them (16 x 9 tiles): the same bits as the forced copies, and the
+    exact-regime value."""
+    for (M, N, K) in [(4096, 7168, 256), (4096, 2112, 256)]:
+        announce(f"layout {layout} planned path {M}x{N}x{K}")
+        rng = np.random.default_rng(M + N)
+        A, sa, B, sb = exact_regime(rng, M, N, K)
+        As, Bs = stored(layout, A, B)
+        monkeypatch.setenv("FG_LAYOUT_COPY", "1")
+        D0 = call(gpu_lib, layout, As, sa, Bs, sb)
+        monkeypatch.delenv("FG_LAYOUT_COPY")
+        D1 = call(gpu_lib, layout, As, sa, Bs, sb)
+        assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
+        assert np.array_equal(bf16_bits(D1), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb)))
 
 
 def test_direct_path_needs_no_workspace(gpu_lib):
