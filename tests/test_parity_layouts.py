@@ -193,18 +193,21 @@ def test_direct_same_bits_as_transposed(gpu_lib, monkeypatch, layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_planned_path_with_workspace(gpu_lib, monkeypatch, layout):
     """With a workspace and the default plan, at a size where the plan skips
-    the copies (16 x 28 tiles of 256 x 256 on the device) and at one where it
-    keeps them (16 x 9 tiles): the same bits as the forced copies, and the
-    exact-regime value."""
-    for (M, N, K) in [(4096, 7168, 256), (4096, 2112, 256)]:
-        announce(f"layout {layout} planned path {M}x{N}x{K}")
-        rng = np.random.default_rng(M + N)
+    the copies (16 x 28 tiles of 256 x 256 on the device), at one where it
+    keeps them (16 x 9 tiles), and at the first size with row strides the
+    copy-free path cannot take (8 bytes of padding: the copies again): the
+    same bits as the forced copies, and the exact-regime value."""
+    for (M, N, K, pad) in [(4096, 7168, 256, 0), (4096, 2112, 256, 0), (4096, 7168, 256, 8)]:
+        announce(f"layout {layout} planned path {M}x{N}x{K} pad {pad}")
+        rng = np.random.default_rng(M + N + pad)
         A, sa, B, sb = exact_regime(rng, M, N, K)
         As, Bs = stored(layout, A, B)
+        # only the MN-major operands take the odd stride (a K-major one keeps the NT rule)
+        pads = (pad if layout[0] == "t" else 0, pad if layout[1] == "n" else 0)
         monkeypatch.setenv("FG_LAYOUT_COPY", "1")
-        D0 = call(gpu_lib, layout, As, sa, Bs, sb)
+        D0 = call(gpu_lib, layout, As, sa, Bs, sb, pad=pads)
         monkeypatch.delenv("FG_LAYOUT_COPY")
-        D1 = call(gpu_lib, layout, As, sa, Bs, sb)
+        D1 = call(gpu_lib, layout, As, sa, Bs, sb, pad=pads)
         assert np.array_equal(bf16_bits(D1), bf16_bits(D0))
         assert np.array_equal(bf16_bits(D1), ogemm.to_bf16(ogemm.gemm_layout(layout, As, sa, Bs, sb)))
 
