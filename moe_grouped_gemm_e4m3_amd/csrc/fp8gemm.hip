@@ -185,6 +185,8 @@ using CfgDefault = fg::TileCfg<128, 128, 64, 64>;
 using CfgBig = fg::BigCfg<256, 256, 4, 2>;
 using CfgBig224 = fg::BigCfg<256, 224, 4, 2>;
 using CfgBig160 = fg::BigCfg<256, 160, 4, 2>;
+// 160-wide tiles with a B staged MN-major (its K rows are 256 bytes)
+using CfgBig160Mn = fg::BigCfg<256, 160, 4, 2, 256>;
 
 template <class K>
 int occupancy_of(K kernel, int threads, int* cache) {
@@ -727,10 +729,9 @@ bool layout_copy_free(int M, int N) {
   return tiles * 4 >= rounds * cus * 3;
 }
 
-// The large kernel on the operands as stored (TA / TB: MN-major), 256x256 tiles.
-template <bool TA, bool TB>
-fg_status launch_layout_direct(fg::GemmParams& p, hipStream_t stream, const char* what) {
-  using Cfg = CfgBig;
+// The large kernel on the operands as stored (TA / TB: MN-major).
+template <class Cfg, bool TA, bool TB>
+fg_status launch_layout_direct_w(fg::GemmParams& p, hipStream_t stream, const char* what) {
   p.tiles_m = (p.rows + Cfg::BM - 1) / Cfg::BM;
   p.tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
   const int64_t slots = (int64_t)p.tiles_m * p.tiles_n;
@@ -743,6 +744,25 @@ fg_status launch_layout_direct(fg::GemmParams& p, hipStream_t stream, const char
                  : launch_big_k<Cfg, fg::kDenseC, false, TA, TB>(p, stream, what);
   return ktail ? launch_big_k<Cfg, fg::kDense, true, TA, TB>(p, stream, what)
                : launch_big_k<Cfg, fg::kDense, false, TA, TB>(p, stream, what);
+}
+
+// 256x256 tiles, or 256x160 where the NT plan takes those (the 256-wide
+// tiles would leave many CUs idle).  Measured on MI355X at 4096 x 2112 x 7168,
+// copy-free: NN 110 -> 100 us, TN 109 -> 96, TT 101 -> 86.  The 224-wide
+// tiles the NT plan takes at N = 7168 were mixed here (NN 8 % slower at
+// K = 16384, TT 2-4 % faster), so those shapes keep the 256-wide tiles.
+// FG_LAYOUT_BN=256 keeps the 256-wide tiles everywhere (tuning).
+template <bool TA, bool TB>
+fg_status launch_layout_direct(fg::GemmParams& p, hipStream_t stream, const char* what) {
+  const char* f = getenv("FG_LAYOUT_BN");
+  const bool narrow = !(f && atoi(f) == 256) && pick_bn((p.rows + 255) / 256, p.N) == 160;
+  if (narrow) {
+    if constexpr (TB)
+      return launch_layout_direct_w<CfgBig160Mn, TA, TB>(p, stream, what);
+    else
+      return launch_layout_direct_w<CfgBig160, TA, TB>(p, stream, what);
+  }
+  return launch_layout_direct_w<CfgBig, TA, TB>(p, stream, what);
 }
 
 template <bool TA, bool TB>

@@ -468,14 +468,16 @@ __global__ __launch_bounds__(C::THREADS, 2) void gemm_fp8_kernel(GemmParams p) {
 // segment.
 // ===========================================================================
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+// BROWS: the B rows a stage holds (BN; 256 for a B staged MN-major, whose
+// slice takes 128 K rows of 256 bytes whatever the tile width).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BROWS_ = BN_>
 struct BigCfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BROWS = BROWS_;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = NWAVES * 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int SM = WM / 16, SN = WN / 16;
-  static constexpr int STAGE = (BM + BN) * 128;
+  static constexpr int STAGE = (BM + BROWS) * 128;
   // 1 KiB (8-row) loads per slice: each wave of the first half loads
   // LOADS_A consecutive A loads and LOADS_B consecutive B loads
   static constexpr int LOADS_A = BM / 8 / (NWAVES / 2), LOADS_B = BN / 8 / (NWAVES / 2);
@@ -696,7 +698,8 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
                                                   uint8_t* sa_area, int wave, int lane, int sa_k = -1) {
   constexpr int BM = C::BM;
   constexpr int HALF = C::NWAVES / 2, LA = C::LOADS_A, LB = C::LOADS_B;
-  static_assert(!(TA || TB) || (BM == 256 && C::BN == 256 && HALF == 4), "MN-major operands: 256x256 tiles");
+  static_assert(!(TA || TB) || (BM == 256 && HALF == 4), "MN-major operands: 256-row tiles, 4 loading waves");
+  static_assert(!TB || C::BROWS >= 256, "an MN-major B needs 256-byte K rows in the stage");
   const bool is_a = wave < HALF;  // wave-uniform: one wave of each SIMD loads
   const int64_t bytes_a = (int64_t)(t.rows_alloc - t.m0 - 1) * p.lda + t.krows;
   const int64_t bytes_b = (int64_t)(p.N - t.n0 - 1) * p.ldb + t.krows;
@@ -723,7 +726,7 @@ __device__ __forceinline__ void issue_slice_loads(const GemmParams& p, const Wor
     }
     if (TB) {
       issue_rows_mn<8>(mn_slice_rsrc(t.B, p.ldb, kb, t.krows, t.n0, p.N), p.ldb, wave * 8, stage + BM * 128, lane,
-                       p.N - t.n0);
+                       min(C::BN, p.N - t.n0));
     } else {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.B + (int64_t)t.n0 * p.ldb, bytes_b);
       if (clip)
