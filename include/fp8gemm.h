@@ -183,7 +183,7 @@ fg_status gemm_fp8_nt_c(const uint8_t* A, int64_t lda, const float* sa, int64_t 
  *    takes the copy-free path where the operands allow it and the large
  *    kernel's 256 x 256 tiles keep the device's CUs at least three quarters
  *    busy over their rounds (measured on MI355X at M = 4096: level with or
- *    2-9 % faster than the copies there, 10-15 % slower than them at
+ *    2-9 % faster than the copies there, 2-7 % slower than them at
  *    N = 2112), and the copies otherwise.  Both paths give the same bits.
  * workspace_bytes == 0 (workspace ignored): the copy-free path; operands it
  *    cannot take give FG_EALIGN.  For callers without device memory to spare.

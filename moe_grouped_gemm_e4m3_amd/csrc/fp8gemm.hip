@@ -715,9 +715,10 @@ bool mn_direct(const void* x, int64_t ld, int ext) {
 // the CUs at least three quarters busy over their rounds.  Measured on
 // MI355X at M = 4096, N = 4096, 7168 and 24576: level with or 2-9 % faster
 // than copying them first (the copies cost a pass over both operands); at
-// N = 2112 (144 such tiles on 256 CUs, against the NT plan's 224 tiles of
-// 256x160) the copies were 10-15 % faster.  FG_LAYOUT_COPY=1 keeps the
-// copies, =0 skips them wherever the operands allow (tests and tuning).
+// N = 2112 (144 such tiles on 256 CUs; the copy-free path then runs the NT
+// plan's 224 tiles of 256x160) the copies were still 2-7 % faster.
+// FG_LAYOUT_COPY=1 keeps the copies, =0 skips them wherever the operands
+// allow (tests and tuning).
 bool layout_copy_free(int M, int N) {
   const char* f = getenv("FG_LAYOUT_COPY");
   if (f && *f) return strcmp(f, "0") == 0;
